@@ -1,0 +1,195 @@
+"""Python binding of libjetfp8 (the MI355X FP8 group-quantize + block-scaled GEMM library).
+
+Argument marshalling only: every step of the quantize / GEMM path runs in the library's gfx950 kernels.
+PyTorch supplies device memory (tensors) and the current HIP stream.  The raw entry points carry the C
+names (jetfp8_quantize, jetfp8_gemm_fwd, jetfp8_gemm_dgrad, jetfp8_gemm_wgrad) and take caller-allocated
+output tensors; the helpers below them (quantize_rows, ..., linear_forward) only allocate outputs and call
+the raw entry points.
+
+The library is loaded from fp8_precision_rl_amd/lib/libjetfp8.so.  If it is missing this module raises on
+first use; there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "lib", "libjetfp8.so")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_MODE, ERR_HIP = 0, -1, -2, -3, -4, -5
+ROWS_1x128, COLS_128x1_T, BLOCKS_128x128 = 0, 1, 2
+EXPORTED = ("jetfp8_quantize", "jetfp8_gemm_fwd", "jetfp8_gemm_dgrad", "jetfp8_gemm_wgrad",
+            "jetfp8_status_string", "jetfp8_version")
+
+_lib = None
+
+
+class JetFP8Error(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn} failed with status {status}: {msg}")
+        self.status = status
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load (once) and type the C entry points.  Raises if the library has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"libjetfp8 is not built ({path} missing); run `python -m fp8_precision_rl_amd.build`")
+    L = ctypes.CDLL(path)
+    vp, i64, c_int = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    L.jetfp8_quantize.restype = c_int
+    L.jetfp8_quantize.argtypes = [vp, i64, i64, c_int, vp, vp, vp, vp]
+    for name in ("jetfp8_gemm_fwd", "jetfp8_gemm_dgrad", "jetfp8_gemm_wgrad"):
+        f = getattr(L, name)
+        f.restype = c_int
+        f.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp]
+    L.jetfp8_status_string.restype = ctypes.c_char_p
+    L.jetfp8_status_string.argtypes = [c_int]
+    L.jetfp8_version.restype = c_int
+    L.jetfp8_version.argtypes = []
+    _lib = L
+    return L
+
+
+def status_string(status: int) -> str:
+    return load_library().jetfp8_status_string(int(status)).decode()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != OK:
+        raise JetFP8Error(fn, status, status_string(status))
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("libjetfp8 takes device tensors only")
+    if not t.is_contiguous():
+        raise ValueError("libjetfp8 takes contiguous (row-major) tensors only")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _dt(t, dtype, name):
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+
+
+# ------------------------------------------------------------------------------------------------
+# Raw entry points: same names and argument order as the C ABI; outputs are caller-allocated.
+# ------------------------------------------------------------------------------------------------
+def jetfp8_quantize(src_bf16, rows: int, cols: int, mode: int, dst_codes, dst_scales, dst_codes_t=None,
+                    stream=None) -> None:
+    L = load_library()
+    st = L.jetfp8_quantize(_ptr(src_bf16), int(rows), int(cols), int(mode), _ptr(dst_codes), _ptr(dst_scales),
+                           _ptr(dst_codes_t), _stream(stream))
+    _check("jetfp8_quantize", st)
+
+
+def jetfp8_gemm_fwd(xq, xs, wq, ws, y_bf16, M: int, N: int, K: int, stream=None) -> None:
+    L = load_library()
+    _check("jetfp8_gemm_fwd", L.jetfp8_gemm_fwd(_ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws), _ptr(y_bf16),
+                                                 int(M), int(N), int(K), _stream(stream)))
+
+
+def jetfp8_gemm_dgrad(dyq, dys, wqT, ws, dx_bf16, M: int, N: int, K: int, stream=None) -> None:
+    L = load_library()
+    _check("jetfp8_gemm_dgrad", L.jetfp8_gemm_dgrad(_ptr(dyq), _ptr(dys), _ptr(wqT), _ptr(ws), _ptr(dx_bf16),
+                                                     int(M), int(N), int(K), _stream(stream)))
+
+
+def jetfp8_gemm_wgrad(dyqT, dysT, xqT, xsT, dw_bf16, M: int, N: int, K: int, stream=None) -> None:
+    L = load_library()
+    _check("jetfp8_gemm_wgrad", L.jetfp8_gemm_wgrad(_ptr(dyqT), _ptr(dysT), _ptr(xqT), _ptr(xsT), _ptr(dw_bf16),
+                                                     int(M), int(N), int(K), _stream(stream)))
+
+
+# ------------------------------------------------------------------------------------------------
+# Allocating helpers (torch tensors in, torch tensors out).
+# ------------------------------------------------------------------------------------------------
+def quantize_rows(x, stream=None):
+    """1x128 groups along the last axis: x bf16 [R, C] -> codes uint8 [R, C], scales fp32 [C/128, R]."""
+    import torch
+    _dt(x, torch.bfloat16, "x")
+    R, C = x.shape
+    q = torch.empty((R, C), dtype=torch.uint8, device=x.device)
+    s = torch.empty((C // 128, R), dtype=torch.float32, device=x.device)
+    jetfp8_quantize(x, R, C, ROWS_1x128, q, s, None, stream)
+    return q, s
+
+
+def quantize_cols_t(x, stream=None):
+    """128x1 groups along the first axis, codes transposed: x bf16 [R, C] -> codes [C, R], scales [R/128, C]."""
+    import torch
+    _dt(x, torch.bfloat16, "x")
+    R, C = x.shape
+    q = torch.empty((C, R), dtype=torch.uint8, device=x.device)
+    s = torch.empty((R // 128, C), dtype=torch.float32, device=x.device)
+    jetfp8_quantize(x, R, C, COLS_128x1_T, q, s, None, stream)
+    return q, s
+
+
+def quantize_blocks(w, transposed: bool = True, stream=None):
+    """128x128 blocks: w bf16 [N, K] -> codes [N, K], scales [N/128, K/128], (codes^T [K, N] if transposed)."""
+    import torch
+    _dt(w, torch.bfloat16, "w")
+    N, K = w.shape
+    q = torch.empty((N, K), dtype=torch.uint8, device=w.device)
+    s = torch.empty((N // 128, K // 128), dtype=torch.float32, device=w.device)
+    qT = torch.empty((K, N), dtype=torch.uint8, device=w.device) if transposed else None
+    jetfp8_quantize(w, N, K, BLOCKS_128x128, q, s, qT, stream)
+    return (q, s, qT) if transposed else (q, s)
+
+
+def gemm_fwd(xq, xs, wq, ws, stream=None):
+    import torch
+    M, K = xq.shape
+    N = wq.shape[0]
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=xq.device)
+    jetfp8_gemm_fwd(xq, xs, wq, ws, y, M, N, K, stream)
+    return y
+
+
+def gemm_dgrad(dyq, dys, wqT, ws, stream=None):
+    import torch
+    M, N = dyq.shape
+    K = wqT.shape[0]
+    dx = torch.empty((M, K), dtype=torch.bfloat16, device=dyq.device)
+    jetfp8_gemm_dgrad(dyq, dys, wqT, ws, dx, M, N, K, stream)
+    return dx
+
+
+def gemm_wgrad(dyqT, dysT, xqT, xsT, stream=None):
+    import torch
+    N, M = dyqT.shape
+    K = xqT.shape[0]
+    dw = torch.empty((N, K), dtype=torch.bfloat16, device=dyqT.device)
+    jetfp8_gemm_wgrad(dyqT, dysT, xqT, xsT, dw, M, N, K, stream)
+    return dw
+
+
+def linear_forward(x, wq, ws, stream=None):
+    """FP8 linear forward (rollout and training share it): quantize x in 1x128 groups, block-scaled GEMM."""
+    xq, xs = quantize_rows(x, stream)
+    return gemm_fwd(xq, xs, wq, ws, stream), (xq, xs)
+
+
+def linear_backward(dy, x, wqT, ws, stream=None):
+    """DGrad and WGrad of the FP8 linear: dY re-quantized along each GEMM's contraction axis."""
+    dyq, dys = quantize_rows(dy, stream)
+    dx = gemm_dgrad(dyq, dys, wqT, ws, stream)
+    dyqT, dysT = quantize_cols_t(dy, stream)
+    xqT, xsT = quantize_cols_t(x, stream)
+    dw = gemm_wgrad(dyqT, dysT, xqT, xsT, stream)
+    return dx, dw

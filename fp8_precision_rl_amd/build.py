@@ -1,0 +1,43 @@
+"""Compile the gfx950 HIP sources into fp8_precision_rl_amd/lib/libjetfp8.so (in-tree, so the built library
+travels with the source tree).
+
+Flags: IEEE fp32 semantics are part of the contract (bit-exact codes and scales, a fixed per-element
+fma sequence), so no fast-math and no contraction beyond the explicit fmaf calls; packed-fp32 VALU
+instructions are disabled.
+"""
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC_DIR = os.path.join(HERE, "csrc")
+LIB_DIR = os.path.join(HERE, "lib")
+LIB = os.path.join(LIB_DIR, "libjetfp8.so")
+SOURCES = ["jetfp8_api.hip", "jetfp8_quant.hip", "jetfp8_gemm.hip"]
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+         "-ffp-contract=off", "-fno-fast-math", "-fno-gpu-flush-denormals-to-zero",
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-Wall", "-Wno-unused-result"]
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(LIB_DIR, exist_ok=True)
+    srcs = [os.path.join(SRC_DIR, s) for s in SOURCES]
+    tmp = LIB + ".tmp"
+    cmd = [HIPCC] + FLAGS + ["-o", tmp] + srcs
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    errs = "\n".join(l for l in (r.stderr or "").splitlines() if "packed-fp32-ops" not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({r.returncode}):\n{errs}")
+    if verbose and errs.strip():
+        print(errs, file=sys.stderr)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    build(verbose=True)

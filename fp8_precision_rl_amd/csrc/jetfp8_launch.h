@@ -1,0 +1,21 @@
+// Host-side launchers of the libjetfp8 kernels (shapes are validated by the C ABI layer before these run).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace jetfp8 {
+
+hipError_t launch_quant_rows(const uint16_t* x, int64_t R, int64_t C, uint8_t* q, float* s, hipStream_t st);
+hipError_t launch_quant_cols_t(const uint16_t* x, int64_t R, int64_t C, uint8_t* qT, float* sT, hipStream_t st);
+hipError_t launch_quant_blocks(const uint16_t* x, int64_t R, int64_t C, uint8_t* q, float* s, uint8_t* qT,
+                               hipStream_t st);
+
+// C[i][j] = sum_g As[g][i] * sb(j, g) * sum_{k in g} A[i][k] * B[j][k], A [I][Kc], B [J][Kc].
+// Block-scaled B: sb(j, g) = Bs[(j / 128) * sbj + g * sbg].  Row-scaled B: sb(j, g) = Bs[g * J + j].
+hipError_t launch_gemm_block_scaled_b(const uint8_t* A, const float* As, const uint8_t* B, const float* Bs,
+                                      uint16_t* C, int64_t I, int64_t J, int64_t Kc, int64_t sbj, int64_t sbg,
+                                      hipStream_t st);
+hipError_t launch_gemm_row_scaled_b(const uint8_t* A, const float* As, const uint8_t* B, const float* Bs,
+                                    uint16_t* C, int64_t I, int64_t J, int64_t Kc, hipStream_t st);
+
+}  // namespace jetfp8

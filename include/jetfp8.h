@@ -1,0 +1,111 @@
+/*
+ * jetfp8.h -- C ABI of the MI355X (gfx950) FP8 group-quantize + block-scaled GEMM library.
+ *
+ * The operations are those of the Jet-RL unified FP8 precision flow ("Jet-RL: Enabling On-Policy FP8
+ * Reinforcement Learning with Unified Training and Rollout Precision Flow", gist.science explainers,
+ * sections "Architecture Centrale" and "Schema de Quantification" / "Esquema de Quantizacao"):
+ * the same FP8 linear layers serve rollout and the training forward; activations are quantized in 1x128
+ * groups, weights in 128x128 blocks; gradients between operators stay BF16 and are quantized inside the
+ * DGrad and WGrad GEMMs, which run in FP8 ("1x128 and 128x1" groupings for WGrad).
+ *
+ * Numerics (readings of what the pages leave open):
+ *   FP8 format ... OCP E4M3 (bias 7, largest finite 448, NaN never produced).
+ *   scale ........ s = fl32(amax / 448) per group, computed on every call (no calibration state).
+ *   code ......... nearest E4M3 value to x / s (exact quotient), ties to the even code, |x/s| > 448
+ *                  saturates to 448; an all-zero group has s = 0 and signed-zero codes.
+ *   GEMMs ........ per output element: acc = +0; for each 128-wide group g of the contraction axis in
+ *                  ascending order: acc = fma(p_g, fl32(sa_g * sb_g), acc), where p_g is the fp32 group
+ *                  dot product formed by one gfx950 FP8 matrix instruction; out = bf16(acc), round to
+ *                  nearest even.  The contraction is never split, so an output row is bitwise the same
+ *                  whatever the number of rows in the call (decode M=1 and a training batch agree).
+ *
+ * Conventions for every entry point:
+ *   - Matrices are dense, row-major, last index contiguous; bf16 tensors are passed as raw 16-bit
+ *     patterns (void*), FP8 codes as uint8_t, scales as float.  No strides.
+ *   - Every pointer is a DEVICE pointer owned by the caller; the library never allocates, frees or
+ *     synchronizes.  Work is enqueued on `stream` (a hipStream_t; NULL = the default stream) and runs
+ *     asynchronously; outputs are valid once the stream has reached that point.
+ *   - Arguments are validated on the host before anything is launched.  Return value: JETFP8_OK, or a
+ *     negative jetfp8_status; on error nothing has been enqueued and outputs are untouched
+ *     (JETFP8_ERR_HIP: a launch was rejected by the runtime; earlier kernels of the same call may have
+ *     been enqueued).  No exception ever crosses this interface.
+ *   - All pointers must be 16-byte aligned (JETFP8_ERR_ALIGN otherwise).  Buffers must not overlap.
+ *   - Sizes: every dimension >= 1; every grouped or contraction axis a multiple of 128, plus the
+ *     per-mode rules below (JETFP8_ERR_SHAPE otherwise); every dimension < 2^31.
+ *   - Thread safety: calls are independent; concurrent calls on different streams are allowed.
+ */
+#ifndef JETFP8_H
+#define JETFP8_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    JETFP8_OK = 0,
+    JETFP8_ERR_NULL = -1,   /* a required pointer is NULL */
+    JETFP8_ERR_SHAPE = -2,  /* a dimension < 1, >= 2^31, or a grouped/contraction axis not a multiple of 128 */
+    JETFP8_ERR_ALIGN = -3,  /* a pointer is not 16-byte aligned */
+    JETFP8_ERR_MODE = -4,   /* unknown grouping mode, or dst_codes_t given for a mode without it */
+    JETFP8_ERR_HIP = -5     /* the HIP runtime rejected a launch */
+} jetfp8_status;
+
+typedef enum {
+    /* 1x128 groups along the contiguous axis (activations X for the forward, dY for DGrad).
+     * src [rows][cols] -> dst_codes [rows][cols], dst_scales [cols/128][rows].  cols % 128 == 0. */
+    JETFP8_ROWS_1x128 = 0,
+    /* 128x1 groups along the row axis, codes written transposed (dY and X for WGrad, grouped along
+     * the token axis).  src [rows][cols] -> dst_codes [cols][rows], dst_scales [rows/128][cols].
+     * rows % 128 == 0, cols % 64 == 0. */
+    JETFP8_COLS_128x1_T = 1,
+    /* 128x128 blocks (weights).  src [rows][cols] -> dst_codes [rows][cols],
+     * dst_scales [rows/128][cols/128], and when dst_codes_t != NULL the same codes transposed,
+     * dst_codes_t [cols][rows] (the B operand of DGrad).  rows % 128 == 0 and cols % 128 == 0. */
+    JETFP8_BLOCKS_128x128 = 2
+} jetfp8_grouping;
+
+/* Group quantization of a bf16 matrix to E4M3 codes plus fp32 scales (Jet-RL explainers,
+ * "Schema de Quantification": 1x128 per-group for activations, 128x128 per-block for weights;
+ * 1x128 and 128x1 for WGrad).  dst_codes_t is only accepted (and optional) for BLOCKS_128x128;
+ * pass NULL for the other modes. */
+int jetfp8_quantize(const void* src_bf16, int64_t rows, int64_t cols, int mode,
+                    uint8_t* dst_codes, float* dst_scales, uint8_t* dst_codes_t, void* stream);
+
+/* Forward FP8 linear (rollout decode, prefill, training forward):
+ *   Y[m][n] = sum_g xs[g][m] * ws[n/128][g] * sum_{k in g} xq[m][k] * wq[n][k]
+ * xq [M][K], xs [K/128][M] (JETFP8_ROWS_1x128 of X); wq [N][K], ws [N/128][K/128]
+ * (JETFP8_BLOCKS_128x128 of W); y [M][N] bf16.  K % 128 == 0, N % 128 == 0, any M >= 1. */
+int jetfp8_gemm_fwd(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws,
+                    void* y_bf16, int64_t M, int64_t N, int64_t K, void* stream);
+
+/* DGrad FP8 GEMM (Jet-RL explainers, "Passage Arriere": DGrad in FP8 with BF16 gradients quantized
+ * on entry):
+ *   dX[m][k] = sum_g dys[g][m] * ws[g][k/128] * sum_{n in g} dyq[m][n] * wqT[k][n]
+ * dyq [M][N], dys [N/128][M] (JETFP8_ROWS_1x128 of dY); wqT [K][N] (the transposed block codes of W
+ * from JETFP8_BLOCKS_128x128), ws [N/128][K/128] (the forward block scales, unchanged);
+ * dx [M][K] bf16.  N % 128 == 0, K % 128 == 0, any M >= 1. */
+int jetfp8_gemm_dgrad(const uint8_t* dyq, const float* dys, const uint8_t* wqT, const float* ws,
+                      void* dx_bf16, int64_t M, int64_t N, int64_t K, void* stream);
+
+/* WGrad FP8 GEMM ("1x128 and 128x1" kernel configuration: both operands grouped along the token axis,
+ * which is the contraction axis):
+ *   dW[n][k] = sum_g dysT[g][n] * xsT[g][k] * sum_{m in g} dyqT[n][m] * xqT[k][m]
+ * dyqT [N][M], dysT [M/128][N] (JETFP8_COLS_128x1_T of dY); xqT [K][M], xsT [M/128][K]
+ * (JETFP8_COLS_128x1_T of X); dw [N][K] bf16, overwritten.  M % 128 == 0, N % 128 == 0,
+ * K % 128 == 0. */
+int jetfp8_gemm_wgrad(const uint8_t* dyqT, const float* dysT, const uint8_t* xqT, const float* xsT,
+                      void* dw_bf16, int64_t M, int64_t N, int64_t K, void* stream);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* jetfp8_status_string(int status);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int jetfp8_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* JETFP8_H */

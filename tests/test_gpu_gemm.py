@@ -1,0 +1,139 @@
+"""GPU parity of the block-scaled FP8 GEMMs (forward, dgrad, wgrad) against the oracle, plus the
+kernel-level unified-flow property: an output row's bits do not depend on how many rows are computed.
+
+Tolerance (stated with the path): relative Frobenius error <= 1e-3 and max |error| <= 1e-2 * rms(out),
+comparing bf16 outputs with the oracle's bf16 outputs.  The oracle's per-group dot product is taken in
+both of its readings: the matrix-instruction model (MFMA) and the exact sum (EXACT).
+"""
+import numpy as np
+import pytest
+
+from conftest import bits_to_dev, compare_bf16, dev_to_bits, f32_to_bits
+
+pytestmark = pytest.mark.gpu
+
+REL_FROB = 1e-3
+MAX_ABS = 1e-2
+
+
+@pytest.fixture(scope="module")
+def jf():
+    import torch
+    import fp8_precision_rl_amd as m
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    m.load_library()
+    return m
+
+
+def _x(M, K, seed, frac=0.01):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    x[:, rng.choice(K, max(1, int(round(frac * K))), replace=False)] *= 50
+    return f32_to_bits(x)
+
+
+def _w(N, K, seed):
+    rng = np.random.default_rng(seed)
+    return f32_to_bits((rng.standard_normal((N, K)) * 0.02).astype(np.float32))
+
+
+def _dy(M, N, seed):
+    rng = np.random.default_rng(seed)
+    return f32_to_bits((rng.standard_t(3, (M, N)) * 1e-3).astype(np.float32))
+
+
+def _report(name, got, orc_ref_mfma, orc_ref_exact):
+    m = compare_bf16(got, orc_ref_mfma)
+    e = compare_bf16(got, orc_ref_exact)
+    print(f"{name}: vs matrix-core model {m}; vs exact group sums {e}", flush=True)
+    return m, e
+
+
+def _assert_tol(name, m, e):
+    assert m["rel_frob"] <= REL_FROB and m["max_abs_over_rms"] <= MAX_ABS, (name, m)
+    assert e["rel_frob"] <= REL_FROB, (name, e)
+
+
+@pytest.mark.parametrize("M,N,K", [(64, 256, 512), (300, 384, 640), (1, 128, 128), (129, 256, 1024)])
+def test_forward_parity(jf, orc, M, N, K):
+    import torch
+    xb, wb = _x(M, K, M + K), _w(N, K, N + K)
+    wq, ws, _ = jf.quantize_blocks(bits_to_dev(wb))
+    y, _ = jf.linear_forward(bits_to_dev(xb), wq, ws)
+    torch.cuda.synchronize()
+    oxq, oxs = orc.quantize_rows(xb)
+    owq, ows = orc.quantize_blocks(wb)
+    got = dev_to_bits(y)
+    m, e = _report(f"fwd {M}x{N}x{K}", got, orc.gemm_fwd(oxq, oxs, owq, ows, mode=orc.MFMA),
+                   orc.gemm_fwd(oxq, oxs, owq, ows, mode=orc.EXACT))
+    _assert_tol("fwd", m, e)
+
+
+@pytest.mark.parametrize("M,N,K", [(64, 256, 512), (300, 384, 256)])
+def test_dgrad_parity(jf, orc, M, N, K):
+    import torch
+    dyb, wb = _dy(M, N, M + N), _w(N, K, N + K + 1)
+    wq, ws, wqT = jf.quantize_blocks(bits_to_dev(wb))
+    dyq, dys = jf.quantize_rows(bits_to_dev(dyb))
+    dx = jf.gemm_dgrad(dyq, dys, wqT, ws)
+    torch.cuda.synchronize()
+    odq, ods = orc.quantize_rows(dyb)
+    owq, ows = orc.quantize_blocks(wb)
+    m, e = _report(f"dgrad {M}x{N}x{K}", dev_to_bits(dx), orc.gemm_dgrad(odq, ods, owq, ows, mode=orc.MFMA),
+                   orc.gemm_dgrad(odq, ods, owq, ows, mode=orc.EXACT))
+    _assert_tol("dgrad", m, e)
+
+
+@pytest.mark.parametrize("M,N,K", [(256, 256, 512), (384, 128, 384)])
+def test_wgrad_parity(jf, orc, M, N, K):
+    import torch
+    dyb, xb = _dy(M, N, M + N + 2), _x(M, K, M + K + 3)
+    dyqT, dysT = jf.quantize_cols_t(bits_to_dev(dyb))
+    xqT, xsT = jf.quantize_cols_t(bits_to_dev(xb))
+    dw = jf.gemm_wgrad(dyqT, dysT, xqT, xsT)
+    torch.cuda.synchronize()
+    odq, ods = orc.quantize_cols(dyb)
+    oxq, oxs = orc.quantize_cols(xb)
+    m, e = _report(f"wgrad {M}x{N}x{K}", dev_to_bits(dw), orc.gemm_wgrad(odq, ods, oxq, oxs, mode=orc.MFMA),
+                   orc.gemm_wgrad(odq, ods, oxq, oxs, mode=orc.EXACT))
+    _assert_tol("wgrad", m, e)
+
+
+def test_rows_are_bitwise_independent_of_M(jf):
+    """Decode (M=1), a small batch (M=32) and a training batch produce bitwise identical rows."""
+    import torch
+    M, N, K = 300, 256, 512
+    xb, wb = _x(M, K, 41), _w(N, K, 42)
+    wq, ws, _ = jf.quantize_blocks(bits_to_dev(wb))
+    x = bits_to_dev(xb)
+    y_all, _ = jf.linear_forward(x, wq, ws)
+    y32, _ = jf.linear_forward(x[100:132].contiguous(), wq, ws)
+    ones = [jf.linear_forward(x[r:r + 1].contiguous(), wq, ws)[0] for r in (0, 131, 299)]
+    torch.cuda.synchronize()
+    full = dev_to_bits(y_all)
+    assert np.array_equal(dev_to_bits(y32), full[100:132])
+    for r, y1 in zip((0, 131, 299), ones):
+        assert np.array_equal(dev_to_bits(y1)[0], full[r])
+
+
+def test_dgrad_equals_forward_on_transposed_blocks(jf):
+    import torch
+    M, N, K = 96, 256, 384
+    dyb, wb = _dy(M, N, 51), _w(N, K, 52)
+    wq, ws, wqT = jf.quantize_blocks(bits_to_dev(wb))
+    dyq, dys = jf.quantize_rows(bits_to_dev(dyb))
+    dx = jf.gemm_dgrad(dyq, dys, wqT, ws)
+    dx_fwd = jf.gemm_fwd(dyq, dys, wqT, ws.t().contiguous())
+    torch.cuda.synchronize()
+    assert np.array_equal(dev_to_bits(dx), dev_to_bits(dx_fwd))
+
+
+def test_repeat_runs_are_bitwise_identical(jf):
+    import torch
+    M, N, K = 256, 512, 1024
+    xb, wb = _x(M, K, 61), _w(N, K, 62)
+    wq, ws, _ = jf.quantize_blocks(bits_to_dev(wb))
+    x = bits_to_dev(xb)
+    outs = [dev_to_bits(jf.linear_forward(x, wq, ws)[0]) for _ in range(3)]
+    torch.cuda.synchronize()
+    assert all(np.array_equal(outs[0], o) for o in outs[1:])

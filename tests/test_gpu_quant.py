@@ -1,0 +1,108 @@
+"""GPU parity of the quantize kernels against the oracle: codes and scales bit for bit."""
+import os
+
+import numpy as np
+import pytest
+
+from conftest import bits_to_dev, f32_to_bits
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def jf():
+    import torch
+    import fp8_precision_rl_amd as m
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    m.load_library()
+    return m
+
+
+def _special_matrix(R, C, seed):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((R, C)).astype(np.float32)
+    x[:, rng.choice(C, max(1, C // 100), replace=False)] *= 50          # outlier channels
+    b = f32_to_bits(x)
+    g = C // 128
+    # special groups (rows mode view): zeros with a negative zero, tiny (subnormal scale), huge, mixed signs
+    if R > 4 and g > 1:
+        b[1, :128] = 0
+        b[1, 7] = 0x8000
+        b[2, 128:256] = f32_to_bits(rng.standard_normal(128).astype(np.float32) * np.float32(1e-37))
+        b[3, :128] = f32_to_bits(rng.standard_normal(128).astype(np.float32) * np.float32(1e37))
+        b[4, 128:256] = (rng.integers(0, 0x80, 128) | (rng.integers(0, 2, 128) << 15)).astype(np.uint16)  # bf16 subnormals
+    return b
+
+
+@pytest.mark.parametrize("R,C", [(64, 512), (37, 384), (300, 1024), (1, 128)])
+def test_rows_bit_exact(jf, orc, R, C):
+    import torch
+    b = _special_matrix(R, C, R * 7 + C)
+    q, s = jf.quantize_rows(bits_to_dev(b))
+    torch.cuda.synchronize()
+    oq, os_ = orc.quantize_rows(b)
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), os_.view(np.uint32))
+    assert np.array_equal(q.cpu().numpy(), oq)
+
+
+@pytest.mark.parametrize("R,C", [(128, 64), (256, 192), (384, 1024)])
+def test_cols_t_bit_exact(jf, orc, R, C):
+    import torch
+    b = _special_matrix(R, C, R + C)
+    q, s = jf.quantize_cols_t(bits_to_dev(b))
+    torch.cuda.synchronize()
+    oq, os_ = orc.quantize_cols(b)
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), os_.view(np.uint32))
+    assert np.array_equal(q.cpu().numpy(), oq.T)
+
+
+@pytest.mark.parametrize("R,C", [(128, 128), (256, 384), (512, 1024)])
+def test_blocks_bit_exact_with_transpose(jf, orc, R, C):
+    import torch
+    rng = np.random.default_rng(R + 3 * C)
+    b = f32_to_bits((rng.standard_normal((R, C)) * 0.02).astype(np.float32))
+    b[5, 9] = f32_to_bits(np.array([[3.0]], np.float32))[0, 0]
+    q, s, qT = jf.quantize_blocks(bits_to_dev(b))
+    q2, s2 = jf.quantize_blocks(bits_to_dev(b), transposed=False)
+    torch.cuda.synchronize()
+    oq, os_ = orc.quantize_blocks(b)
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), os_.view(np.uint32))
+    assert np.array_equal(q.cpu().numpy(), oq)
+    assert np.array_equal(qT.cpu().numpy(), oq.T)
+    assert np.array_equal(q2.cpu().numpy(), oq) and np.array_equal(s2.cpu().numpy(), s.cpu().numpy())
+
+
+def _pair_groups(amax_bits):
+    """Groups covering every (x, amax) pair for the given amax values: each row is one group of 128 whose
+    first element is +amax, the others walk through all bf16 magnitudes <= amax with alternating signs."""
+    rows = []
+    for a in amax_bits:
+        xs = np.arange(0, int(a) + 1, dtype=np.uint32).astype(np.uint16)
+        xs = xs | ((np.arange(xs.size) & 1).astype(np.uint16) << 15)
+        n = int(np.ceil(xs.size / 127))
+        pad = np.zeros(n * 127, np.uint16)
+        pad[:xs.size] = xs
+        blk = np.empty((n, 128), np.uint16)
+        blk[:, 0] = a
+        blk[:, 1:] = pad.reshape(n, 127)
+        rows.append(blk)
+    return np.concatenate(rows)
+
+
+def test_all_x_amax_pairs_sampled(jf, orc):
+    """Codes depend only on (x, amax): check every x for a spread of amax values (every 29th positive finite
+    bf16 amax plus edge values), i.e. about 1/29 of all pairs.  JETFP8_FULL_SWEEP=1 checks all of them."""
+    import torch
+    full = os.environ.get("JETFP8_FULL_SWEEP") == "1"
+    all_a = np.arange(1, 0x7F80, dtype=np.uint32)
+    amax = all_a if full else np.unique(np.concatenate([all_a[::29], [1, 2, 0x7F, 0x80, 0x81, 0x3F80, 0x43E0, 0x7F7F]]))
+    chunk = 2048 if not full else 1024
+    for i in range(0, amax.size, chunk):
+        g = _pair_groups(amax[i:i + chunk].astype(np.uint16))
+        q, s = jf.quantize_rows(bits_to_dev(g))
+        torch.cuda.synchronize()
+        oq, os_ = orc.quantize_rows(g)
+        assert np.array_equal(s.cpu().numpy().view(np.uint32), os_.view(np.uint32)), i
+        qq = q.cpu().numpy()
+        bad = np.argwhere(qq != oq)
+        assert bad.size == 0, [(hex(int(g[r, c])), hex(int(g[r, 0])), hex(int(qq[r, c])), hex(int(oq[r, c]))) for r, c in bad[:5]]
