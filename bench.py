@@ -1,0 +1,244 @@
+#!/usr/bin/env python3
+"""Benchmark of the FP8 group-quantize + block-scaled GEMM path on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic inputs, for every linear of the
+workload: 128x128 block quantization of the bf16 master weights (with the transposed copy), 1x128
+quantization of X, the forward GEMM, 1x128 quantization of dY, DGrad, 128x1 quantization of dY and X
+(transposed), WGrad.  Inputs are generated on the GPU and resident in HBM before timing starts; outputs
+are preallocated.  The headline value is GEMM TFLOP/s over the whole step (GEMM flops / step time,
+quantization included).
+
+Prints one JSON line.  Besides the contract fields it carries
+  roofline      the GEMM kernel: algorithmic flops (2*M*N*K per launch) / mean launch time, measured with
+                HIP events on the launch stream over the timed steps, against the MI355X dense FP8 peak;
+                traffic = HBM bytes per launch from rocprofv3 counters when supplied (--traffic-json).
+  roofline_quant the quantize kernels: algorithmic bytes / time against 8 TB/s.
+  cpu_baseline  the CPU oracle timed on this host on a bounded sample of the same workload.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+FP8_PEAK_TFLOPS = 5000.0      # MI355X dense FP8 matrix peak
+HBM_PEAK_GBS = 8000.0         # MI355X HBM3E
+METRIC = "block-scaled FP8 GEMM TFLOP/s (fwd+dgrad+wgrad), % of MI355X FP8 peak"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="llama3_8b_train_m16384")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-sample-rows", type=int, default=64)
+    p.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "gemm_traffic.json"),
+                   help="per-launch HBM bytes measured by rocprofv3 for this workload (optional)")
+    return p.parse_args()
+
+
+class Linear:
+    """Device buffers of one FP8 linear layer for a full training step."""
+
+    def __init__(self, wl, index, torch, workloads):
+        d = workloads.device_linear(wl, index)
+        self.name, self.M, self.K, self.N = d["name"], d["M"], d["K"], d["N"]
+        M, K, N = self.M, self.K, self.N
+        dev = d["x"].device
+        u8, f32, bf = torch.uint8, torch.float32, torch.bfloat16
+        self.x, self.w, self.dy = d["x"], d["w"], d["dy"]
+        self.wq = torch.empty((N, K), dtype=u8, device=dev)
+        self.wqT = torch.empty((K, N), dtype=u8, device=dev)
+        self.ws = torch.empty((N // 128, K // 128), dtype=f32, device=dev)
+        self.xq = torch.empty((M, K), dtype=u8, device=dev)
+        self.xs = torch.empty((K // 128, M), dtype=f32, device=dev)
+        self.y = torch.empty((M, N), dtype=bf, device=dev)
+        self.dyq = torch.empty((M, N), dtype=u8, device=dev)
+        self.dys = torch.empty((N // 128, M), dtype=f32, device=dev)
+        self.dx = torch.empty((M, K), dtype=bf, device=dev)
+        self.dyqT = torch.empty((N, M), dtype=u8, device=dev)
+        self.dysT = torch.empty((M // 128, N), dtype=f32, device=dev)
+        self.xqT = torch.empty((K, M), dtype=u8, device=dev)
+        self.xsT = torch.empty((M // 128, K), dtype=f32, device=dev)
+        self.dw = torch.empty((N, K), dtype=bf, device=dev)
+
+    def gemm_flops(self):
+        return 3 * 2 * self.M * self.N * self.K
+
+    def quant_bytes(self):
+        M, N, K = self.M, self.N, self.K
+        rows = 2 + 1 + 4 / 128                      # bf16 in, code out, one fp32 scale per 128
+        return {"w_blocks_T": N * K * (2 + 1 + 1 + 4 / 16384), "x_rows": M * K * rows, "dy_rows": M * N * rows,
+                "dy_cols_t": M * N * rows, "x_cols_t": M * K * rows}
+
+
+def run_step(L, jf, st, ev=None):
+    """One pass of the hot path over one linear.  ev: optional list collecting (kind, name, flops_or_bytes,
+    start_event, end_event) around each launch."""
+    M, N, K = L.M, L.N, L.K
+
+    def timed(kind, name, amount, fn):
+        if ev is None:
+            fn()
+            return
+        import torch
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        ev.append((kind, name, amount, a, b))
+
+    qb = L.quant_bytes()
+    timed("quant", "w_blocks_T", qb["w_blocks_T"],
+          lambda: jf.jetfp8_quantize(L.w, N, K, jf.BLOCKS_128x128, L.wq, L.ws, L.wqT, st))
+    timed("quant", "x_rows", qb["x_rows"], lambda: jf.jetfp8_quantize(L.x, M, K, jf.ROWS_1x128, L.xq, L.xs, None, st))
+    timed("gemm", "fwd", 2 * M * N * K, lambda: jf.jetfp8_gemm_fwd(L.xq, L.xs, L.wq, L.ws, L.y, M, N, K, st))
+    timed("quant", "dy_rows", qb["dy_rows"],
+          lambda: jf.jetfp8_quantize(L.dy, M, N, jf.ROWS_1x128, L.dyq, L.dys, None, st))
+    timed("gemm", "dgrad", 2 * M * N * K, lambda: jf.jetfp8_gemm_dgrad(L.dyq, L.dys, L.wqT, L.ws, L.dx, M, N, K, st))
+    timed("quant", "dy_cols_t", qb["dy_cols_t"],
+          lambda: jf.jetfp8_quantize(L.dy, M, N, jf.COLS_128x1_T, L.dyqT, L.dysT, None, st))
+    timed("quant", "x_cols_t", qb["x_cols_t"],
+          lambda: jf.jetfp8_quantize(L.x, M, K, jf.COLS_128x1_T, L.xqT, L.xsT, None, st))
+    timed("gemm", "wgrad", 2 * M * N * K, lambda: jf.jetfp8_gemm_wgrad(L.dyqT, L.dysT, L.xqT, L.xsT, L.dw, M, N, K, st))
+
+
+def cpu_baseline(wl, rows, workloads):
+    """The oracle (unchanged) on a bounded sample of the workload: for every linear, the full weight
+    quantization, then forward and DGrad for `rows` token rows and WGrad for `rows` rows of dW over one
+    128-token group, with all of this host's threads."""
+    import numpy as np
+    import oracle
+    threads = oracle.default_threads()
+    flops = 0
+    elapsed = 0.0
+    for i, (name, K, N) in enumerate(wl.linears):
+        h = workloads.host_linear(workloads.Workload(wl.name, 128, wl.linears, wl.outlier_frac, wl.seed, True, ""), i)
+        t0 = time.perf_counter()
+        wq, ws = oracle.quantize_blocks(h["w"], threads)
+        xq, xs = oracle.quantize_rows(h["x"], threads)
+        dyq, dys = oracle.quantize_rows(h["dy"], threads)
+        oracle.gemm_fwd(xq, xs, wq, ws, rows=np.arange(rows), mode=oracle.MFMA, threads=threads)
+        oracle.gemm_dgrad(dyq, dys, wq, ws, rows=np.arange(rows), mode=oracle.MFMA, threads=threads)
+        dyqc, dysc = oracle.quantize_cols(h["dy"], threads)
+        xqc, xsc = oracle.quantize_cols(h["x"], threads)
+        oracle.gemm_wgrad(dyqc, dysc, xqc, xsc, rows=np.arange(rows), mode=oracle.MFMA, threads=threads)
+        elapsed += time.perf_counter() - t0
+        flops += 2 * rows * N * K * 2 + 2 * rows * K * 128
+    return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": (f"per linear: full 128x128 weight quantization; forward and dgrad for {rows} token rows; "
+                       f"wgrad for {rows} rows of dW over one 128-token group; total {flops / 1e9:.1f} GFLOP "
+                       f"in {elapsed:.1f} s"),
+            "seconds": elapsed}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path has no multi-GPU part.",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import fp8_precision_rl_amd as jf
+    import workloads
+
+    jf.load_library()          # raises if the HIP library is not built: there is no fallback
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(3)
+    wl = workloads.WORKLOADS[args.workload]
+    layers = [Linear(wl, i, torch, workloads) for i in range(len(wl.linears))]
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    print(f"[bench] {wl.name}: {wl.description}; inputs resident", file=sys.stderr, flush=True)
+
+    for _ in range(args.warmup):
+        for L in layers:
+            run_step(L, jf, st)
+    torch.cuda.synchronize()
+    print(f"[bench] warmup {args.warmup} done", file=sys.stderr, flush=True)
+
+    ev = []
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    t_start.record()
+    for _ in range(args.steps):
+        for L in layers:
+            run_step(L, jf, st, ev)
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    total_ms = t_start.elapsed_time(t_end)
+    ms_per_step = total_ms / args.steps
+    step_flops = sum(L.gemm_flops() for L in layers)
+    value = step_flops / (ms_per_step * 1e-3) / 1e12
+
+    gemm_ms = sum(a.elapsed_time(b) for k, _, _, a, b in ev if k == "gemm")
+    gemm_flops = sum(f for k, _, f, _, _ in ev if k == "gemm")
+    n_gemm = sum(1 for k, *_ in ev if k == "gemm")
+    quant_ms = sum(a.elapsed_time(b) for k, _, _, a, b in ev if k == "quant")
+    quant_bytes = sum(f for k, _, f, _, _ in ev if k == "quant")
+    achieved = gemm_flops / (gemm_ms * 1e-3) / 1e12
+    per = {}
+    for k, name, amt, a, b in ev:
+        key = f"{k}:{name}"
+        per.setdefault(key, [0.0, 0.0])
+        per[key][0] += a.elapsed_time(b)
+        per[key][1] += amt
+    traffic = None
+    if os.path.exists(args.traffic_json):
+        try:
+            tj = json.load(open(args.traffic_json))
+            if tj.get("workload") == wl.name:
+                traffic = tj.get("gemm_bytes_per_launch")
+        except (OSError, ValueError):
+            traffic = None
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3 (fp32 accumulate, bf16 out)",
+        "data": "synthetic (seeded torch generator on device: X~N(0,1) with 0.1% outlier channels x50, "
+                "W~N(0,0.02^2), dY~1e-3*Student-t(3))",
+        "config": {"workload": wl.name, "tokens": wl.M,
+                   "linears": [{"name": n, "K": K, "N": N} for n, K, N in wl.linears],
+                   "step": "per linear: W block quant(+T), X rows quant, fwd, dY rows quant, dgrad, "
+                           "dY/X cols quant (T), wgrad"},
+        "pct_of_fp8_peak": round(100 * value / FP8_PEAK_TFLOPS, 2),
+        "gemm_only_tflops": round(achieved, 2),
+        "wall_s": round(wall, 4),
+        "roofline": {"bound": "mfma", "kernel": "gemm_nt_kernel (fwd, dgrad, wgrad)", "achieved": round(achieved, 2),
+                     "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / FP8_PEAK_TFLOPS, 4),
+                     "traffic": traffic, "launches": n_gemm,
+                     "mean_launch_us": round(1e3 * gemm_ms / max(n_gemm, 1), 2),
+                     "flops_per_launch_mean": gemm_flops / max(n_gemm, 1)},
+        "roofline_quant": {"bound": "hbm", "achieved": round(quant_bytes / (quant_ms * 1e-3) / 1e9, 1),
+                           "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                           "frac": round(quant_bytes / (quant_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+        "per_kernel": {k: {"ms_per_step": round(v[0] / args.steps, 4),
+                           ("tflops" if k.startswith("gemm") else "gbs"):
+                               round(v[1] / (v[0] * 1e-3) / (1e12 if k.startswith("gemm") else 1e9), 1)}
+                       for k, v in per.items()},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample_rows, workloads)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
