@@ -23,6 +23,15 @@ int check_gemm(const void* a, const void* as, const void* b, const void* bs, con
     return JETFP8_OK;
 }
 
+// 32-bit offset limits of the GEMM kernels (I rows and J rows of the two operands, contraction Kc): a
+// block's 256-row operand band and each scale array must stay below 2^31 bytes.
+int check_gemm_extent(int64_t I, int64_t J, int64_t Kc) {
+    const int64_t G = Kc / 128;
+    if (256 * Kc > jetfp8::kMaxGemmBand || G * I * 4 > jetfp8::kMaxGemmBand || G * J * 4 > jetfp8::kMaxGemmBand)
+        return JETFP8_ERR_SHAPE;
+    return JETFP8_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -67,7 +76,8 @@ int jetfp8_quantize(const void* src_bf16, int64_t rows, int64_t cols, int mode, 
 
 int jetfp8_gemm_fwd(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws, void* y_bf16, int64_t M,
                     int64_t N, int64_t K, void* stream) {
-    const int rc = check_gemm(xq, xs, wq, ws, y_bf16, M, N, K, false);
+    int rc = check_gemm(xq, xs, wq, ws, y_bf16, M, N, K, false);
+    if (rc == JETFP8_OK) rc = check_gemm_extent(M, N, K);
     if (rc != JETFP8_OK) return rc;
     return hip_status(jetfp8::launch_gemm_block_scaled_b(xq, xs, wq, ws, static_cast<uint16_t*>(y_bf16), M, N, K,
                                                          K / 128, 1, static_cast<hipStream_t>(stream)));
@@ -75,7 +85,8 @@ int jetfp8_gemm_fwd(const uint8_t* xq, const float* xs, const uint8_t* wq, const
 
 int jetfp8_gemm_dgrad(const uint8_t* dyq, const float* dys, const uint8_t* wqT, const float* ws, void* dx_bf16,
                       int64_t M, int64_t N, int64_t K, void* stream) {
-    const int rc = check_gemm(dyq, dys, wqT, ws, dx_bf16, M, N, K, false);
+    int rc = check_gemm(dyq, dys, wqT, ws, dx_bf16, M, N, K, false);
+    if (rc == JETFP8_OK) rc = check_gemm_extent(M, K, N);
     if (rc != JETFP8_OK) return rc;
     return hip_status(jetfp8::launch_gemm_block_scaled_b(dyq, dys, wqT, ws, static_cast<uint16_t*>(dx_bf16), M, K, N,
                                                          1, K / 128, static_cast<hipStream_t>(stream)));
@@ -83,7 +94,8 @@ int jetfp8_gemm_dgrad(const uint8_t* dyq, const float* dys, const uint8_t* wqT, 
 
 int jetfp8_gemm_wgrad(const uint8_t* dyqT, const float* dysT, const uint8_t* xqT, const float* xsT, void* dw_bf16,
                       int64_t M, int64_t N, int64_t K, void* stream) {
-    const int rc = check_gemm(dyqT, dysT, xqT, xsT, dw_bf16, M, N, K, true);
+    int rc = check_gemm(dyqT, dysT, xqT, xsT, dw_bf16, M, N, K, true);
+    if (rc == JETFP8_OK) rc = check_gemm_extent(N, K, M);
     if (rc != JETFP8_OK) return rc;
     return hip_status(jetfp8::launch_gemm_row_scaled_b(dyqT, dysT, xqT, xsT, static_cast<uint16_t*>(dw_bf16), N, K, M,
                                                        static_cast<hipStream_t>(stream)));

@@ -11,11 +11,12 @@
 //
 // Layout of the work (large-M kernel):
 //   - 512 threads = 8 waves (2 per SIMD), block tile 256 x 128, wave tile 64 x 64 (4 x 4 MFMA tiles);
-//   - A and B group tiles stream global -> LDS with global_load_lds_dwordx4 into a double buffer (one
-//     barrier per group); LDS rows are 128 bytes with 16-byte chunk c of row r stored at c ^ ((r >> 1) & 7),
-//     which makes both the 16-lane fragment reads and the lane-ordered LDS writes bank-conflict free;
-//   - block-scaled B (forward, DGrad): s = fl32(sa * sb) is formed once per row and group in LDS, so the
-//     VALU does one fma per output per group; row-scaled B (WGrad): the lanes form sa * sb per element;
+//   - A and B group tiles and their scales stream global -> LDS with global_load_lds into a 3-stage ring
+//     (two groups in flight while one is multiplied, one barrier per group);
+//   - LDS rows are 128 bytes with the 16-byte chunk c of row r stored at c ^ ((r >> 1) & 7), which makes
+//     both the 16-lane fragment reads and the lane-ordered LDS writes bank-conflict free;
+//   - block-scaled B (forward, DGrad): s = fl32(sa * sb) per row and group (the block scale is uniform over
+//     the tile); row-scaled B (WGrad): sa * sb per element;
 //   - blocks are renumbered so that each XCD (8 per device, dispatched round robin) works on a compact
 //     band of output tiles that share A rows and B rows in its L2.
 #include "jetfp8_common.h"
@@ -38,7 +39,19 @@ constexpr int BK = 128;            // one quantization group along the contracti
 constexpr int L_BM = 256, L_BN = 128, L_THREADS = 512;
 constexpr int L_A_BYTES = L_BM * BK, L_B_BYTES = L_BN * BK;
 
-__device__ __forceinline__ int swz_off(int r, int c) { return r * BK + ((c ^ ((r >> 1) & 7)) << 4); }
+// s_waitcnt immediates (gfx9 encoding: vmcnt [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
+constexpr int kWaitVm6Lgkm0 = 6 | (7 << 4);   // vmcnt <= 6, lgkmcnt == 0, expcnt not waited on
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+// Raw buffer descriptor over [base, base + bytes) (stride 0, range-checked: loads past the end return
+// zero).  base and bytes must be block-uniform values (scalar registers); then so is the descriptor.
+// bytes < 2^31 is guaranteed by the host-side shape limits (kMaxGemmBand).
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+#define JETFP8_BUFFER_LOAD_LDS(r, lds, size, voffset, soffset) \
+    __builtin_amdgcn_raw_ptr_buffer_load_lds((r), (lds), (size), (voffset), (soffset), 0, 0)
 
 // Renumber a 1-D block index so that XCD x (which receives blocks x, x+8, ...) owns a contiguous range of
 // tiles, then walk tiles in bands of `group_m` tile-rows, N fastest inside a band.
@@ -55,67 +68,82 @@ __device__ __forceinline__ void tile_of_block(int pid, int tiles_m, int tiles_n,
     tn = w / gsz;
 }
 
+// One ring stage: A tile, B tile and the scales of one group.  Three distinct LDS objects (not one array
+// indexed by a run-time stage) let the compiler see that the stage being filled by the direct-to-LDS loads
+// is not the stage being read, so it does not drain the loads before every LDS read.
+struct __attribute__((aligned(1024))) LargeStage {
+    uint8_t a[L_A_BYTES];
+    uint8_t b[L_B_BYTES];
+    float sa[L_BM];    // row scales of A
+    float sb[L_BN];    // row scales of B (WGrad)
+};
+
 template <bool ROW_SCALED_B>
 __global__ __launch_bounds__(L_THREADS, 1) void gemm_large_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ As, const uint8_t* __restrict__ B,
     const float* __restrict__ Bs, uint16_t* __restrict__ Cout, int64_t I, int64_t J, int64_t Kc, int64_t sbj,
     int64_t sbg, int tiles_m, int tiles_n) {
-    __shared__ __attribute__((aligned(1024))) uint8_t lds_a[2][L_A_BYTES];
-    __shared__ __attribute__((aligned(1024))) uint8_t lds_b[2][L_B_BYTES];
-    __shared__ __attribute__((aligned(16))) float lds_s[2][L_BM];      // s (block B) or sa (row B)
-    __shared__ __attribute__((aligned(16))) float lds_sb[2][L_BN];     // sb (row B only)
+    // 3-deep ring: while group g is multiplied, groups g+1 and g+2 are in flight.
+    __shared__ LargeStage stage0, stage1, stage2;
 
-    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int t = threadIdx.x, lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);     // wave-uniform, kept in scalar registers
     const int wm = wave >> 1, wn = wave & 1;
     int tmi, tni;
     tile_of_block(blockIdx.x, tiles_m, tiles_n, tmi, tni);
+    // the tile index is block-uniform; the integer divisions above run on the vector unit, so say so
+    tmi = __builtin_amdgcn_readfirstlane(tmi);
+    tni = __builtin_amdgcn_readfirstlane(tni);
     const int64_t i0 = (int64_t)tmi * L_BM, j0 = (int64_t)tni * L_BN;
     const int G = (int)(Kc / BK);
+    // rows past I re-read the last row (32-bit scalar arithmetic: all dims are < 2^31)
+    const int rows_left = (int)I - tmi * L_BM;
+    const uint32_t last_row = (uint32_t)(rows_left < L_BM ? rows_left - 1 : L_BM - 1);
 
-    // ---- global -> LDS staging addresses.  Instruction c of wave w fills the 1 KB LDS region
-    //      (c * 8 + w), i.e. rows 8 * (c * 8 + w) .. +7; lane l lands at row +l/8, physical chunk l%8.
+    // ---- global -> LDS staging with buffer loads: a scalar descriptor per operand (base = the block's row
+    //      band, size = its valid bytes, so any stray offset reads zero instead of faulting), a
+    //      loop-invariant 32-bit lane offset, and the group step as the scalar offset.  Instruction c of
+    //      wave w fills the 1 KB LDS region (c * 8 + w), i.e. rows 8 * (c * 8 + w) .. +7; lane l lands at
+    //      row +l/8, physical chunk l%8.
     const int lrow = lane >> 3, pchunk = lane & 7;
-    const uint8_t* ga[4];
+    const rsrc_t ra = make_rsrc(A + i0 * Kc, (int)(last_row + 1) * (int)Kc);
+    const rsrc_t rb = make_rsrc(B + j0 * Kc, L_BN * (int)Kc);
+    uint32_t oa[4], ob[2];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-        const int r = (c * 8 + wave) * 8 + lrow;
-        const int lc = pchunk ^ ((r >> 1) & 7);
-        const int64_t gr = (i0 + r < I) ? i0 + r : I - 1;     // rows past I re-read row I-1, never stored
-        ga[c] = A + gr * Kc + lc * 16;
+        const uint32_t r = (c * 8 + wave) * 8 + lrow;
+        const uint32_t lc = pchunk ^ ((r >> 1) & 7);
+        oa[c] = min(r, last_row) * (uint32_t)Kc + lc * 16;   // rows past I re-read the last row, never stored
     }
-    const uint8_t* gb[2];
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
-        const int r = (c * 8 + wave) * 8 + lrow;
-        const int lc = pchunk ^ ((r >> 1) & 7);
-        gb[c] = B + (j0 + r) * Kc + lc * 16;
+        const uint32_t r = (c * 8 + wave) * 8 + lrow;
+        const uint32_t lc = pchunk ^ ((r >> 1) & 7);
+        ob[c] = r * (uint32_t)Kc + lc * 16;
     }
-    auto issue_tiles = [&](int g, int stage) {
-        const int64_t go = (int64_t)g * BK;
+    // scale rows: waves 0..3 bring 64 A-row scales each, waves 4..5 (row-scaled B) 64 B-row scales each,
+    // one dword per lane, straight into LDS.  Issued before the tiles, so that "all but the last 6 memory
+    // operations done" means "this group complete" for every wave.
+    const bool has_scale_load = wave < 4 || (ROW_SCALED_B && wave < 6);
+    const rsrc_t rs = (wave < 4) ? make_rsrc(As + i0, (G * (int)I - (int)i0) * 4)
+                                 : make_rsrc(Bs + j0, (G * (int)J - (int)j0) * 4);
+    const uint32_t sstep = (uint32_t)((wave < 4) ? I : J) * 4;
+    const uint32_t os = 4 * ((wave < 4) ? min((uint32_t)(wave * 64 + lane), last_row) : (uint32_t)((wave - 4) * 64 + lane));
+    auto issue = [&](int g, LargeStage& S) {
+        if (has_scale_load) {
+            float* dst = (wave < 4) ? &S.sa[wave * 64] : &S.sb[(wave - 4) * 64];
+            JETFP8_BUFFER_LOAD_LDS(rs, (lds_void*)dst, 4, (int)os, (int)((uint32_t)g * sstep));
+        }
+        const uint32_t go = (uint32_t)g * BK;
 #pragma unroll
         for (int c = 0; c < 4; ++c)
-            __builtin_amdgcn_global_load_lds(ga[c] + go, (lds_void*)(&lds_a[stage][(c * 8 + wave) * 1024]), 16, 0, 0);
+            JETFP8_BUFFER_LOAD_LDS(ra, (lds_void*)(&S.a[(c * 8 + wave) * 1024]), 16, (int)oa[c], (int)go);
 #pragma unroll
         for (int c = 0; c < 2; ++c)
-            __builtin_amdgcn_global_load_lds(gb[c] + go, (lds_void*)(&lds_b[stage][(c * 8 + wave) * 1024]), 16, 0, 0);
+            JETFP8_BUFFER_LOAD_LDS(rb, (lds_void*)(&S.b[(c * 8 + wave) * 1024]), 16, (int)ob[c], (int)go);
     };
-
-    // ---- scale staging: thread t < 256 owns row i0 + t; for row-scaled B, threads 256..383 own column
-    //      j0 + t - 256.  Values for group g + 1 are loaded into registers during group g - 1's compute.
-    const int64_t srow = (i0 + (t & 255) < I) ? i0 + (t & 255) : I - 1;
-    auto load_scales = [&](int g, float& a, float& b) {
-        a = As[(int64_t)g * I + srow];
-        if (ROW_SCALED_B) b = (t >= 256 && t < 384) ? Bs[(int64_t)g * J + j0 + (t - 256)] : 0.0f;
-        else b = Bs[(j0 / 128) * sbj + (int64_t)g * sbg];
-    };
-    auto store_scales = [&](int stage, float a, float b) {
-        if (ROW_SCALED_B) {
-            if (t < 256) lds_s[stage][t] = a;
-            else if (t < 384) lds_sb[stage][t - 256] = b;
-        } else if (t < 256) {
-            lds_s[stage][t] = a * b;                           // s = fl32(sa * sb), once per row and group
-        }
-    };
+    // block-scaled B: one scale per (128-block of B rows, group), uniform over the block tile
+    auto block_scale = [&](int g) -> float { return Bs[(j0 / 128) * sbj + (int64_t)g * sbg]; };
 
     v4f acc[4][4];
 #pragma unroll
@@ -123,63 +151,98 @@ __global__ __launch_bounds__(L_THREADS, 1) void gemm_large_kernel(
 #pragma unroll
         for (int b = 0; b < 4; ++b) acc[a][b] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
 
-    // prologue: group 0 tiles and scales, group 1 scales in registers
-    issue_tiles(0, 0);
-    float sa_n, sb_n;
-    load_scales(0, sa_n, sb_n);
-    store_scales(0, sa_n, sb_n);
-    if (G > 1) load_scales(1, sa_n, sb_n);
-
     const int qrow = 4 * (lane >> 4);      // first output row of this lane inside a 16x16 tile
     const int qcol = lane & 15;            // output column of this lane inside a 16x16 tile
-    const int cp = 2 * (lane >> 4);        // logical 16-byte chunk pair of this lane's fragment bytes
+    // Fragment bytes of this lane: row (lane & 15) of each 16-row tile, logical chunks cp and cp + 1.  The
+    // tile's first row is a multiple of 16, so the swizzle depends on (lane & 15) only and consecutive
+    // tiles are 2048 bytes apart: one base offset per chunk, tiles by immediate offsets.
+    const uint32_t rl = lane & 15, cp = 2 * (lane >> 4), swz = (rl >> 1) & 7;
+    const uint32_t fa0 = (wm * 64 + rl) * BK + ((cp ^ swz) << 4), fa1 = (wm * 64 + rl) * BK + (((cp + 1) ^ swz) << 4);
+    const uint32_t fb0 = (wn * 64 + rl) * BK + ((cp ^ swz) << 4), fb1 = (wn * 64 + rl) * BK + (((cp + 1) ^ swz) << 4);
 
-    for (int g = 0; g < G; ++g) {
-        const int st = g & 1;
-        __builtin_amdgcn_s_waitcnt(0);     // this thread's tile loads (and scale loads) have landed
-        __syncthreads();                   // ... everyone's; and the other stage is no longer read
-        if (g + 1 < G) {
-            issue_tiles(g + 1, st ^ 1);
-            store_scales(st ^ 1, sa_n, sb_n);
-            if (g + 2 < G) load_scales(g + 2, sa_n, sb_n);
-        }
+    // One group: wait for its stage, refill the stage read one group ago, multiply.
+    auto step = [&](int g, LargeStage& S, LargeStage& refill, float sbv) {
+        __builtin_amdgcn_sched_barrier(0);   // keep each group's code in place (bounded register pressure)
+        // this wave's loads of group g landed (only group g+1's six tile loads may still be in flight),
+        // this wave's LDS reads of group g-1 returned; then every wave of the block is past that point
+        if (g + 1 < G) __builtin_amdgcn_s_waitcnt(kWaitVm6Lgkm0);
+        else __builtin_amdgcn_s_waitcnt(0);
+        __builtin_amdgcn_s_barrier();
+        if (g + 2 < G) issue(g + 2, refill);
 
         // scales of this lane's 16 rows (and 4 columns for row-scaled B)
         v4f s4[4];
 #pragma unroll
-        for (int tm = 0; tm < 4; ++tm) s4[tm] = *reinterpret_cast<const v4f*>(&lds_s[st][wm * 64 + tm * 16 + qrow]);
+        for (int tm = 0; tm < 4; ++tm) {
+            s4[tm] = *reinterpret_cast<const v4f*>(&S.sa[wm * 64 + tm * 16 + qrow]);
+            if (!ROW_SCALED_B) s4[tm] = s4[tm] * sbv;          // s = fl32(sa * sb)
+        }
         float sbc[4];
         if (ROW_SCALED_B) {
 #pragma unroll
-            for (int tn = 0; tn < 4; ++tn) sbc[tn] = lds_sb[st][wn * 64 + tn * 16 + qcol];
+            for (int tn = 0; tn < 4; ++tn) sbc[tn] = S.sb[wn * 64 + tn * 16 + qcol];
         }
-
         v8i bfr[4];
 #pragma unroll
         for (int tn = 0; tn < 4; ++tn) {
-            const int r = wn * 64 + tn * 16 + (lane & 15);
-            const uint4 lo = *reinterpret_cast<const uint4*>(&lds_b[st][swz_off(r, cp)]);
-            const uint4 hi = *reinterpret_cast<const uint4*>(&lds_b[st][swz_off(r, cp + 1)]);
+            const uint4 lo = *reinterpret_cast<const uint4*>(&S.b[fb0 + tn * 2048]);
+            const uint4 hi = *reinterpret_cast<const uint4*>(&S.b[fb1 + tn * 2048]);
             bfr[tn] = (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
         }
-#pragma unroll
-        for (int tm = 0; tm < 4; ++tm) {
-            const int r = wm * 64 + tm * 16 + (lane & 15);
-            const uint4 lo = *reinterpret_cast<const uint4*>(&lds_a[st][swz_off(r, cp)]);
-            const uint4 hi = *reinterpret_cast<const uint4*>(&lds_a[st][swz_off(r, cp + 1)]);
-            const v8i af = (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-            v4f p[4];
-#pragma unroll
-            for (int tn = 0; tn < 4; ++tn) p[tn] = mfma_group(af, bfr[tn]);
+        auto a_frag = [&](int tm) -> v8i {
+            const uint4 lo = *reinterpret_cast<const uint4*>(&S.a[fa0 + tm * 2048]);
+            const uint4 hi = *reinterpret_cast<const uint4*>(&S.a[fa1 + tm * 2048]);
+            return (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        };
+        auto promote = [&](int tm, const v4f* p) {
 #pragma unroll
             for (int tn = 0; tn < 4; ++tn)
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
-                    const float s = ROW_SCALED_B ? s4[tm][v] * sbc[tn] : s4[tm][v];
-                    acc[tm][tn][v] = fmaf(p[tn][v], s, acc[tm][tn][v]);
+                    const float sc = ROW_SCALED_B ? s4[tm][v] * sbc[tn] : s4[tm][v];
+                    acc[tm][tn][v] = fmaf(p[tn][v], sc, acc[tm][tn][v]);
                 }
-        }
+            // pin the promotion here: without this the compiler sinks it below later matrix ops and keeps
+            // every group product alive at once
+#pragma unroll
+            for (int tn = 0; tn < 4; ++tn) asm volatile("" : "+v"(acc[tm][tn]));
+        };
+        // software pipeline over the 4 row tiles: the matrix ops of tile tm+1 run while tile tm is promoted
+        v4f pa[4], pb[4];
+        v8i af = a_frag(0);
+#pragma unroll
+        for (int tn = 0; tn < 4; ++tn) pa[tn] = mfma_group(af, bfr[tn]);
+        af = a_frag(1);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int tn = 0; tn < 4; ++tn) pb[tn] = mfma_group(af, bfr[tn]);
+        af = a_frag(2);
+        promote(0, pa);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int tn = 0; tn < 4; ++tn) pa[tn] = mfma_group(af, bfr[tn]);
+        af = a_frag(3);
+        promote(1, pb);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int tn = 0; tn < 4; ++tn) pb[tn] = mfma_group(af, bfr[tn]);
+        promote(2, pa);
+        __builtin_amdgcn_sched_barrier(0);
+        promote(3, pb);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    issue(0, stage0);
+    if (G > 1) issue(1, stage1);
+    // ring positions: group g lives in stage g % 3; at group g the stage of group g - 1 is refilled
+    int g = 0;
+    for (; g + 3 <= G; g += 3) {
+        step(g, stage0, stage2, ROW_SCALED_B ? 0.0f : block_scale(g));
+        step(g + 1, stage1, stage0, ROW_SCALED_B ? 0.0f : block_scale(g + 1));
+        step(g + 2, stage2, stage1, ROW_SCALED_B ? 0.0f : block_scale(g + 2));
     }
+    if (g < G) step(g, stage0, stage2, ROW_SCALED_B ? 0.0f : block_scale(g));
+    if (g + 1 < G) step(g + 1, stage1, stage0, ROW_SCALED_B ? 0.0f : block_scale(g + 1));
 
     // epilogue: bf16, round to nearest even
 #pragma unroll

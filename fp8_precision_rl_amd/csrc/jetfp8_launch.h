@@ -5,6 +5,10 @@
 
 namespace jetfp8 {
 
+// The GEMM kernels address a block's operand band (256 rows x contraction bytes) and a scale array
+// (groups x rows x 4 bytes) through 32-bit buffer offsets; the C ABI rejects shapes beyond this.
+constexpr int64_t kMaxGemmBand = ((int64_t)1 << 31) - 1;
+
 hipError_t launch_quant_rows(const uint16_t* x, int64_t R, int64_t C, uint8_t* q, float* s, hipStream_t st);
 hipError_t launch_quant_cols_t(const uint16_t* x, int64_t R, int64_t C, uint8_t* qT, float* sT, hipStream_t st);
 hipError_t launch_quant_blocks(const uint16_t* x, int64_t R, int64_t C, uint8_t* q, float* s, uint8_t* qT,

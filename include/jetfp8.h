@@ -31,7 +31,9 @@
  *     been enqueued).  No exception ever crosses this interface.
  *   - All pointers must be 16-byte aligned (JETFP8_ERR_ALIGN otherwise).  Buffers must not overlap.
  *   - Sizes: every dimension >= 1; every grouped or contraction axis a multiple of 128, plus the
- *     per-mode rules below (JETFP8_ERR_SHAPE otherwise); every dimension < 2^31.
+ *     per-mode rules below (JETFP8_ERR_SHAPE otherwise); every dimension < 2^31.  GEMMs additionally
+ *     need 256 * (contraction length) < 2^31 and (contraction length / 128) * (rows of either operand)
+ *     * 4 < 2^31 bytes of scales (they address operand bands and scale arrays with 32-bit offsets).
  *   - Thread safety: calls are independent; concurrent calls on different streams are allowed.
  */
 #ifndef JETFP8_H
