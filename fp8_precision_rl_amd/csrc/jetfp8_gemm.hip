@@ -10,11 +10,11 @@
 // not depend on the tile an element lands in, so a row's bits do not depend on M.
 //
 // Layout of the work (large-M kernel):
-//   - 512 threads = 8 waves (2 per SIMD), block tile 256 x 128, wave tile 64 x 64 (4 x 4 MFMA tiles);
-//   - A and B group tiles and their scales stream global -> LDS with global_load_lds into a 3-stage ring
-//     (two groups in flight while one is multiplied, one barrier per group);
-//   - LDS rows are 128 bytes with the 16-byte chunk c of row r stored at c ^ ((r >> 1) & 7), which makes
-//     both the 16-lane fragment reads and the lane-ordered LDS writes bank-conflict free;
+//   - 512 threads = 8 waves (2 per SIMD), block tile 256 x 256, wave tile 128 x 64 (8 x 4 MFMA tiles), so
+//     each fragment byte read from LDS feeds 2.7 matrix ops on average (LDS bandwidth is the tight resource);
+//   - A and B group tiles and their scales stream global -> LDS with buffer_load ... lds into a 2-stage
+//     ring (one group in flight while one is multiplied, one barrier per group);
+//   - LDS rows are 128 bytes with the 16-byte chunks of a row XOR-permuted (see swz) for the fragment reads;
 //   - block-scaled B (forward, DGrad): s = fl32(sa * sb) per row and group (the block scale is uniform over
 //     the tile); row-scaled B (WGrad): sa * sb per element;
 //   - blocks are renumbered so that each XCD (8 per device, dispatched round robin) works on a compact
@@ -37,16 +37,13 @@ __device__ __forceinline__ v4f mfma_group(const v8i& a, const v8i& b) {
 }
 
 constexpr int BK = 128;            // one quantization group along the contraction axis
-constexpr int L_BM = 256, L_BN = 128, L_THREADS = 512;
+constexpr int L_BM = 256, L_BN = 256, L_THREADS = 512;
 constexpr int L_A_BYTES = L_BM * BK, L_B_BYTES = L_BN * BK;
 
 // LDS row layout: 128-byte rows, the 16-byte chunk c of row r stored at chunk c ^ swz(r).  The XOR
 // pattern was chosen by measurement on gfx950 (fragment reads at ~170 B/clk/CU against ~113 for the
 // plain c ^ (r & 7)); it depends on r & 15 only, so 16-row tiles share one pattern.
 __device__ __forceinline__ uint32_t swz(uint32_t r) { return (((r & 7) * 5) & 7) ^ ((r >> 3) & 1); }
-
-// s_waitcnt immediates (gfx9 encoding: vmcnt [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
-constexpr int kWaitVm6Lgkm0 = 6 | (7 << 4);   // vmcnt <= 6, lgkmcnt == 0, expcnt not waited on
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
@@ -74,7 +71,7 @@ __device__ __forceinline__ void tile_of_block(int pid, int tiles_m, int tiles_n,
     tn = w / gsz;
 }
 
-// One ring stage: A tile, B tile and the scales of one group.  Three distinct LDS objects (not one array
+// One ring stage: A tile, B tile and the scales of one group.  Distinct LDS objects (not one array
 // indexed by a run-time stage) let the compiler see that the stage being filled by the direct-to-LDS loads
 // is not the stage being read, so it does not drain the loads before every LDS read.
 struct __attribute__((aligned(1024))) LargeStage {
@@ -89,12 +86,12 @@ __global__ __launch_bounds__(L_THREADS, 1) void gemm_large_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ As, const uint8_t* __restrict__ B,
     const float* __restrict__ Bs, uint16_t* __restrict__ Cout, int64_t I, int64_t J, int64_t Kc, int64_t sbj,
     int64_t sbg, int tiles_m, int tiles_n) {
-    // 3-deep ring: while group g is multiplied, groups g+1 and g+2 are in flight.
-    __shared__ LargeStage stage0, stage1, stage2;
+    // 2-deep ring: while group g is multiplied, group g+1 is in flight.
+    __shared__ LargeStage stage0, stage1;
 
     const int t = threadIdx.x, lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);     // wave-uniform, kept in scalar registers
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave >> 2, wn = wave & 3;                      // wave tile: rows wm*128.., cols wn*64..
     int tmi, tni;
     tile_of_block(blockIdx.x, tiles_m, tiles_n, tmi, tni);
     // the tile index is block-uniform; the integer divisions above run on the vector unit, so say so
@@ -102,58 +99,47 @@ __global__ __launch_bounds__(L_THREADS, 1) void gemm_large_kernel(
     tni = __builtin_amdgcn_readfirstlane(tni);
     const int64_t i0 = (int64_t)tmi * L_BM, j0 = (int64_t)tni * L_BN;
     const int G = (int)(Kc / BK);
-    // rows past I re-read the last row (32-bit scalar arithmetic: all dims are < 2^31)
-    const int rows_left = (int)I - tmi * L_BM;
-    const uint32_t last_row = (uint32_t)(rows_left < L_BM ? rows_left - 1 : L_BM - 1);
+    // 32-bit scalar arithmetic: all dims are < 2^31 and operand bands < 2^31 bytes
+    const int rows_a = min((int)I - tmi * L_BM, L_BM), rows_b = min((int)J - tni * L_BN, L_BN);
 
-    // ---- global -> LDS staging with buffer loads: a scalar descriptor per operand (base = the block's row
-    //      band, size = its valid bytes, so any stray offset reads zero instead of faulting), a
-    //      loop-invariant 32-bit lane offset, and the group step as the scalar offset.  Instruction c of
-    //      wave w fills the 1 KB LDS region (c * 8 + w), i.e. rows 8 * (c * 8 + w) .. +7; lane l lands at
-    //      row +l/8, physical chunk l%8.
-    const int lrow = lane >> 3, pchunk = lane & 7;
-    const rsrc_t ra = make_rsrc(A + i0 * Kc, (int)(last_row + 1) * (int)Kc);
-    const rsrc_t rb = make_rsrc(B + j0 * Kc, L_BN * (int)Kc);
-    uint32_t oa[4], ob[2];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        const uint32_t r = (c * 8 + wave) * 8 + lrow;
-        const uint32_t lc = pchunk ^ swz(r);
-        oa[c] = min(r, last_row) * (uint32_t)Kc + lc * 16;   // rows past I re-read the last row, never stored
-    }
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-        const uint32_t r = (c * 8 + wave) * 8 + lrow;
-        const uint32_t lc = pchunk ^ swz(r);
-        ob[c] = r * (uint32_t)Kc + lc * 16;
-    }
-    // scale rows: waves 0..3 bring 64 A-row scales each, waves 4..5 (row-scaled B) 64 B-row scales each,
-    // one dword per lane, straight into LDS.  Issued before the tiles, so that "all but the last 6 memory
-    // operations done" means "this group complete" for every wave.
-    const bool has_scale_load = wave < 4 || (ROW_SCALED_B && wave < 6);
+    // ---- global -> LDS staging with buffer loads.  Each operand has a scalar descriptor over the block's
+    //      row band, so rows past I (or J) read as zero and are never stored.  Instruction c of wave w fills
+    //      the 1 KB LDS region (c * 8 + w): rows 64 c + 8 w .. +7; lane l lands at row +l/8, physical chunk
+    //      l%8.  The row's swizzle depends on r & 15 only, so one lane offset serves all c, and the c and
+    //      group terms go into the scalar offset.
+    const rsrc_t ra = make_rsrc(A + i0 * Kc, rows_a * (int)Kc);
+    const rsrc_t rb = make_rsrc(B + j0 * Kc, rows_b * (int)Kc);
+    const uint32_t r0 = wave * 8 + (lane >> 3);
+    const int ooff = (int)(r0 * (uint32_t)Kc + (((lane & 7) ^ swz(r0)) << 4));
+    const int cstep = 64 * (int)Kc;
+    // scale rows: waves 0..3 bring 64 A-row scales each, waves 4..7 (row-scaled B) 64 B-row scales each,
+    // one dword per lane, straight into LDS; out-of-range rows read as zero.
+    const bool has_scale_load = wave < 4 || ROW_SCALED_B;
     const rsrc_t rs = (wave < 4) ? make_rsrc(As + i0, (G * (int)I - (int)i0) * 4)
                                  : make_rsrc(Bs + j0, (G * (int)J - (int)j0) * 4);
-    const uint32_t sstep = (uint32_t)((wave < 4) ? I : J) * 4;
-    const uint32_t os = 4 * ((wave < 4) ? min((uint32_t)(wave * 64 + lane), last_row) : (uint32_t)((wave - 4) * 64 + lane));
+    const int sstep = ((wave < 4) ? (int)I : (int)J) * 4;
+    const int os = ((wave & 3) * 64 + lane) * 4;
     auto issue = [&](int g, LargeStage& S) {
         if (has_scale_load) {
             float* dst = (wave < 4) ? &S.sa[wave * 64] : &S.sb[(wave - 4) * 64];
-            JETFP8_BUFFER_LOAD_LDS(rs, (lds_void*)dst, 4, (int)os, (int)((uint32_t)g * sstep));
+            JETFP8_BUFFER_LOAD_LDS(rs, (lds_void*)dst, 4, os, g * sstep);
         }
-        const uint32_t go = (uint32_t)g * BK;
+        const int go = g * BK;
 #pragma unroll
         for (int c = 0; c < 4; ++c)
-            JETFP8_BUFFER_LOAD_LDS(ra, (lds_void*)(&S.a[(c * 8 + wave) * 1024]), 16, (int)oa[c], (int)go);
+            JETFP8_BUFFER_LOAD_LDS(ra, (lds_void*)(&S.a[(c * 8 + wave) * 1024]), 16, ooff, go + c * cstep);
 #pragma unroll
-        for (int c = 0; c < 2; ++c)
-            JETFP8_BUFFER_LOAD_LDS(rb, (lds_void*)(&S.b[(c * 8 + wave) * 1024]), 16, (int)ob[c], (int)go);
+        for (int c = 0; c < 4; ++c)
+            JETFP8_BUFFER_LOAD_LDS(rb, (lds_void*)(&S.b[(c * 8 + wave) * 1024]), 16, ooff, go + c * cstep);
     };
-    // block-scaled B: one scale per (128-block of B rows, group), uniform over the block tile
-    auto block_scale = [&](int g) -> float { return Bs[(j0 / 128) * sbj + (int64_t)g * sbg]; };
+    // block-scaled B: one scale per (128-block of B rows, group); a wave's 64 columns lie in one block.
+    // Columns past J (last tile when J is an odd multiple of 128) use the last block: never stored.
+    const int64_t bblk = min<int64_t>((j0 + wn * 64) / 128, J / 128 - 1);
+    auto block_scale = [&](int g) -> float { return Bs[bblk * sbj + (int64_t)g * sbg]; };
 
-    v4f acc[4][4];
+    v4f acc[8][4];
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < 8; ++a)
 #pragma unroll
         for (int b = 0; b < 4; ++b) acc[a][b] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
 
@@ -162,25 +148,24 @@ __global__ __launch_bounds__(L_THREADS, 1) void gemm_large_kernel(
     // tile's first row is a multiple of 16, so the swizzle depends on (lane & 15) only and consecutive
     // tiles are 2048 bytes apart: one base offset per chunk, tiles by immediate offsets.
     const uint32_t rl = lane & 15, cp = 2 * (lane >> 4), sw = swz(rl);
-    const uint32_t fa0 = (wm * 64 + rl) * BK + ((cp ^ sw) << 4), fa1 = (wm * 64 + rl) * BK + (((cp + 1) ^ sw) << 4);
+    const uint32_t fa0 = (wm * 128 + rl) * BK + ((cp ^ sw) << 4), fa1 = (wm * 128 + rl) * BK + (((cp + 1) ^ sw) << 4);
     const uint32_t fb0 = (wn * 64 + rl) * BK + ((cp ^ sw) << 4), fb1 = (wn * 64 + rl) * BK + (((cp + 1) ^ sw) << 4);
 
-    // One group: wait for its stage, refill the stage read one group ago, multiply.
+    // One group: wait for its stage, refill the other stage (read one group ago), multiply.
     auto step = [&](int g, LargeStage& S, LargeStage& refill, float sbv) {
         __builtin_amdgcn_sched_barrier(0);   // keep each group's code in place (bounded register pressure)
-        // this wave's loads of group g landed (only group g+1's six tile loads may still be in flight),
-        // this wave's LDS reads of group g-1 returned; then every wave of the block is past that point
-        if (g + 1 < G) __builtin_amdgcn_s_waitcnt(kWaitVm6Lgkm0);
-        else __builtin_amdgcn_s_waitcnt(0);
+        // this wave's loads of group g landed and its LDS reads of group g-1 returned; then every wave of
+        // the block is past that point
+        __builtin_amdgcn_s_waitcnt(0);
         __builtin_amdgcn_s_barrier();
-        if (g + 2 < G) issue(g + 2, refill);
+        if (g + 1 < G) issue(g + 1, refill);
 
         // The matrix op takes the B fragment as its first operand, so lane l holds output row (l & 15) of
         // each 16-row tile and the 4 consecutive columns 4 * (l >> 4) .. +3: one A-row scale per tile.
-        float s1[4];
+        float s1[8];
 #pragma unroll
-        for (int tm = 0; tm < 4; ++tm) {
-            s1[tm] = S.sa[wm * 64 + tm * 16 + rl];
+        for (int tm = 0; tm < 8; ++tm) {
+            s1[tm] = S.sa[wm * 128 + tm * 16 + rl];
             if (!ROW_SCALED_B) s1[tm] = s1[tm] * sbv;            // s = fl32(sa * sb)
         }
         v4f sb4[4];
@@ -213,54 +198,53 @@ __global__ __launch_bounds__(L_THREADS, 1) void gemm_large_kernel(
 #pragma unroll
             for (int tn = 0; tn < 4; ++tn) asm volatile("" : "+v"(acc[tm][tn]));
         };
-        // software pipeline over the 4 row tiles: the matrix ops of tile tm+1 run while tile tm is promoted
+        // software pipeline over the 8 row tiles: the matrix ops of tile tm+1 run while tile tm is promoted
         v4f pa[4], pb[4];
         v8i af = a_frag(0);
 #pragma unroll
         for (int tn = 0; tn < 4; ++tn) pa[tn] = mfma_group(bfr[tn], af);
-        af = a_frag(1);
-        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int tn = 0; tn < 4; ++tn) pb[tn] = mfma_group(bfr[tn], af);
-        af = a_frag(2);
-        promote(0, pa);
-        __builtin_amdgcn_sched_barrier(0);
+        for (int tm = 1; tm < 8; ++tm) {
+            af = a_frag(tm);
+            __builtin_amdgcn_sched_barrier(0);
+            if (tm & 1) {
 #pragma unroll
-        for (int tn = 0; tn < 4; ++tn) pa[tn] = mfma_group(bfr[tn], af);
-        af = a_frag(3);
-        promote(1, pb);
-        __builtin_amdgcn_sched_barrier(0);
+                for (int tn = 0; tn < 4; ++tn) pb[tn] = mfma_group(bfr[tn], af);
+                promote(tm - 1, pa);
+            } else {
 #pragma unroll
-        for (int tn = 0; tn < 4; ++tn) pb[tn] = mfma_group(bfr[tn], af);
-        promote(2, pa);
+                for (int tn = 0; tn < 4; ++tn) pa[tn] = mfma_group(bfr[tn], af);
+                promote(tm - 1, pb);
+            }
+        }
         __builtin_amdgcn_sched_barrier(0);
-        promote(3, pb);
+        promote(7, pb);
         __builtin_amdgcn_sched_barrier(0);
     };
 
     issue(0, stage0);
-    if (G > 1) issue(1, stage1);
-    // ring positions: group g lives in stage g % 3; at group g the stage of group g - 1 is refilled
     int g = 0;
-    for (; g + 3 <= G; g += 3) {
-        step(g, stage0, stage2, ROW_SCALED_B ? 0.0f : block_scale(g));
+    for (; g + 2 <= G; g += 2) {
+        step(g, stage0, stage1, ROW_SCALED_B ? 0.0f : block_scale(g));
         step(g + 1, stage1, stage0, ROW_SCALED_B ? 0.0f : block_scale(g + 1));
-        step(g + 2, stage2, stage1, ROW_SCALED_B ? 0.0f : block_scale(g + 2));
     }
-    if (g < G) step(g, stage0, stage2, ROW_SCALED_B ? 0.0f : block_scale(g));
-    if (g + 1 < G) step(g + 1, stage1, stage0, ROW_SCALED_B ? 0.0f : block_scale(g + 1));
+    if (g < G) step(g, stage0, stage1, ROW_SCALED_B ? 0.0f : block_scale(g));
 
-    // epilogue: bf16, round to nearest even; each lane writes 4 consecutive columns (8 bytes) per tile
+    // epilogue: bf16, round to nearest even; each lane writes 4 consecutive columns (8 bytes) per tile.
+    // J is a multiple of 128, so a lane's 4 columns are either all inside J or all outside.
 #pragma unroll
-    for (int tm = 0; tm < 4; ++tm) {
-        const int64_t r = i0 + wm * 64 + tm * 16 + rl;
+    for (int tm = 0; tm < 8; ++tm) {
+        const int64_t r = i0 + wm * 128 + tm * 16 + rl;
         if (r < I) {
 #pragma unroll
             for (int tn = 0; tn < 4; ++tn) {
-                uint2 w;
-                w.x = f32_to_bf16_rne(acc[tm][tn][0]) | (f32_to_bf16_rne(acc[tm][tn][1]) << 16);
-                w.y = f32_to_bf16_rne(acc[tm][tn][2]) | (f32_to_bf16_rne(acc[tm][tn][3]) << 16);
-                *reinterpret_cast<uint2*>(&Cout[r * J + j0 + wn * 64 + tn * 16 + qc4]) = w;
+                const int64_t c = j0 + wn * 64 + tn * 16 + qc4;
+                if (c < J) {
+                    uint2 w;
+                    w.x = f32_to_bf16_rne(acc[tm][tn][0]) | (f32_to_bf16_rne(acc[tm][tn][1]) << 16);
+                    w.y = f32_to_bf16_rne(acc[tm][tn][2]) | (f32_to_bf16_rne(acc[tm][tn][3]) << 16);
+                    *reinterpret_cast<uint2*>(&Cout[r * J + c]) = w;
+                }
             }
         }
     }
@@ -269,7 +253,7 @@ __global__ __launch_bounds__(L_THREADS, 1) void gemm_large_kernel(
 template <bool ROW_SCALED_B>
 static hipError_t launch_large(const uint8_t* A, const float* As, const uint8_t* B, const float* Bs, uint16_t* C,
                                int64_t I, int64_t J, int64_t Kc, int64_t sbj, int64_t sbg, hipStream_t st) {
-    const int tiles_m = (int)((I + L_BM - 1) / L_BM), tiles_n = (int)(J / L_BN);
+    const int tiles_m = (int)((I + L_BM - 1) / L_BM), tiles_n = (int)((J + L_BN - 1) / L_BN);
     hipLaunchKernelGGL(gemm_large_kernel<ROW_SCALED_B>, dim3(tiles_m * tiles_n), dim3(L_THREADS), 0, st, A, As, B,
                        Bs, C, I, J, Kc, sbj, sbg, tiles_m, tiles_n);
     return hipGetLastError();
