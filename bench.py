@@ -36,10 +36,43 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="llama3_8b_train_m16384")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-sample-rows", type=int, default=64)
+    p.add_argument("--cpu-sample-rows", type=int, default=128)
     p.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "gemm_traffic.json"),
                    help="per-launch HBM bytes measured by rocprofv3 for this workload (optional)")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="first run a 1 GiB device-to-device copy (known bytes) to scale rocprofv3 byte counters")
     return p.parse_args()
+
+
+GEMM_SOURCE = os.path.join(ROOT, "fp8_precision_rl_amd", "csrc", "jetfp8_gemm.hip")
+
+
+def source_digest(path=GEMM_SOURCE) -> str:
+    import hashlib
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()
+
+
+def recorded_traffic(path, workload):
+    """HBM bytes per GEMM launch recorded from rocprofv3 FETCH_SIZE / WRITE_SIZE runs (scaled by a copy
+    kernel of known size), or None when absent, for another workload, or taken on a different kernel."""
+    try:
+        tj = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    if tj.get("workload") != workload or tj.get("kernel_source_sha256") != source_digest():
+        return None
+    return tj.get("gemm_bytes_per_launch")
+
+
+def copy_calibration(torch):
+    """1 GiB uint8 device copy, twice: reads and writes exactly 2^30 bytes per launch."""
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
 
 
 class Linear:
@@ -152,6 +185,8 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(3)
     wl = workloads.WORKLOADS[args.workload]
+    if args.calibrate_copy:
+        copy_calibration(torch)
     layers = [Linear(wl, i, torch, workloads) for i in range(len(wl.linears))]
     torch.cuda.synchronize()
     st = torch.cuda.current_stream()
@@ -191,14 +226,7 @@ def main():
         per.setdefault(key, [0.0, 0.0])
         per[key][0] += a.elapsed_time(b)
         per[key][1] += amt
-    traffic = None
-    if os.path.exists(args.traffic_json):
-        try:
-            tj = json.load(open(args.traffic_json))
-            if tj.get("workload") == wl.name:
-                traffic = tj.get("gemm_bytes_per_launch")
-        except (OSError, ValueError):
-            traffic = None
+    traffic = recorded_traffic(args.traffic_json, wl.name)
 
     out = {
         "metric": METRIC,
@@ -221,7 +249,7 @@ def main():
         "pct_of_fp8_peak": round(100 * value / FP8_PEAK_TFLOPS, 2),
         "gemm_only_tflops": round(achieved, 2),
         "wall_s": round(wall, 4),
-        "roofline": {"bound": "mfma", "kernel": "gemm_nt_kernel (fwd, dgrad, wgrad)", "achieved": round(achieved, 2),
+        "roofline": {"bound": "mfma", "kernel": "gemm_large_kernel (fwd, dgrad, wgrad)", "achieved": round(achieved, 2),
                      "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / FP8_PEAK_TFLOPS, 4),
                      "traffic": traffic, "launches": n_gemm,
                      "mean_launch_us": round(1e3 * gemm_ms / max(n_gemm, 1), 2),
