@@ -81,61 +81,77 @@ struct __attribute__((aligned(1024))) LargeStage {
     float sb[L_BN];    // row scales of B (WGrad)
 };
 
+// Per-tile values shared by the block: output tile coordinates and the buffer descriptors of the tile's
+// operand bands and scale rows.  Built from block-uniform values only, so everything stays in scalar
+// registers.
+struct TileCtx {
+    int tmi, tni;          // tile row / column
+    int i0, j0;            // first output row / column
+    rsrc_t ra, rb;         // A rows i0 .. i0+255, B rows j0 .. j0+255 (clipped to I, J)
+    rsrc_t rsa, rsb;       // A-row scales from i0; B-row scales from j0 (row-scaled B only)
+};
+
 template <bool ROW_SCALED_B>
 __global__ __launch_bounds__(L_THREADS, 1) void gemm_large_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ As, const uint8_t* __restrict__ B,
     const float* __restrict__ Bs, uint16_t* __restrict__ Cout, int64_t I, int64_t J, int64_t Kc, int64_t sbj,
     int64_t sbg, int tiles_m, int tiles_n) {
-    // 2-deep ring: while group g is multiplied, group g+1 is in flight.
+    // 2-deep ring: while group g is multiplied, the next group is in flight.
     __shared__ LargeStage stage0, stage1;
 
     const int t = threadIdx.x, lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);     // wave-uniform, kept in scalar registers
     const int wm = wave >> 2, wn = wave & 3;                      // wave tile: rows wm*128.., cols wn*64..
-    int tmi, tni;
-    tile_of_block(blockIdx.x, tiles_m, tiles_n, tmi, tni);
-    // the tile index is block-uniform; the integer divisions above run on the vector unit, so say so
-    tmi = __builtin_amdgcn_readfirstlane(tmi);
-    tni = __builtin_amdgcn_readfirstlane(tni);
-    const int64_t i0 = (int64_t)tmi * L_BM, j0 = (int64_t)tni * L_BN;
     const int G = (int)(Kc / BK);
-    // 32-bit scalar arithmetic: all dims are < 2^31 and operand bands < 2^31 bytes
-    const int rows_a = min((int)I - tmi * L_BM, L_BM), rows_b = min((int)J - tni * L_BN, L_BN);
+    const int T = tiles_m * tiles_n;
+    // Persistent blocks: block b computes tiles b, b + gridDim.x, ... one after the other; the ring and its
+    // prefetch run on across tile boundaries, and a tile's output is stored while the next tile's first
+    // group is multiplied (row of tiles tm just before that row's first promotion).  Every block has at least one tile (grid <= number of tiles).
+    const int nsteps = ((T - 1 - (int)blockIdx.x) / (int)gridDim.x + 1) * G;
 
-    // ---- global -> LDS staging with buffer loads.  Each operand has a scalar descriptor over the block's
-    //      row band, so rows past I (or J) read as zero and are never stored.  Instruction c of wave w fills
-    //      the 1 KB LDS region (c * 8 + w): rows 64 c + 8 w .. +7; lane l lands at row +l/8, physical chunk
-    //      l%8.  The row's swizzle depends on r & 15 only, so one lane offset serves all c, and the c and
-    //      group terms go into the scalar offset.
-    const rsrc_t ra = make_rsrc(A + i0 * Kc, rows_a * (int)Kc);
-    const rsrc_t rb = make_rsrc(B + j0 * Kc, rows_b * (int)Kc);
-    const uint32_t r0 = wave * 8 + (lane >> 3);
+    auto tile_ctx = [&](int pid) __attribute__((always_inline)) -> TileCtx {
+        TileCtx c;
+        int tm_, tn_;
+        tile_of_block(pid, tiles_m, tiles_n, tm_, tn_);
+        // the tile index is block-uniform; the integer divisions above run on the vector unit, so say so
+        c.tmi = __builtin_amdgcn_readfirstlane(tm_);
+        c.tni = __builtin_amdgcn_readfirstlane(tn_);
+        c.i0 = c.tmi * L_BM;
+        c.j0 = c.tni * L_BN;
+        // 32-bit scalar arithmetic: all dims are < 2^31 and operand bands < 2^31 bytes
+        const int rows_a = min((int)I - c.i0, L_BM), rows_b = min((int)J - c.j0, L_BN);
+        c.ra = make_rsrc(A + (int64_t)c.i0 * Kc, rows_a * (int)Kc);
+        c.rb = make_rsrc(B + (int64_t)c.j0 * Kc, rows_b * (int)Kc);
+        c.rsa = make_rsrc(As + c.i0, (G * (int)I - c.i0) * 4);
+        c.rsb = make_rsrc(Bs + (ROW_SCALED_B ? c.j0 : 0), ROW_SCALED_B ? (G * (int)J - c.j0) * 4 : 0);
+        return c;
+    };
+
+    // ---- global -> LDS staging with buffer loads, issued by waves 0..3 (on each SIMD the older wave,
+    //      which the issue arbitration favours, so it reaches the group barrier first and has the time).
+    //      Each operand has a scalar descriptor over the tile's row band, so rows past I (or J) read as
+    //      zero and are never stored.  Instruction c of wave w (w < 4) fills the 1 KB LDS region
+    //      (4 c + w): rows 32 c + 8 w .. +7; lane l lands at row +l/8, physical chunk l%8.  The row's
+    //      swizzle depends on r & 15 only, so one lane offset serves all c, and the c and group terms go
+    //      into the scalar offset.  Scales: one dword per lane, 64 A-row scales per wave (and 64 B-row
+    //      scales for row-scaled B); out-of-range rows read as zero.
+    const bool issues = wave < 4;
+    const uint32_t r0 = (wave & 3) * 8 + (lane >> 3);
     const int ooff = (int)(r0 * (uint32_t)Kc + (((lane & 7) ^ swz(r0)) << 4));
-    const int cstep = 64 * (int)Kc;
-    // scale rows: waves 0..3 bring 64 A-row scales each, waves 4..7 (row-scaled B) 64 B-row scales each,
-    // one dword per lane, straight into LDS; out-of-range rows read as zero.
-    const bool has_scale_load = wave < 4 || ROW_SCALED_B;
-    const rsrc_t rs = (wave < 4) ? make_rsrc(As + i0, (G * (int)I - (int)i0) * 4)
-                                 : make_rsrc(Bs + j0, (G * (int)J - (int)j0) * 4);
-    const int sstep = ((wave < 4) ? (int)I : (int)J) * 4;
+    const int cstep = 32 * (int)Kc;
     const int os = ((wave & 3) * 64 + lane) * 4;
-    auto issue = [&](int g, LargeStage& S) {
-        if (has_scale_load) {
-            float* dst = (wave < 4) ? &S.sa[wave * 64] : &S.sb[(wave - 4) * 64];
-            JETFP8_BUFFER_LOAD_LDS(rs, (lds_void*)dst, 4, os, g * sstep);
-        }
+    auto issue = [&](const TileCtx& c, int g, LargeStage& S) __attribute__((always_inline)) {
+        if (!issues) return;
+        JETFP8_BUFFER_LOAD_LDS(c.rsa, (lds_void*)&S.sa[wave * 64], 4, os, g * (int)I * 4);
+        if (ROW_SCALED_B) JETFP8_BUFFER_LOAD_LDS(c.rsb, (lds_void*)&S.sb[wave * 64], 4, os, g * (int)J * 4);
         const int go = g * BK;
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
-            JETFP8_BUFFER_LOAD_LDS(ra, (lds_void*)(&S.a[(c * 8 + wave) * 1024]), 16, ooff, go + c * cstep);
+        for (int k = 0; k < 8; ++k)
+            JETFP8_BUFFER_LOAD_LDS(c.ra, (lds_void*)(&S.a[(k * 4 + wave) * 1024]), 16, ooff, go + k * cstep);
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
-            JETFP8_BUFFER_LOAD_LDS(rb, (lds_void*)(&S.b[(c * 8 + wave) * 1024]), 16, ooff, go + c * cstep);
+        for (int k = 0; k < 8; ++k)
+            JETFP8_BUFFER_LOAD_LDS(c.rb, (lds_void*)(&S.b[(k * 4 + wave) * 1024]), 16, ooff, go + k * cstep);
     };
-    // block-scaled B: one scale per (128-block of B rows, group); a wave's 64 columns lie in one block.
-    // Columns past J (last tile when J is an odd multiple of 128) use the last block: never stored.
-    const int64_t bblk = min<int64_t>((j0 + wn * 64) / 128, J / 128 - 1);
-    auto block_scale = [&](int g) -> float { return Bs[bblk * sbj + (int64_t)g * sbg]; };
 
     v4f acc[8][4];
 #pragma unroll
@@ -151,27 +167,85 @@ __global__ __launch_bounds__(L_THREADS, 1) void gemm_large_kernel(
     const uint32_t fa0 = (wm * 128 + rl) * BK + ((cp ^ sw) << 4), fa1 = (wm * 128 + rl) * BK + (((cp + 1) ^ sw) << 4);
     const uint32_t fb0 = (wn * 64 + rl) * BK + ((cp ^ sw) << 4), fb1 = (wn * 64 + rl) * BK + (((cp + 1) ^ sw) << 4);
 
-    // One group: wait for its stage, refill the other stage (read one group ago), multiply.
-    auto step = [&](int g, LargeStage& S, LargeStage& refill, float sbv) {
+    // Output of one row of 16x16 tiles: bf16, round to nearest even; each lane writes 4 consecutive columns
+    // (8 bytes) per tile.  J is a multiple of 128, so a lane's 4 columns are either all inside J or all
+    // outside.  The accumulators of the row are cleared for the next tile.
+    auto store_row = [&](int tm, int i0, int j0) __attribute__((always_inline)) {
+        const int64_t r = i0 + wm * 128 + tm * 16 + rl;
+        if (r < I) {
+#pragma unroll
+            for (int tn = 0; tn < 4; ++tn) {
+                const int64_t c = j0 + wn * 64 + tn * 16 + qc4;
+                if (c < J) {
+                    uint2 w;
+                    w.x = f32_to_bf16_rne(acc[tm][tn][0]) | (f32_to_bf16_rne(acc[tm][tn][1]) << 16);
+                    w.y = f32_to_bf16_rne(acc[tm][tn][2]) | (f32_to_bf16_rne(acc[tm][tn][3]) << 16);
+                    *reinterpret_cast<uint2*>(&Cout[r * J + c]) = w;
+                }
+            }
+        }
+#pragma unroll
+        for (int tn = 0; tn < 4; ++tn) acc[tm][tn] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
+    };
+
+    // compute cursor (tile, group) and issue cursor (one step ahead)
+    int cpid = blockIdx.x, cg = 0;
+    TileCtx cur = tile_ctx(cpid);
+    int ipid = cpid, ig = 0;
+    TileCtx iss = cur;
+    int prev_i0 = 0, prev_j0 = 0;
+    auto advance_issue = [&]() __attribute__((always_inline)) {
+        if (++ig == G) {
+            ig = 0;
+            ipid += gridDim.x;
+            if (ipid < T) iss = tile_ctx(ipid);
+        }
+    };
+
+    // One step: wait for the current group's stage, refill the other stage (read one step ago) with the
+    // next group (of this tile or of the block's next tile), store the previous tile at a tile's first
+    // group, multiply.
+    auto step = [&](int s, LargeStage& S, LargeStage& refill) __attribute__((always_inline)) {
         __builtin_amdgcn_sched_barrier(0);   // keep each group's code in place (bounded register pressure)
-        // this wave's loads of group g landed and its LDS reads of group g-1 returned; then every wave of
-        // the block is past that point
+        // this wave's loads of this group landed, its LDS reads of the previous one returned and its
+        // stores of the previous tile completed; then every wave of the block is past that point
         __builtin_amdgcn_s_waitcnt(0);
         __builtin_amdgcn_s_barrier();
-        if (g + 1 < G) issue(g + 1, refill);
+        if (s + 1 < nsteps) {
+            issue(iss, ig, refill);
+            advance_issue();
+        }
+        // first group of a tile after the first: the previous tile's rows are stored one row of tiles at a
+        // time, each just before its first promotion, so the stores spread over the group.  Row-scaled B
+        // (long contraction, few tiles per block, no register room in the hot loop) stores the whole tile
+        // here instead.
+        const bool first_of_tile = cg == 0 && s > 0;
+        const bool flush = !ROW_SCALED_B && first_of_tile;
+        if (ROW_SCALED_B && first_of_tile) {
+#pragma unroll
+            for (int tm = 0; tm < 8; ++tm) store_row(tm, prev_i0, prev_j0);
+        }
+        // block-scaled B: one scale per (128-block of B rows, group); a wave's 64 columns lie in one block.
+        // Columns past J (last tile when J is an odd multiple of 128) use the last block: never stored.
+        float sbv = 0.0f;
+        if (!ROW_SCALED_B) {
+            const int bblk = min((cur.j0 + wn * 64) / 128, (int)(J / 128) - 1);
+            sbv = Bs[(int64_t)bblk * sbj + (int64_t)cg * sbg];
+        }
 
         // The matrix op takes the B fragment as its first operand, so lane l holds output row (l & 15) of
         // each 16-row tile and the 4 consecutive columns 4 * (l >> 4) .. +3: one A-row scale per tile.
         float s1[8];
+        const float* sar = S.sa + (wm * 128 + (int)rl);     // tiles by immediate offsets
 #pragma unroll
         for (int tm = 0; tm < 8; ++tm) {
-            s1[tm] = S.sa[wm * 128 + tm * 16 + rl];
+            s1[tm] = sar[tm * 16];
             if (!ROW_SCALED_B) s1[tm] = s1[tm] * sbv;            // s = fl32(sa * sb)
         }
         v4f sb4[4];
         if (ROW_SCALED_B) {
 #pragma unroll
-            for (int tn = 0; tn < 4; ++tn) sb4[tn] = *reinterpret_cast<const v4f*>(&S.sb[wn * 64 + tn * 16 + qc4]);
+            for (int tn = 0; tn < 4; ++tn) sb4[tn] = *reinterpret_cast<const v4f*>(S.sb + (wn * 64 + qc4) + tn * 16);
         }
         v8i bfr[4];
 #pragma unroll
@@ -180,17 +254,22 @@ __global__ __launch_bounds__(L_THREADS, 1) void gemm_large_kernel(
             const uint4 hi = *reinterpret_cast<const uint4*>(&S.b[fb1 + tn * 2048]);
             bfr[tn] = (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
         }
-        auto a_frag = [&](int tm) -> v8i {
+        auto a_frag = [&](int tm) __attribute__((always_inline)) -> v8i {
             const uint4 lo = *reinterpret_cast<const uint4*>(&S.a[fa0 + tm * 2048]);
             const uint4 hi = *reinterpret_cast<const uint4*>(&S.a[fa1 + tm * 2048]);
             return (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
         };
-        auto promote = [&](int tm, const v4f* p) {
+        auto promote = [&](int tm, const v4f* p) __attribute__((always_inline)) {
+            if (flush) store_row(tm, prev_i0, prev_j0);
+            // row-scaled B: the tile's 16 scale products are formed here; the pinned copy of the row scale
+            // keeps the compiler from forming all 128 of a group at once
+            float srow = s1[tm];
+            if (ROW_SCALED_B) asm volatile("" : "+v"(srow));
 #pragma unroll
             for (int tn = 0; tn < 4; ++tn)
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
-                    const float sc = ROW_SCALED_B ? s1[tm] * sb4[tn][v] : s1[tm];
+                    const float sc = ROW_SCALED_B ? srow * sb4[tn][v] : srow;
                     acc[tm][tn][v] = fmaf(p[tn][v], sc, acc[tm][tn][v]);
                 }
             // pin the promotion here: without this the compiler sinks it below later matrix ops and keeps
@@ -220,42 +299,50 @@ __global__ __launch_bounds__(L_THREADS, 1) void gemm_large_kernel(
         __builtin_amdgcn_sched_barrier(0);
         promote(7, pb);
         __builtin_amdgcn_sched_barrier(0);
+        // advance the compute cursor
+        if (++cg == G) {
+            cg = 0;
+            prev_i0 = cur.i0;
+            prev_j0 = cur.j0;
+            cpid += gridDim.x;
+            if (cpid < T) cur = tile_ctx(cpid);
+        }
     };
 
-    issue(0, stage0);
-    int g = 0;
-    for (; g + 2 <= G; g += 2) {
-        step(g, stage0, stage1, ROW_SCALED_B ? 0.0f : block_scale(g));
-        step(g + 1, stage1, stage0, ROW_SCALED_B ? 0.0f : block_scale(g + 1));
+    issue(iss, ig, stage0);
+    advance_issue();
+    int s = 0;
+    for (; s + 2 <= nsteps; s += 2) {
+        step(s, stage0, stage1);
+        step(s + 1, stage1, stage0);
     }
-    if (g < G) step(g, stage0, stage1, ROW_SCALED_B ? 0.0f : block_scale(g));
+    if (s < nsteps) step(s, stage0, stage1);
+#pragma unroll
+    for (int tm = 0; tm < 8; ++tm) store_row(tm, prev_i0, prev_j0);
+}
 
-    // epilogue: bf16, round to nearest even; each lane writes 4 consecutive columns (8 bytes) per tile.
-    // J is a multiple of 128, so a lane's 4 columns are either all inside J or all outside.
-#pragma unroll
-    for (int tm = 0; tm < 8; ++tm) {
-        const int64_t r = i0 + wm * 128 + tm * 16 + rl;
-        if (r < I) {
-#pragma unroll
-            for (int tn = 0; tn < 4; ++tn) {
-                const int64_t c = j0 + wn * 64 + tn * 16 + qc4;
-                if (c < J) {
-                    uint2 w;
-                    w.x = f32_to_bf16_rne(acc[tm][tn][0]) | (f32_to_bf16_rne(acc[tm][tn][1]) << 16);
-                    w.y = f32_to_bf16_rne(acc[tm][tn][2]) | (f32_to_bf16_rne(acc[tm][tn][3]) << 16);
-                    *reinterpret_cast<uint2*>(&Cout[r * J + c]) = w;
-                }
-            }
-        }
+// Compute units of the current device (one persistent block per compute unit: a block's LDS ring
+// takes most of a CU's LDS).
+static int device_cu_count() {
+    static int cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cache[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cache[dev] = n;
     }
+    return cache[dev];
 }
 
 template <bool ROW_SCALED_B>
 static hipError_t launch_large(const uint8_t* A, const float* As, const uint8_t* B, const float* Bs, uint16_t* C,
                                int64_t I, int64_t J, int64_t Kc, int64_t sbj, int64_t sbg, hipStream_t st) {
     const int tiles_m = (int)((I + L_BM - 1) / L_BM), tiles_n = (int)((J + L_BN - 1) / L_BN);
-    hipLaunchKernelGGL(gemm_large_kernel<ROW_SCALED_B>, dim3(tiles_m * tiles_n), dim3(L_THREADS), 0, st, A, As, B,
-                       Bs, C, I, J, Kc, sbj, sbg, tiles_m, tiles_n);
+    const int tiles = tiles_m * tiles_n;
+    const int grid = min(tiles, device_cu_count());
+    hipLaunchKernelGGL(gemm_large_kernel<ROW_SCALED_B>, dim3(grid), dim3(L_THREADS), 0, st, A, As, B, Bs, C, I,
+                       J, Kc, sbj, sbg, tiles_m, tiles_n);
     return hipGetLastError();
 }
 
