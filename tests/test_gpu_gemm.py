@@ -2,8 +2,11 @@
 kernel-level unified-flow property: an output row's bits do not depend on how many rows are computed.
 
 Tolerance (stated with the path): relative Frobenius error <= 1e-3 and max |error| <= 1e-2 * rms(out),
-comparing bf16 outputs with the oracle's bf16 outputs.  The oracle's per-group dot product is taken in
-both of its readings: the matrix-instruction model (MFMA) and the exact sum (EXACT).
+comparing bf16 outputs with the oracle's bf16 outputs, where the oracle's per-group dot product follows the
+matrix instruction (MFMA mode).  Against the oracle's exact group sums (EXACT mode) the relative Frobenius
+error must stay within 1e-3, or within 1.25x the distance between the oracle's two modes on the same inputs:
+on heavy-tailed groups the instruction's own alignment (which the MFMA mode reproduces) alone can move the
+bf16 outputs by slightly more than 1e-3 from the exact sums.
 """
 import numpy as np
 import pytest
@@ -45,13 +48,16 @@ def _dy(M, N, seed):
 def _report(name, got, orc_ref_mfma, orc_ref_exact):
     m = compare_bf16(got, orc_ref_mfma)
     e = compare_bf16(got, orc_ref_exact)
+    e["model_vs_exact"] = compare_bf16(orc_ref_mfma, orc_ref_exact)["rel_frob"]
     print(f"{name}: vs matrix-core model {m}; vs exact group sums {e}", flush=True)
     return m, e
 
 
 def _assert_tol(name, m, e):
     assert m["rel_frob"] <= REL_FROB and m["max_abs_over_rms"] <= MAX_ABS, (name, m)
-    assert e["rel_frob"] <= REL_FROB, (name, e)
+    # against the exact group sums: the bound, or no further than the matrix instruction's own rounding
+    # (as the model reproduces it) puts the oracle's two readings apart
+    assert e["rel_frob"] <= max(REL_FROB, 1.25 * e["model_vs_exact"]), (name, e)
 
 
 @pytest.mark.parametrize("M,N,K", [(64, 256, 512), (300, 384, 640), (1, 128, 128), (129, 256, 1024)])

@@ -11,7 +11,8 @@ Recipe (host path, numpy PCG64):
   * X  ~ N(0, 1); a fraction of the K columns (round(frac*K), at least 1, chosen without replacement,
         the same columns for every row) is multiplied by 50 before bf16 rounding;
   * W  ~ N(0, 0.02^2)            (0.02 is the standard deviation);
-  * dY ~ 1e-3 * Student-t(nu=3);
+  * dY ~ 1e-3 * Student-t(nu=3) (host: numpy's standard_t; device: Z / sqrt(chi^2_3 / 3) from four
+        standard normals);
   * values are drawn in fp32 and rounded to bf16 by torch (round to nearest even).
 Large workloads use the device path: the same distributions drawn with a seeded torch generator on the
 GPU (fp32 draw, bf16 rounding), because host generation of multi-GB tensors would dominate the run.
@@ -133,11 +134,18 @@ def device_linear(workload: Workload, index: int, device="cuda", M: Optional[int
            "outlier_cols": cols.numpy()}
     del x, w
     if workload.backward:
-        # Student-t(3) = Z / sqrt(V/3), V ~ chi^2(3) = Gamma(1.5, scale 2)
-        z = torch.randn((M, N), generator=g, device=device, dtype=torch.float32)
-        v = torch._standard_gamma(torch.full((M, N), 1.5, device=device), generator=g) * 2.0
-        out["dy"] = (z / torch.sqrt(v / 3.0) * 1e-3).to(torch.bfloat16)
-        del z, v
+        # Student-t(3) = Z / sqrt(V / 3) with V ~ chi^2(3), the sum of three squared standard normals.  Drawn
+        # in row chunks of at most 2^26 elements (bounded temporaries, no tensor beyond 2^31 elements in any
+        # generator kernel).
+        dy = torch.empty((M, N), dtype=torch.bfloat16, device=device)
+        rows = max(1, (1 << 26) // N)
+        for r0 in range(0, M, rows):
+            r1 = min(M, r0 + rows)
+            z = torch.randn((4, r1 - r0, N), generator=g, device=device, dtype=torch.float32)
+            v = z[1] * z[1] + z[2] * z[2] + z[3] * z[3]
+            dy[r0:r1] = (z[0] / torch.sqrt(v / 3.0) * 1e-3).to(torch.bfloat16)
+            del z, v
+        out["dy"] = dy
     return out
 
 
