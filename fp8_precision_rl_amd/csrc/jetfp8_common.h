@@ -14,21 +14,41 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
     return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-// Per-group quantization constants.  s = fl32(amax / 448); the element quotient x / s is formed as
-// (x * p2) * fl32(1 / (s * p2)) with p2 a power of two that keeps the reciprocal finite for tiny s
-// (both products by p2 are exact).
+// Per-group quantization constants.
+//
+// s = fl32(amax / 448), computed as the fp32 rounding of the fp64 product amax * fl64(1/448).  That is the
+// correctly rounded quotient: amax is a bf16 value A * 2^e (A < 2^8), so amax / 448 = (A / 7) * 2^(e-6) is
+// either exact in fp32 (7 divides A) or a non-dyadic number at relative distance >= 2^-28 from every fp32
+// rounding boundary, far more than the fp64 product's error (< 2^-52).
+// rcp approximates 1 / s within 1 ulp (hardware reciprocal); the exact path forms its quotient as
+// (x * p2) * r with p2 a power of two that keeps the reciprocal finite for tiny s (both products by p2
+// are exact).
 struct GroupScale {
-    float s;   // stored scale
-    float r;   // fl32(1 / (s * p2)), +inf when s == 0
-    float p2;  // 2^64 when s < 2^-64, else 1
+    float s;     // stored scale
+    float r;     // ~1 / (s * p2) (1 ulp), +inf when s == 0
+    float p2;    // 2^64 when s < 2^-64, else 1
+    float rcp;   // ~1 / s (1 ulp), used by the fast path
+    bool tiny;   // s < 2^-64 (including the all-zero group): every element takes the exact path
 };
 
 __device__ __forceinline__ GroupScale make_group_scale(float amax) {
     GroupScale g;
-    g.s = __fdiv_rn(amax, 448.0f);
-    g.p2 = (g.s < 0x1p-64f) ? 0x1p64f : 1.0f;
-    g.r = __frcp_rn(g.s * g.p2);
+    g.s = (float)((double)amax * (1.0 / 448.0));
+    g.tiny = !(g.s >= 0x1p-64f);
+    g.p2 = g.tiny ? 0x1p64f : 1.0f;
+    g.r = __builtin_amdgcn_rcpf(g.s * g.p2);
+    g.rcp = __builtin_amdgcn_rcpf(g.s);
     return g;
+}
+
+// Maximum over the 16 lanes of a DPP row (lanes 16k .. 16k+15), without LDS traffic: swap within pairs,
+// within quads, mirror within each half row, mirror the row.
+__device__ __forceinline__ float row16_max(float a) {
+    a = fmaxf(a, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(a), 0xB1, 0xF, 0xF, false)));
+    a = fmaxf(a, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(a), 0x4E, 0xF, 0xF, false)));
+    a = fmaxf(a, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(a), 0x141, 0xF, 0xF, false)));
+    a = fmaxf(a, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(a), 0x140, 0xF, 0xF, false)));
+    return a;
 }
 
 // Approximate quotient x / s (relative error <= 2^-23 + 2^-48): exact +-0 for an all-zero group.
@@ -70,10 +90,47 @@ __device__ __forceinline__ float quantize_value(float x, const GroupScale& g) {
     return resolve_midpoint(x, q, g.s);
 }
 
-// Four codes of one group packed little-endian into a uint32.
-__device__ __forceinline__ uint32_t encode4(float x0, float x1, float x2, float x3, const GroupScale& g) {
-    uint32_t w = cvt2_e4m3<false>(quantize_value(x0, g), quantize_value(x1, g), 0u);
-    return cvt2_e4m3<true>(quantize_value(x2, g), quantize_value(x3, g), w);
+// Eight codes of one group, packed little-endian into two uint32.
+//
+// Fast path: q = fl32(x * rcp) is within 3 ulps of x / s (rcp within 1 ulp of 1 / s, one more rounding),
+// and the hardware conversion rounds q to nearest even.  That equals the rounding of the exact quotient
+// unless an E4M3 rounding midpoint lies between q and x / s, or q is itself a midpoint.  Every midpoint
+// (and zero) has the low 15 bits of its fp32 pattern clear -- the normal-range midpoints have 19, the
+// subnormal-range ones at least 20 -- and a midpoint within 3 ulps of q is in q's binade, so it is within 3
+// of q's bit pattern.  Whenever some q of the eight has its pattern within 4 of a multiple of 2^15 (or the
+// group's scale is tiny), all eight take the exact path above.  That happens for about 2^-11.8 of the
+// elements of ordinary data; exact zeros always take it.
+__device__ __forceinline__ uint2 pack8(const float q[8]) {
+    uint2 out;
+    out.x = cvt2_e4m3<true>(q[2], q[3], cvt2_e4m3<false>(q[0], q[1], 0u));
+    out.y = cvt2_e4m3<true>(q[6], q[7], cvt2_e4m3<false>(q[4], q[5], 0u));
+    return out;
+}
+
+// Fast path only: the eight codes, and whether they must be redone by encode8_exact.
+__device__ __forceinline__ uint2 encode8_fast(const float x[8], const GroupScale& g, bool& redo) {
+    float q[8];
+    uint32_t near = 0xFFFFFFFFu;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        q[i] = x[i] * g.rcp;
+        near = min(near, (__float_as_uint(q[i]) + 4u) & 0x7FFFu);
+    }
+    redo = g.tiny || near <= 8u;
+    return pack8(q);
+}
+
+__device__ __forceinline__ uint2 encode8_exact(const float x[8], const GroupScale& g) {
+    float q[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) q[i] = quantize_value(x[i], g);
+    return pack8(q);
+}
+
+__device__ __forceinline__ uint2 encode8(const float x[8], const GroupScale& g) {
+    bool redo;
+    const uint2 c = encode8_fast(x, g, redo);
+    return redo ? encode8_exact(x, g) : c;
 }
 
 }  // namespace jetfp8

@@ -11,74 +11,110 @@
 
 namespace jetfp8 {
 
-// 16 lanes own one 1x128 group (8 bf16 per lane, one 16-byte load); a 256-thread block owns the same
-// group column of 16 consecutive rows, so the 16 scales it writes are contiguous.
-__global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restrict__ x, int64_t R, int64_t C,
-                                                         uint8_t* __restrict__ q, float* __restrict__ s) {
-    const int lane16 = threadIdx.x & 15;
-    const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
-    const int64_t g = blockIdx.y;
-    const bool live = row < R;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    const int64_t off = row * C + g * 128 + lane16 * 8;
-    if (live) v = *reinterpret_cast<const uint4*>(x + off);
-    float f[8];
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+// 16-byte streaming load (read once: non-temporal).
+__device__ __forceinline__ uint4 load16_nt(const uint16_t* p) {
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+__device__ __forceinline__ void unpack8(const uint4& v, float f[8]) {
     f[0] = bf16_to_f32(v.x & 0xFFFFu); f[1] = bf16_to_f32(v.x >> 16);
     f[2] = bf16_to_f32(v.y & 0xFFFFu); f[3] = bf16_to_f32(v.y >> 16);
     f[4] = bf16_to_f32(v.z & 0xFFFFu); f[5] = bf16_to_f32(v.z >> 16);
     f[6] = bf16_to_f32(v.w & 0xFFFFu); f[7] = bf16_to_f32(v.w >> 16);
-    float a = 0.0f;
+}
+
+// 1x128 groups.  A block of QR_WAVES waves owns a tile of 32 rows x 512 columns (4 groups per row): each
+// wave reads 1 KB runs of one row (16 lanes per group, 8 bf16 per lane) and writes 512-byte runs of codes;
+// the tile's 4 x 32 scales are written as four whole 128-byte lines.  All loads of a thread are issued
+// before the first is used.  Blocks are numbered along the columns first.
+constexpr int QR_ROWS = 32, QR_COLS = 512, QR_WAVES = 8, QR_PASSES = QR_ROWS / QR_WAVES;
+
+__global__ __launch_bounds__(QR_WAVES * 64) void quant_rows_kernel(const uint16_t* __restrict__ x, int64_t R,
+                                                                   int64_t C, uint8_t* __restrict__ q,
+                                                                   float* __restrict__ s, uint32_t col_blocks) {
+    __shared__ float sc[4][QR_ROWS];
+    const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
+    const int gl = lane >> 4, lane16 = lane & 15;
+    const uint32_t cb = blockIdx.x % col_blocks, rb = blockIdx.x / col_blocks;
+    const int64_t c0 = (int64_t)cb * QR_COLS, r0 = (int64_t)rb * QR_ROWS;
+    const int64_t col = c0 + gl * 128 + lane16 * 8;
+    const bool col_ok = col < C;       // C is a multiple of 128: a group is wholly inside or outside
+    uint4 v[QR_PASSES];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(f[i]));
+    for (int p = 0; p < QR_PASSES; ++p) {
+        const int64_t row = r0 + p * QR_WAVES + wave;
+        v[p] = make_uint4(0, 0, 0, 0);
+        if (col_ok && row < R) v[p] = load16_nt(x + row * C + col);
+    }
 #pragma unroll
-    for (int m = 8; m >= 1; m >>= 1) a = fmaxf(a, __shfl_xor(a, m, 16));
-    const GroupScale gs = make_group_scale(a);
-    uint2 out;
-    out.x = encode4(f[0], f[1], f[2], f[3], gs);
-    out.y = encode4(f[4], f[5], f[6], f[7], gs);
-    if (live) {
-        *reinterpret_cast<uint2*>(q + off) = out;
-        if (lane16 == 0) s[g * R + row] = gs.s;
+    for (int p = 0; p < QR_PASSES; ++p) {
+        const int64_t row = r0 + p * QR_WAVES + wave;
+        float f[8];
+        unpack8(v[p], f);
+        float a = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(f[i]));
+        a = row16_max(a);
+        const GroupScale gs = make_group_scale(a);
+        const uint2 out = encode8(f, gs);
+        if (col_ok && row < R) *reinterpret_cast<uint2*>(q + row * C + col) = out;
+        if (lane16 == 0) sc[gl][p * QR_WAVES + wave] = gs.s;
+    }
+    __syncthreads();
+    if (t < 4 * QR_ROWS) {
+        const int g = t / QR_ROWS, r = t % QR_ROWS;
+        const int64_t gg = c0 / 128 + g;
+        if (gg * 128 < C && r0 + r < R) s[gg * R + r0 + r] = sc[g][r];
     }
 }
 
-// One block owns a 128-row x 64-column tile: it stages the tile in LDS, reduces each column's 128
-// values, and writes the codes transposed (each column becomes 128 contiguous bytes of the output).
+// 128x1 groups, codes transposed, without LDS.  A 256-thread block owns a 128-row x 128-column tile.
+// Lane l of DPP row k (16 lanes) of wave w loads the 8x8 sub-tile of rows 8l .. 8l+7 and columns
+// 32w + 8k .. +7 (eight 16-byte loads, all issued first), so each column's 128-row group is spread over
+// the 16 lanes of one DPP row: a column's amax is a 16-lane row reduction, and the lane then holds 8
+// consecutive rows of each of its 8 columns -- 8 bytes of the transposed output each, and the row's 16
+// lanes write 128 contiguous bytes of a transposed row.
 __global__ __launch_bounds__(256) void quant_cols_t_kernel(const uint16_t* __restrict__ x, int64_t R, int64_t C,
-                                                           uint8_t* __restrict__ qT, float* __restrict__ sT) {
-    __shared__ uint16_t tile[128][64 + 2];
-    __shared__ float red[4][64];
-    const int t = threadIdx.x;
-    const int64_t r0 = (int64_t)blockIdx.y * 128;
-    const int64_t c0 = (int64_t)blockIdx.x * 64;
+                                                           uint8_t* __restrict__ qT, float* __restrict__ sT,
+                                                           uint32_t col_blocks) {
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int l = lane & 15, k = lane >> 4;
+    const uint32_t cb = blockIdx.x % col_blocks, rb = blockIdx.x / col_blocks;
+    const int64_t r0 = (int64_t)rb * 128;
+    const int64_t c = (int64_t)cb * 128 + wave * 32 + k * 8;     // first of this lane's 8 columns
+    const bool ok = c < C;                                         // C is a multiple of 64, so of 8
+    uint4 v[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int id = t + 256 * i;           // 1024 chunks of 8 bf16: 128 rows x 8 chunks
-        const int row = id >> 3, ch = id & 7;
-        const uint4 v = *reinterpret_cast<const uint4*>(x + (r0 + row) * C + c0 + ch * 8);
-        uint32_t* dst = reinterpret_cast<uint32_t*>(&tile[row][ch * 8]);
-        dst[0] = v.x; dst[1] = v.y; dst[2] = v.z; dst[3] = v.w;
+    for (int i = 0; i < 8; ++i) {
+        v[i] = make_uint4(0, 0, 0, 0);
+        if (ok) v[i] = load16_nt(x + (r0 + 8 * l + i) * C + c);
     }
-    __syncthreads();
-    const int col = t & 63, part = t >> 6;    // 4 parts of 32 rows each
-    float f[32];
-    float a = 0.0f;
+    // column j of the sub-tile: element i is the 16-bit half (j & 1) of word (j >> 1) of v[i]
+    auto elem = [&](int i, int j) -> float {
+        const uint32_t w = (j >> 1) == 0 ? v[i].x : (j >> 1) == 1 ? v[i].y : (j >> 1) == 2 ? v[i].z : v[i].w;
+        return bf16_to_f32((j & 1) ? (w >> 16) : (w & 0xFFFFu));
+    };
+    float my_scale = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-        f[i] = bf16_to_f32(tile[part * 32 + i][col]);
-        a = fmaxf(a, fabsf(f[i]));
+    for (int j = 0; j < 8; ++j) {
+        float f[8];
+        float a = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            f[i] = elem(i, j);
+            a = fmaxf(a, fabsf(f[i]));
+        }
+        a = row16_max(a);
+        const GroupScale gs = make_group_scale(a);
+        const uint2 out = encode8(f, gs);
+        if (ok) *reinterpret_cast<uint2*>(qT + (c + j) * R + r0 + 8 * l) = out;
+        if (l == j) my_scale = gs.s;
     }
-    red[part][col] = a;
-    __syncthreads();
-    a = fmaxf(fmaxf(red[0][col], red[1][col]), fmaxf(red[2][col], red[3][col]));
-    const GroupScale gs = make_group_scale(a);
-    uint32_t w[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) w[i] = encode4(f[4 * i], f[4 * i + 1], f[4 * i + 2], f[4 * i + 3], gs);
-    uint8_t* dst = qT + (c0 + col) * R + r0 + part * 32;
-    reinterpret_cast<uint4*>(dst)[0] = make_uint4(w[0], w[1], w[2], w[3]);
-    reinterpret_cast<uint4*>(dst)[1] = make_uint4(w[4], w[5], w[6], w[7]);
-    if (part == 0) sT[(int64_t)blockIdx.y * C + c0 + col] = gs.s;
+    // lanes 0..7 of each DPP row hold the scales of its 8 columns: 32 contiguous bytes per row
+    if (ok && l < 8) sT[(int64_t)rb * C + c + l] = my_scale;
 }
 
 // One block owns one 128x128 block: 8 rows x 8 columns per thread, a block-wide amax, codes written in
@@ -113,9 +149,7 @@ __global__ __launch_bounds__(256) void quant_blocks_kernel(const uint16_t* __res
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int row = (t >> 4) + 16 * i;
-        uint2 out;
-        out.x = encode4(f[i][0], f[i][1], f[i][2], f[i][3], gs);
-        out.y = encode4(f[i][4], f[i][5], f[i][6], f[i][7], gs);
+        const uint2 out = encode8(f[i], gs);
         *reinterpret_cast<uint2*>(q + (r0 + row) * C + c0 + ch * 8) = out;
         if (qT) {
             uint32_t* crow = reinterpret_cast<uint32_t*>(&codes[row][ch * 8]);
@@ -141,15 +175,19 @@ __global__ __launch_bounds__(256) void quant_blocks_kernel(const uint16_t* __res
 }
 
 hipError_t launch_quant_rows(const uint16_t* x, int64_t R, int64_t C, uint8_t* q, float* s, hipStream_t st) {
-    dim3 grid((unsigned)((R + 15) / 16), (unsigned)(C / 128));
-    hipLaunchKernelGGL(quant_rows_kernel, grid, dim3(256), 0, st, x, R, C, q, s);
+    const int64_t col_blocks = (C + QR_COLS - 1) / QR_COLS, row_blocks = (R + QR_ROWS - 1) / QR_ROWS;
+    if (col_blocks * row_blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(quant_rows_kernel, dim3((unsigned)(col_blocks * row_blocks)), dim3(QR_WAVES * 64), 0, st, x, R,
+                       C, q, s, (uint32_t)col_blocks);
     return hipGetLastError();
 }
 
 hipError_t launch_quant_cols_t(const uint16_t* x, int64_t R, int64_t C, uint8_t* qT, float* sT, hipStream_t st) {
-    // C is a multiple of 128, so of 64; R a multiple of 128.
-    dim3 grid((unsigned)(C / 64), (unsigned)(R / 128));
-    hipLaunchKernelGGL(quant_cols_t_kernel, grid, dim3(256), 0, st, x, R, C, qT, sT);
+    // R is a multiple of 128 (whole groups); C a multiple of 64 (a partial last column tile is masked).
+    const int64_t col_blocks = (C + 127) / 128, row_blocks = R / 128;
+    if (col_blocks * row_blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(quant_cols_t_kernel, dim3((unsigned)(col_blocks * row_blocks)), dim3(256), 0, st, x, R, C, qT,
+                       sT, (uint32_t)col_blocks);
     return hipGetLastError();
 }
 
