@@ -39,6 +39,8 @@ __device__ __forceinline__ v4f mfma_group(const v8i& a, const v8i& b) {
 constexpr int BK = 128;            // one quantization group along the contraction axis
 constexpr int L_BM = 256, L_BN = 256, L_THREADS = 512;
 constexpr int L_A_BYTES = L_BM * BK, L_B_BYTES = L_BN * BK;
+// s_waitcnt immediate: lgkmcnt == 0 only (vmcnt and expcnt at their maxima)
+constexpr int kWaitLgkm0 = 0xF | (7 << 4) | (3 << 14);
 
 // LDS row layout: 128-byte rows, the 16-byte chunk c of row r stored at chunk c ^ swz(r).  The XOR
 // pattern was chosen by measurement on gfx950 (fragment reads at ~170 B/clk/CU against ~113 for the
@@ -127,30 +129,28 @@ __global__ __launch_bounds__(L_THREADS, 1) void gemm_large_kernel(
         return c;
     };
 
-    // ---- global -> LDS staging with buffer loads, issued by waves 0..3 (on each SIMD the older wave,
-    //      which the issue arbitration favours, so it reaches the group barrier first and has the time).
-    //      Each operand has a scalar descriptor over the tile's row band, so rows past I (or J) read as
-    //      zero and are never stored.  Instruction c of wave w (w < 4) fills the 1 KB LDS region
-    //      (4 c + w): rows 32 c + 8 w .. +7; lane l lands at row +l/8, physical chunk l%8.  The row's
-    //      swizzle depends on r & 15 only, so one lane offset serves all c, and the c and group terms go
-    //      into the scalar offset.  Scales: one dword per lane, 64 A-row scales per wave (and 64 B-row
-    //      scales for row-scaled B); out-of-range rows read as zero.
-    const bool issues = wave < 4;
-    const uint32_t r0 = (wave & 3) * 8 + (lane >> 3);
+    // ---- global -> LDS staging with buffer loads, spread over the first four row tiles of the previous
+    //      group (one A and one B instruction per wave per tile) so that no wave stalls on a burst of load
+    //      issues and the fragment reads at the start of a group meet no load traffic.  Each operand has a
+    //      scalar descriptor over the tile's row band, so rows past I (or J) read as zero and are never
+    //      stored.  Part c of wave w fills the 1 KB LDS region (8 c + w) of A and of B: rows 64 c + 8 w ..
+    //      +7; lane l lands at row +l/8, physical chunk l%8.  The row's swizzle depends on r & 15 only, so
+    //      one lane offset serves all c, and the c and group terms go into the scalar offset.  Scales (with
+    //      part 0): one dword per lane, waves 0..3 bring 64 A-row scales each, waves 4..7 (row-scaled B)
+    //      64 B-row scales each; out-of-range rows read as zero.
+    const uint32_t r0 = wave * 8 + (lane >> 3);
     const int ooff = (int)(r0 * (uint32_t)Kc + (((lane & 7) ^ swz(r0)) << 4));
-    const int cstep = 32 * (int)Kc;
+    const int cstep = 64 * (int)Kc;
     const int os = ((wave & 3) * 64 + lane) * 4;
-    auto issue = [&](const TileCtx& c, int g, LargeStage& S) __attribute__((always_inline)) {
-        if (!issues) return;
-        JETFP8_BUFFER_LOAD_LDS(c.rsa, (lds_void*)&S.sa[wave * 64], 4, os, g * (int)I * 4);
-        if (ROW_SCALED_B) JETFP8_BUFFER_LOAD_LDS(c.rsb, (lds_void*)&S.sb[wave * 64], 4, os, g * (int)J * 4);
-        const int go = g * BK;
-#pragma unroll
-        for (int k = 0; k < 8; ++k)
-            JETFP8_BUFFER_LOAD_LDS(c.ra, (lds_void*)(&S.a[(k * 4 + wave) * 1024]), 16, ooff, go + k * cstep);
-#pragma unroll
-        for (int k = 0; k < 8; ++k)
-            JETFP8_BUFFER_LOAD_LDS(c.rb, (lds_void*)(&S.b[(k * 4 + wave) * 1024]), 16, ooff, go + k * cstep);
+    auto issue_part = [&](int c, const TileCtx& tc, int g, LargeStage& S) __attribute__((always_inline)) {
+        if (c == 0) {
+            if (wave < 4) JETFP8_BUFFER_LOAD_LDS(tc.rsa, (lds_void*)&S.sa[wave * 64], 4, os, g * (int)I * 4);
+            else if (ROW_SCALED_B)
+                JETFP8_BUFFER_LOAD_LDS(tc.rsb, (lds_void*)&S.sb[(wave - 4) * 64], 4, os, g * (int)J * 4);
+        }
+        const int go = g * BK + c * cstep;
+        JETFP8_BUFFER_LOAD_LDS(tc.ra, (lds_void*)(&S.a[(c * 8 + wave) * 1024]), 16, ooff, go);
+        JETFP8_BUFFER_LOAD_LDS(tc.rb, (lds_void*)(&S.b[(c * 8 + wave) * 1024]), 16, ooff, go);
     };
 
     v4f acc[8][4];
@@ -202,19 +202,16 @@ __global__ __launch_bounds__(L_THREADS, 1) void gemm_large_kernel(
         }
     };
 
-    // One step: wait for the current group's stage, refill the other stage (read one step ago) with the
-    // next group (of this tile or of the block's next tile), store the previous tile at a tile's first
-    // group, multiply.
+    // One step: wait for the current group's stage, store the previous tile at a tile's first group,
+    // multiply, and (during the first row tiles) refill the other stage (read one step ago) with the next
+    // group, of this tile or of the block's next tile.
     auto step = [&](int s, LargeStage& S, LargeStage& refill) __attribute__((always_inline)) {
         __builtin_amdgcn_sched_barrier(0);   // keep each group's code in place (bounded register pressure)
         // this wave's loads of this group landed, its LDS reads of the previous one returned and its
         // stores of the previous tile completed; then every wave of the block is past that point
         __builtin_amdgcn_s_waitcnt(0);
         __builtin_amdgcn_s_barrier();
-        if (s + 1 < nsteps) {
-            issue(iss, ig, refill);
-            advance_issue();
-        }
+        const bool refill_next = s + 1 < nsteps;   // the next step's group goes into the other stage
         // first group of a tile after the first: the previous tile's rows are stored one row of tiles at a
         // time, each just before its first promotion, so the stores spread over the group.  Row-scaled B
         // (long contraction, few tiles per block, no register room in the hot loop) stores the whole tile
@@ -285,6 +282,7 @@ __global__ __launch_bounds__(L_THREADS, 1) void gemm_large_kernel(
 #pragma unroll
         for (int tm = 1; tm < 8; ++tm) {
             af = a_frag(tm);
+            if (tm <= 4 && refill_next) issue_part(tm - 1, iss, ig, refill);
             __builtin_amdgcn_sched_barrier(0);
             if (tm & 1) {
 #pragma unroll
@@ -299,6 +297,7 @@ __global__ __launch_bounds__(L_THREADS, 1) void gemm_large_kernel(
         __builtin_amdgcn_sched_barrier(0);
         promote(7, pb);
         __builtin_amdgcn_sched_barrier(0);
+        if (refill_next) advance_issue();
         // advance the compute cursor
         if (++cg == G) {
             cg = 0;
@@ -309,7 +308,8 @@ __global__ __launch_bounds__(L_THREADS, 1) void gemm_large_kernel(
         }
     };
 
-    issue(iss, ig, stage0);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) issue_part(c, iss, ig, stage0);
     advance_issue();
     int s = 0;
     for (; s + 2 <= nsteps; s += 2) {
@@ -335,6 +335,165 @@ static int device_cu_count() {
     return cache[dev];
 }
 
+// ---- small-M kernel (rollout decode: I <= 16 * RT rows) -----------------------------------------------
+// The large tiles would leave most of the machine idle and stream each weight row through LDS for a handful
+// of output rows, so the decode shape gets its own schedule with the same per-element operation sequence:
+//   - the output is cut into slices of 16 columns (16 rows of B) by all I rows; persistent 512-thread blocks
+//     take slices b, b + gridDim.x, ... and the operand loads run on across slice boundaries, so the weight
+//     stream never drains between slices;
+//   - the groups of the contraction are dealt out in chunks of 8, one group per wave: the wave forms the
+//     group products of its group with one V_MFMA_F32_16X16X128_F8F6F4 per 16-row tile (B fragment first,
+//     C = 0, exactly as the large kernel), and parks them in LDS;
+//   - after a barrier every wave runs the promotion acc = fma(p, fl32(sa * sb), acc) for its share of the
+//     outputs over the chunk's groups in ascending order -- the same chain the large kernel runs, so every
+//     output row is bitwise the same whichever kernel computed it;
+//   - operand fragments go straight from global memory into registers, D_AHEAD chunks ahead (range-checked
+//     buffer loads: rows past I and groups past the contraction read as zero and are never promoted); the
+//     A-row scales of all groups sit in LDS for the block's lifetime.
+constexpr int D_WAVES = 8, D_THREADS = 64 * D_WAVES, D_AHEAD = 3;
+constexpr int D_SA_MAX = 8192;     // A-row scales kept in LDS: (contraction / 128) * rows <= 8192
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+template <int RT>
+__global__ __launch_bounds__(D_THREADS) void gemm_decode_kernel(
+    const uint8_t* __restrict__ A, const float* __restrict__ As, const uint8_t* __restrict__ B,
+    const float* __restrict__ Bs, uint16_t* __restrict__ Cout, int64_t I, int64_t J, int64_t Kc, int64_t sbj,
+    int64_t sbg) {
+    constexpr int PAIRS = RT * 4;                             // (row tile, lane component) pairs of outputs
+    constexpr int EPW = (PAIRS + D_WAVES - 1) / D_WAVES;      // pairs per wave in the promotion chain
+    __shared__ v4f pbuf[2][D_WAVES][RT][64];
+    __shared__ float sa_tab[D_SA_MAX];
+    const int t = threadIdx.x, lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int G = (int)(Kc / BK), nchunks = (G + D_WAVES - 1) / D_WAVES;
+    const int Ii = (int)I;
+    const int slices = (int)(J / 16);
+    // chunk stream of this block: slices blockIdx.x, + gridDim.x, ...; nchunks chunks each
+    const int nstream = ((slices - 1 - (int)blockIdx.x) / (int)gridDim.x + 1) * nchunks;
+    auto slice_col = [&](int sc) -> int { return ((int)blockIdx.x + sc * (int)gridDim.x) * 16; };
+
+    // lane l holds row (l & 15) of a 16-row tile, contraction bytes 32 (l >> 4) .. +31 of the group
+    const rsrc_t ra = make_rsrc(A, Ii * (int)Kc);
+    const int kofs = 32 * (lane >> 4);
+    const int vb = (lane & 15) * (int)Kc + kofs;
+    int va[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) va[rt] = (rt * 16 + (lane & 15)) * (int)Kc + kofs;
+
+    // promotion-chain ownership: pair q = wave + 8 e -> row tile q >> 2, lane component q & 3
+    float acc[EPW];
+#pragma unroll
+    for (int e = 0; e < EPW; ++e) acc[e] = 0.0f;
+
+    u32x4 wf[D_AHEAD][2], af[D_AHEAD][RT][2];
+    // stream position c -> slice c / nchunks (B rows of that slice only: 16 x Kc bytes), group chunk
+    // c % nchunks.  Positions past the block's stream load unconditionally (a conditional load would make
+    // the compiler wait for it where the paths join) through an empty descriptor: they read zeros.
+    auto load_chunk = [&](int c, u32x4 (&w)[2], u32x4 (&a)[RT][2]) __attribute__((always_inline)) {
+        const int sc = __builtin_amdgcn_readfirstlane(c / nchunks), ch = c - sc * nchunks;
+        const bool live = c < nstream;
+        const rsrc_t rb = make_rsrc(live ? B + (int64_t)slice_col(sc) * Kc : B, live ? 16 * (int)Kc : 0);
+        const int so = (ch * D_WAVES + wave) * BK;
+        w[0] = __builtin_amdgcn_raw_buffer_load_b128(rb, vb, so, 0);
+        w[1] = __builtin_amdgcn_raw_buffer_load_b128(rb, vb + 16, so, 0);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            a[rt][0] = __builtin_amdgcn_raw_buffer_load_b128(ra, va[rt], so, 0);
+            a[rt][1] = __builtin_amdgcn_raw_buffer_load_b128(ra, va[rt] + 16, so, 0);
+        }
+    };
+    // block scales of a chunk's 8 groups (the slice's 16 columns lie in one 128-column block)
+    auto load_sb = [&](int c, float (&sb)[D_WAVES]) __attribute__((always_inline)) {
+        const int sc = c / nchunks, ch = c - sc * nchunks;
+        const int64_t sb_base = (int64_t)(slice_col(sc) / 128) * sbj;
+#pragma unroll
+        for (int gi = 0; gi < D_WAVES; ++gi) sb[gi] = Bs[sb_base + (int64_t)min(ch * D_WAVES + gi, G - 1) * sbg];
+    };
+    auto store_slice = [&](int sc) __attribute__((always_inline)) {
+        const int j0 = slice_col(sc);
+        // pair q of lane l is row (q >> 2) * 16 + (l & 15), column j0 + 4 (l >> 4) + (q & 3)
+#pragma unroll
+        for (int e = 0; e < EPW; ++e) {
+            const int q = wave + D_WAVES * e;
+            const int m = (q >> 2) * 16 + (lane & 15);
+            if (q < PAIRS && m < Ii)
+                Cout[(int64_t)m * J + j0 + 4 * (lane >> 4) + (q & 3)] = (uint16_t)f32_to_bf16_rne(acc[e]);
+            acc[e] = 0.0f;
+        }
+    };
+
+    // the A-row scales of every group (the same for all slices) in LDS: sa_tab[g * I + m]; filled before the
+    // first operand loads are issued, so waiting for it does not wait for them
+    for (int i = t; i < G * Ii; i += D_THREADS) sa_tab[i] = As[i];
+#pragma unroll
+    for (int k = 0; k < D_AHEAD; ++k) load_chunk(k, wf[k], af[k]);
+    float sb_cur[D_WAVES];
+    load_sb(0, sb_cur);
+    // LDS writes done, then every wave is here (a plain barrier: the operand loads stay in flight)
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    __builtin_amdgcn_s_barrier();
+
+    auto chunk = [&](int c, u32x4 (&w)[2], u32x4 (&a)[RT][2]) __attribute__((always_inline)) {
+        float sb_nxt[D_WAVES];
+        load_sb(min(c + 1, nstream - 1), sb_nxt);
+        const v8i bfrag = (v8i){(int)w[0][0], (int)w[0][1], (int)w[0][2], (int)w[0][3],
+                                (int)w[1][0], (int)w[1][1], (int)w[1][2], (int)w[1][3]};
+        v4f p[RT];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            const v8i afrag = (v8i){(int)a[rt][0][0], (int)a[rt][0][1], (int)a[rt][0][2], (int)a[rt][0][3],
+                                    (int)a[rt][1][0], (int)a[rt][1][1], (int)a[rt][1][2], (int)a[rt][1][3]};
+            p[rt] = mfma_group(bfrag, afrag);
+        }
+        load_chunk(c + D_AHEAD, w, a);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) pbuf[c & 1][wave][rt][lane] = p[rt];
+        // this wave's products (and its chain reads of two chunks ago) are in LDS, then every wave is here;
+        // a plain barrier, so the operand loads of the next chunks stay in flight
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+        __builtin_amdgcn_s_barrier();
+        const int ch = c % nchunks;
+        // promotion chain over the chunk's groups, ascending
+#pragma unroll
+        for (int gi = 0; gi < D_WAVES; ++gi) {
+            if (ch * D_WAVES + gi < G) {
+#pragma unroll
+                for (int e = 0; e < EPW; ++e) {
+                    const int q = wave + D_WAVES * e;
+                    const int m = (q >> 2) * 16 + (lane & 15);
+                    if (q < PAIRS) {
+                        const float pv = pbuf[c & 1][gi][q >> 2][lane][q & 3];
+                        const float sa = m < Ii ? sa_tab[(ch * D_WAVES + gi) * Ii + m] : 0.0f;
+                        acc[e] = fmaf(pv, sa * sb_cur[gi], acc[e]);          // s = fl32(sa * sb)
+                    }
+                }
+            }
+        }
+        if (ch == nchunks - 1) store_slice(c / nchunks);
+#pragma unroll
+        for (int gi = 0; gi < D_WAVES; ++gi) sb_cur[gi] = sb_nxt[gi];
+    };
+    int c = 0;
+    for (; c + D_AHEAD <= nstream; c += D_AHEAD) {
+#pragma unroll
+        for (int k = 0; k < D_AHEAD; ++k) chunk(c + k, wf[k], af[k]);
+    }
+#pragma unroll
+    for (int k = 0; k < D_AHEAD; ++k)
+        if (c + k < nstream) chunk(c + k, wf[k], af[k]);
+}
+
+template <int RT>
+static hipError_t launch_decode(const uint8_t* A, const float* As, const uint8_t* B, const float* Bs, uint16_t* C,
+                                int64_t I, int64_t J, int64_t Kc, int64_t sbj, int64_t sbg, hipStream_t st) {
+    const int slices = (int)(J / 16);
+    const int grid = min(slices, device_cu_count());   // one block per CU (register budget)
+    hipLaunchKernelGGL(gemm_decode_kernel<RT>, dim3((unsigned)grid), dim3(D_THREADS), 0, st, A, As, B, Bs, C, I, J,
+                       Kc, sbj, sbg);
+    return hipGetLastError();
+}
+
 template <bool ROW_SCALED_B>
 static hipError_t launch_large(const uint8_t* A, const float* As, const uint8_t* B, const float* Bs, uint16_t* C,
                                int64_t I, int64_t J, int64_t Kc, int64_t sbj, int64_t sbg, hipStream_t st) {
@@ -349,6 +508,11 @@ static hipError_t launch_large(const uint8_t* A, const float* As, const uint8_t*
 hipError_t launch_gemm_block_scaled_b(const uint8_t* A, const float* As, const uint8_t* B, const float* Bs,
                                       uint16_t* C, int64_t I, int64_t J, int64_t Kc, int64_t sbj, int64_t sbg,
                                       hipStream_t st) {
+    // decode sizes: the small-M schedule (same per-element sequence, so the same bits)
+    if (I <= 32 && (Kc / BK) * I <= D_SA_MAX) {
+        if (I <= 16) return launch_decode<1>(A, As, B, Bs, C, I, J, Kc, sbj, sbg, st);
+        return launch_decode<2>(A, As, B, Bs, C, I, J, Kc, sbj, sbg, st);
+    }
     return launch_large<false>(A, As, B, Bs, C, I, J, Kc, sbj, sbg, st);
 }
 
