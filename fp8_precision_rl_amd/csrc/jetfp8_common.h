@@ -51,6 +51,31 @@ __device__ __forceinline__ float row16_max(float a) {
     return a;
 }
 
+// Lane-wise magnitude maximum of two pairs of bf16 values (bit patterns packed two to a word).  For finite
+// values the order of the 15 magnitude bits is the order of the magnitudes, so the maximum is taken on
+// 16-bit integers, two per instruction.
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t max_mag2(uint32_t a, uint32_t b) {
+    const u16x2_t m = __builtin_elementwise_max(__builtin_bit_cast(u16x2_t, a & 0x7FFF7FFFu),
+                                                __builtin_bit_cast(u16x2_t, b & 0x7FFF7FFFu));
+    return __builtin_bit_cast(uint32_t, m);
+}
+
+// Largest magnitude among the eight bf16 values of v, as a bf16 bit pattern.
+__device__ __forceinline__ uint32_t amax8_bits(const uint4& v) {
+    const uint32_t m = max_mag2(max_mag2(v.x, v.y), max_mag2(v.z, v.w));
+    return max(m & 0xFFFFu, m >> 16);
+}
+
+// Integer maximum over the 16 lanes of a DPP row (same exchange pattern as row16_max; 0 is the identity).
+__device__ __forceinline__ uint32_t row16_max_u32(uint32_t a) {
+    a = max(a, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a, 0xB1, 0xF, 0xF, false));
+    a = max(a, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a, 0x4E, 0xF, 0xF, false));
+    a = max(a, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a, 0x141, 0xF, 0xF, false));
+    a = max(a, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a, 0x140, 0xF, 0xF, false));
+    return a;
+}
+
 // Approximate quotient x / s (relative error <= 2^-23 + 2^-48): exact +-0 for an all-zero group.
 __device__ __forceinline__ float approx_quotient(float x, const GroupScale& g) {
     return (g.s == 0.0f) ? x : (x * g.p2) * g.r;
@@ -59,9 +84,13 @@ __device__ __forceinline__ float approx_quotient(float x, const GroupScale& g) {
 // The E4M3 value nearest to the exact quotient x / s.  `q` is the approximate quotient.  Away from an
 // E4M3 rounding midpoint q already rounds like the exact quotient, so q is returned and the hardware
 // conversion (round to nearest even) finishes the job.  Within 2^-18 quanta of a midpoint -- a band
-// wider than q's error -- the side is decided exactly: |x| is compared with midpoint * s in fp64,
-// where the product (<= 5 + 24 significant bits) and the difference's sign are exact.
-__device__ __forceinline__ float resolve_midpoint(float x, float q, float s) {
+// wider than q's error -- the side is decided exactly from the sign of |x| p2 - mid (s p2), formed by one
+// fused multiply-add: mid = (2 fl + 1) 2^(qe-1) has at most 5 significant bits and both products by the
+// power of two p2 are exact, so the fma rounds the exact difference once, which keeps its sign.  Both
+// terms are multiples of 2^-133 (|x| p2 because x is bf16; mid s p2 is a multiple of a coarser power of
+// two since mid >= 2^-10 and s p2 >= 2^-85 in either case), so a nonzero difference is at least 2^-133 and
+// never rounds to zero.
+__device__ __forceinline__ float resolve_midpoint(float x, float q, const GroupScale& g) {
     float aq = fabsf(q);
     int e = __builtin_amdgcn_frexp_expf(aq);            // aq = f * 2^e, f in [0.5, 1)
     int qe = max(e - 1, -6) - 3;                        // log2 of the E4M3 quantum at aq
@@ -69,11 +98,11 @@ __device__ __forceinline__ float resolve_midpoint(float x, float q, float s) {
     float fl = floorf(y);
     float frac = y - fl;
     if (fabsf(frac - 0.5f) > 0x1p-18f) return q;
-    double mid = ((double)fl + 0.5) * __builtin_amdgcn_ldexp((double)1.0, qe);
-    double d = fabs((double)x) - mid * (double)s;
+    const float mid = __builtin_amdgcn_ldexpf(fl + 0.5f, qe);
+    const float d = fmaf(-mid, g.s * g.p2, fabsf(x) * g.p2);
     float pick;
-    if (d > 0.0) pick = fl + 1.0f;
-    else if (d < 0.0) pick = fl;
+    if (d > 0.0f) pick = fl + 1.0f;
+    else if (d < 0.0f) pick = fl;
     else pick = (((int)fl & 1) == 0) ? fl : fl + 1.0f;   // exact tie: even code
     return copysignf(__builtin_amdgcn_ldexpf(pick, qe), x);
 }
@@ -87,7 +116,7 @@ __device__ __forceinline__ uint32_t cvt2_e4m3(float a, float b, uint32_t old) {
 
 __device__ __forceinline__ float quantize_value(float x, const GroupScale& g) {
     float q = approx_quotient(x, g);
-    return resolve_midpoint(x, q, g.s);
+    return resolve_midpoint(x, q, g);
 }
 
 // Eight codes of one group, packed little-endian into two uint32.
@@ -95,11 +124,11 @@ __device__ __forceinline__ float quantize_value(float x, const GroupScale& g) {
 // Fast path: q = fl32(x * rcp) is within 3 ulps of x / s (rcp within 1 ulp of 1 / s, one more rounding),
 // and the hardware conversion rounds q to nearest even.  That equals the rounding of the exact quotient
 // unless an E4M3 rounding midpoint lies between q and x / s, or q is itself a midpoint.  Every midpoint
-// (and zero) has the low 15 bits of its fp32 pattern clear -- the normal-range midpoints have 19, the
-// subnormal-range ones at least 20 -- and a midpoint within 3 ulps of q is in q's binade, so it is within 3
-// of q's bit pattern.  Whenever some q of the eight has its pattern within 4 of a multiple of 2^15 (or the
-// group's scale is tiny), all eight take the exact path above.  That happens for about 2^-11.8 of the
-// elements of ordinary data; exact zeros always take it.
+// has at most 4 fraction bits -- an odd multiple of 2^(E-4) inside the binade [2^E, 2^(E+1)) of the normal
+// range, an odd multiple of 2^-10 below 2^-6 -- so the low 19 bits of its fp32 pattern are clear, and a
+// midpoint within 3 ulps of q has its pattern within 3 of q's.
+// Whenever some q of the eight has its pattern within 4 of a multiple of 2^19 (or the group's scale is
+// tiny), all eight take the exact path above: about 2^-15.8 of the elements of ordinary data.
 __device__ __forceinline__ uint2 pack8(const float q[8]) {
     uint2 out;
     out.x = cvt2_e4m3<true>(q[2], q[3], cvt2_e4m3<false>(q[0], q[1], 0u));
@@ -114,9 +143,9 @@ __device__ __forceinline__ uint2 encode8_fast(const float x[8], const GroupScale
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         q[i] = x[i] * g.rcp;
-        near = min(near, (__float_as_uint(q[i]) + 4u) & 0x7FFFu);
+        near = min(near, (__float_as_uint(q[i]) + 4u) << 13);     // low 19 bits of (pattern + 4), at the top
     }
-    redo = g.tiny || near <= 8u;
+    redo = g.tiny || near <= (8u << 13);
     return pack8(q);
 }
 

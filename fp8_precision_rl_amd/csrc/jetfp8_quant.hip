@@ -11,13 +11,8 @@
 
 namespace jetfp8 {
 
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-
-// 16-byte streaming load (read once: non-temporal).
-__device__ __forceinline__ uint4 load16_nt(const uint16_t* p) {
-    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
-    return make_uint4(v[0], v[1], v[2], v[3]);
-}
+// 16-byte load (plain: measured faster than non-temporal loads for these access patterns on gfx950).
+__device__ __forceinline__ uint4 load16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
 
 __device__ __forceinline__ void unpack8(const uint4& v, float f[8]) {
     f[0] = bf16_to_f32(v.x & 0xFFFFu); f[1] = bf16_to_f32(v.x >> 16);
@@ -29,7 +24,9 @@ __device__ __forceinline__ void unpack8(const uint4& v, float f[8]) {
 // 1x128 groups.  A block of QR_WAVES waves owns a tile of 32 rows x 512 columns (4 groups per row): each
 // wave reads 1 KB runs of one row (16 lanes per group, 8 bf16 per lane) and writes 512-byte runs of codes;
 // the tile's 4 x 32 scales are written as four whole 128-byte lines.  All loads of a thread are issued
-// before the first is used.  Blocks are numbered along the columns first.
+// before the first is used, unconditionally: lanes past the last row or column load an in-bounds stand-in
+// (row R-1, column 0) and store nothing, so no branch separates the loads.  Blocks are numbered along the
+// columns first.
 constexpr int QR_ROWS = 32, QR_COLS = 512, QR_WAVES = 8, QR_PASSES = QR_ROWS / QR_WAVES;
 
 __global__ __launch_bounds__(QR_WAVES * 64) void quant_rows_kernel(const uint16_t* __restrict__ x, int64_t R,
@@ -42,23 +39,19 @@ __global__ __launch_bounds__(QR_WAVES * 64) void quant_rows_kernel(const uint16_
     const int64_t c0 = (int64_t)cb * QR_COLS, r0 = (int64_t)rb * QR_ROWS;
     const int64_t col = c0 + gl * 128 + lane16 * 8;
     const bool col_ok = col < C;       // C is a multiple of 128: a group is wholly inside or outside
+    const int64_t lcol = col_ok ? col : 0;
     uint4 v[QR_PASSES];
 #pragma unroll
     for (int p = 0; p < QR_PASSES; ++p) {
-        const int64_t row = r0 + p * QR_WAVES + wave;
-        v[p] = make_uint4(0, 0, 0, 0);
-        if (col_ok && row < R) v[p] = load16_nt(x + row * C + col);
+        const int64_t row = min(r0 + p * QR_WAVES + wave, R - 1);
+        v[p] = load16(x + row * C + lcol);
     }
 #pragma unroll
     for (int p = 0; p < QR_PASSES; ++p) {
         const int64_t row = r0 + p * QR_WAVES + wave;
         float f[8];
         unpack8(v[p], f);
-        float a = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(f[i]));
-        a = row16_max(a);
-        const GroupScale gs = make_group_scale(a);
+        const GroupScale gs = make_group_scale(bf16_to_f32(row16_max_u32(amax8_bits(v[p]))));
         const uint2 out = encode8(f, gs);
         if (col_ok && row < R) *reinterpret_cast<uint2*>(q + row * C + col) = out;
         if (lane16 == 0) sc[gl][p * QR_WAVES + wave] = gs.s;
@@ -86,29 +79,31 @@ __global__ __launch_bounds__(256) void quant_cols_t_kernel(const uint16_t* __res
     const int64_t r0 = (int64_t)rb * 128;
     const int64_t c = (int64_t)cb * 128 + wave * 32 + k * 8;     // first of this lane's 8 columns
     const bool ok = c < C;                                         // C is a multiple of 64, so of 8
+    const int64_t lc = ok ? c : 0;                                 // in-bounds stand-in: loaded, never stored
     uint4 v[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        v[i] = make_uint4(0, 0, 0, 0);
-        if (ok) v[i] = load16_nt(x + (r0 + 8 * l + i) * C + c);
-    }
+    for (int i = 0; i < 8; ++i) v[i] = load16(x + (r0 + 8 * l + i) * C + lc);
     // column j of the sub-tile: element i is the 16-bit half (j & 1) of word (j >> 1) of v[i]
     auto elem = [&](int i, int j) -> float {
         const uint32_t w = (j >> 1) == 0 ? v[i].x : (j >> 1) == 1 ? v[i].y : (j >> 1) == 2 ? v[i].z : v[i].w;
         return bf16_to_f32((j & 1) ? (w >> 16) : (w & 0xFFFFu));
     };
+    // per-lane magnitude maxima of the 8 columns, two columns per word
+    uint32_t cm[4];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        auto word = [&](int i) { return w == 0 ? v[i].x : w == 1 ? v[i].y : w == 2 ? v[i].z : v[i].w; };
+        cm[w] = max_mag2(max_mag2(max_mag2(word(0), word(1)), max_mag2(word(2), word(3))),
+                         max_mag2(max_mag2(word(4), word(5)), max_mag2(word(6), word(7))));
+    }
     float my_scale = 0.0f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         float f[8];
-        float a = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            f[i] = elem(i, j);
-            a = fmaxf(a, fabsf(f[i]));
-        }
-        a = row16_max(a);
-        const GroupScale gs = make_group_scale(a);
+        for (int i = 0; i < 8; ++i) f[i] = elem(i, j);
+        const uint32_t half = (j & 1) ? (cm[j >> 1] >> 16) : (cm[j >> 1] & 0xFFFFu);
+        const GroupScale gs = make_group_scale(bf16_to_f32(row16_max_u32(half)));
         const uint2 out = encode8(f, gs);
         if (ok) *reinterpret_cast<uint2*>(qT + (c + j) * R + r0 + 8 * l) = out;
         if (l == j) my_scale = gs.s;
@@ -122,30 +117,26 @@ __global__ __launch_bounds__(256) void quant_cols_t_kernel(const uint16_t* __res
 __global__ __launch_bounds__(256) void quant_blocks_kernel(const uint16_t* __restrict__ x, int64_t R, int64_t C,
                                                            uint8_t* __restrict__ q, float* __restrict__ s,
                                                            uint8_t* __restrict__ qT) {
-    __shared__ float wred[4];
+    __shared__ uint32_t wred[4];
     __shared__ uint8_t codes[128][128 + 4];
     const int t = threadIdx.x;
     const int64_t r0 = (int64_t)blockIdx.y * 128, c0 = (int64_t)blockIdx.x * 128;
     const int ch = t & 15;                    // 16-byte chunk within a 256-byte row
     float f[8][8];
-    float a = 0.0f;
+    uint32_t a = 0;      // magnitude maximum as a bf16 bit pattern (see amax8_bits)
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int row = (t >> 4) + 16 * i;
-        const uint4 v = *reinterpret_cast<const uint4*>(x + (r0 + row) * C + c0 + ch * 8);
-        f[i][0] = bf16_to_f32(v.x & 0xFFFFu); f[i][1] = bf16_to_f32(v.x >> 16);
-        f[i][2] = bf16_to_f32(v.y & 0xFFFFu); f[i][3] = bf16_to_f32(v.y >> 16);
-        f[i][4] = bf16_to_f32(v.z & 0xFFFFu); f[i][5] = bf16_to_f32(v.z >> 16);
-        f[i][6] = bf16_to_f32(v.w & 0xFFFFu); f[i][7] = bf16_to_f32(v.w >> 16);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) a = fmaxf(a, fabsf(f[i][j]));
+        const uint4 v = load16(x + (r0 + row) * C + c0 + ch * 8);
+        unpack8(v, f[i]);
+        a = max(a, amax8_bits(v));
     }
 #pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) a = fmaxf(a, __shfl_xor(a, m, 64));
+    for (int m = 32; m >= 1; m >>= 1) a = max(a, (uint32_t)__shfl_xor((int)a, m, 64));
     if ((t & 63) == 0) wred[t >> 6] = a;
     __syncthreads();
-    a = fmaxf(fmaxf(wred[0], wred[1]), fmaxf(wred[2], wred[3]));
-    const GroupScale gs = make_group_scale(a);
+    a = max(max(wred[0], wred[1]), max(wred[2], wred[3]));
+    const GroupScale gs = make_group_scale(bf16_to_f32(a));
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int row = (t >> 4) + 16 * i;
