@@ -81,30 +81,19 @@ __device__ __forceinline__ float approx_quotient(float x, const GroupScale& g) {
     return (g.s == 0.0f) ? x : (x * g.p2) * g.r;
 }
 
-// The E4M3 value nearest to the exact quotient x / s.  `q` is the approximate quotient.  Away from an
-// E4M3 rounding midpoint q already rounds like the exact quotient, so q is returned and the hardware
-// conversion (round to nearest even) finishes the job.  Within 2^-18 quanta of a midpoint -- a band
-// wider than q's error -- the side is decided exactly from the sign of |x| p2 - mid (s p2), formed by one
-// fused multiply-add: mid = (2 fl + 1) 2^(qe-1) has at most 5 significant bits and both products by the
-// power of two p2 are exact, so the fma rounds the exact difference once, which keeps its sign.  Both
-// terms are multiples of 2^-133 (|x| p2 because x is bf16; mid s p2 is a multiple of a coarser power of
-// two since mid >= 2^-10 and s p2 >= 2^-85 in either case), so a nonzero difference is at least 2^-133 and
-// never rounds to zero.
-__device__ __forceinline__ float resolve_midpoint(float x, float q, const GroupScale& g) {
-    float aq = fabsf(q);
-    int e = __builtin_amdgcn_frexp_expf(aq);            // aq = f * 2^e, f in [0.5, 1)
-    int qe = max(e - 1, -6) - 3;                        // log2 of the E4M3 quantum at aq
-    float y = __builtin_amdgcn_ldexpf(aq, -qe);         // aq in quanta: [8,16) normal, [0,8) subnormal
-    float fl = floorf(y);
-    float frac = y - fl;
-    if (fabsf(frac - 0.5f) > 0x1p-18f) return q;
-    const float mid = __builtin_amdgcn_ldexpf(fl + 0.5f, qe);
-    const float d = fmaf(-mid, g.s * g.p2, fabsf(x) * g.p2);
-    float pick;
-    if (d > 0.0f) pick = fl + 1.0f;
-    else if (d < 0.0f) pick = fl;
-    else pick = (((int)fl & 1) == 0) ? fl : fl + 1.0f;   // exact tie: even code
-    return copysignf(__builtin_amdgcn_ldexpf(pick, qe), x);
+// Exact rounding near a midpoint.  `q` approximates x / s within 3 ulps and `m` is the E4M3 rounding
+// midpoint nearest to it (see encode8).  The side of m on which the exact quotient lies is the sign of
+// |x| p2 - m (s p2), formed by one fused multiply-add: m has at most 5 significant bits and both products by
+// the power of two p2 are exact, so the fma rounds the exact difference once, which keeps its sign.  Both
+// terms are multiples of 2^-133 (|x| p2 because x is bf16; m s p2 because m is a multiple of 2^-10 and s p2 a
+// normal fp32 >= 2^-85), so a nonzero difference is at least 2^-133 and never rounds to zero.  The result
+// is m's fp32 neighbour on that side, which the hardware conversion rounds away from m, or m itself on an
+// exact tie, which the conversion rounds to the even code.
+__device__ __forceinline__ float resolve_at_midpoint(float x, float m, const GroupScale& g) {
+    const float d = fmaf(-m, g.s * g.p2, fabsf(x) * g.p2);
+    const uint32_t mb = __float_as_uint(m);
+    const float r = d > 0.0f ? __uint_as_float(mb + 1u) : (d < 0.0f ? __uint_as_float(mb - 1u) : m);
+    return copysignf(r, x);
 }
 
 // Two E4M3 codes packed into the low (HI_WORD=false) or high 16 bits of `old`.  The quotients never
@@ -114,21 +103,21 @@ __device__ __forceinline__ uint32_t cvt2_e4m3(float a, float b, uint32_t old) {
     return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)old, HI_WORD);
 }
 
-__device__ __forceinline__ float quantize_value(float x, const GroupScale& g) {
-    float q = approx_quotient(x, g);
-    return resolve_midpoint(x, q, g);
-}
-
 // Eight codes of one group, packed little-endian into two uint32.
 //
-// Fast path: q = fl32(x * rcp) is within 3 ulps of x / s (rcp within 1 ulp of 1 / s, one more rounding),
-// and the hardware conversion rounds q to nearest even.  That equals the rounding of the exact quotient
-// unless an E4M3 rounding midpoint lies between q and x / s, or q is itself a midpoint.  Every midpoint
-// has at most 4 fraction bits -- an odd multiple of 2^(E-4) inside the binade [2^E, 2^(E+1)) of the normal
-// range, an odd multiple of 2^-10 below 2^-6 -- so the low 19 bits of its fp32 pattern are clear, and a
-// midpoint within 3 ulps of q has its pattern within 3 of q's.
-// Whenever some q of the eight has its pattern within 4 of a multiple of 2^19 (or the group's scale is
-// tiny), all eight take the exact path above: about 2^-15.8 of the elements of ordinary data.
+// q = fl32(x * rcp) is within 3 ulps of x / s (rcp within 1 ulp of 1 / s, one more rounding; a tiny scale
+// uses the p2-scaled quotient, same bound), and the hardware conversion rounds q to nearest even.  That
+// equals the rounding of the exact quotient unless an E4M3 rounding midpoint lies between q and x / s, or q
+// is itself one: such a midpoint is within 3 ulps of q.  Each element is screened on its own:
+//   - normal range (>= 2^-6): the midpoints are 1.mmm1 x 2^E, patterns that are odd multiples of 2^19 (low
+//     20 bits exactly 0x80000), at least 2^(E-4) inside their binade; a q within 3 ulps shares the binade,
+//     so its pattern is within 3 of the midpoint's.  Screen: low 20 bits of (pattern + 4 - 0x80000) <= 8;
+//     the midpoint is then the pattern rounded to a multiple of 2^19.
+//   - below 2^-6 the midpoints are the odd multiples of 2^-10: every nonzero q at or below 2^-6 + 3 ulps is
+//     screened, with the midpoint (floor(512 |q|) + 1/2) / 512 of its quantum cell.
+// The representable values (low 20 bits zero), among them the 448 of each group's largest element, pass.
+// A screened element (about 0.5 % of LLM-like bf16 data, where x and amax share 8-bit significands) takes
+// resolve_at_midpoint in a branch of its own, so a wave pays for the element positions its lanes flagged.
 __device__ __forceinline__ uint2 pack8(const float q[8]) {
     uint2 out;
     out.x = cvt2_e4m3<true>(q[2], q[3], cvt2_e4m3<false>(q[0], q[1], 0u));
@@ -136,30 +125,27 @@ __device__ __forceinline__ uint2 pack8(const float q[8]) {
     return out;
 }
 
-// Fast path only: the eight codes, and whether they must be redone by encode8_exact.
-__device__ __forceinline__ uint2 encode8_fast(const float x[8], const GroupScale& g, bool& redo) {
+__device__ __forceinline__ uint2 encode8(const float x[8], const GroupScale& g) {
     float q[8];
-    uint32_t near = 0xFFFFFFFFu;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) q[i] = x[i] * g.rcp;
+    if (g.tiny) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) q[i] = approx_quotient(x[i], g);
+    }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        q[i] = x[i] * g.rcp;
-        near = min(near, (__float_as_uint(q[i]) + 4u) << 13);     // low 19 bits of (pattern + 4), at the top
+        const uint32_t b = __float_as_uint(q[i]);
+        const bool near_mid = ((b + (4u - 0x80000u)) << 12) <= (8u << 12);
+        const bool small = (b << 1) - 2u <= 2u * (0x3C800000u + 3u) - 2u;   // 0 < |q| <= 2^-6 + 3 ulps
+        if (near_mid || small) {
+            const float aq = fabsf(q[i]);
+            const float m = small ? (floorf(aq * 512.0f) + 0.5f) * 0x1p-9f
+                                  : __uint_as_float((__float_as_uint(aq) + 0x40000u) & 0xFFF80000u);
+            q[i] = resolve_at_midpoint(x[i], m, g);
+        }
     }
-    redo = g.tiny || near <= (8u << 13);
     return pack8(q);
-}
-
-__device__ __forceinline__ uint2 encode8_exact(const float x[8], const GroupScale& g) {
-    float q[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) q[i] = quantize_value(x[i], g);
-    return pack8(q);
-}
-
-__device__ __forceinline__ uint2 encode8(const float x[8], const GroupScale& g) {
-    bool redo;
-    const uint2 c = encode8_fast(x, g, redo);
-    return redo ? encode8_exact(x, g) : c;
 }
 
 }  // namespace jetfp8

@@ -11,6 +11,8 @@ constexpr int64_t kMaxGemmBand = ((int64_t)1 << 31) - 1;
 
 hipError_t launch_quant_rows(const uint16_t* x, int64_t R, int64_t C, uint8_t* q, float* s, hipStream_t st);
 hipError_t launch_quant_cols_t(const uint16_t* x, int64_t R, int64_t C, uint8_t* qT, float* sT, hipStream_t st);
+hipError_t launch_quant_dual(const uint16_t* x, int64_t R, int64_t C, uint8_t* q, float* s, uint8_t* qT, float* sT,
+                             hipStream_t st);
 hipError_t launch_quant_blocks(const uint16_t* x, int64_t R, int64_t C, uint8_t* q, float* s, uint8_t* qT,
                                hipStream_t st);
 

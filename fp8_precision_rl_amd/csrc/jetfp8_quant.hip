@@ -9,6 +9,10 @@
 #include "jetfp8_common.h"
 #include "jetfp8_launch.h"
 
+#ifndef JETFP8_DUAL_LDS
+#define JETFP8_DUAL_LDS true
+#endif
+
 namespace jetfp8 {
 
 // 16-byte load (plain: measured faster than non-temporal loads for these access patterns on gfx950).
@@ -112,6 +116,106 @@ __global__ __launch_bounds__(256) void quant_cols_t_kernel(const uint16_t* __res
     if (ok && l < 8) sT[(int64_t)rb * C + c + l] = my_scale;
 }
 
+// 1x128 and 128x1 groups of the same tensor from one read (the activation / gradient feeding a forward or DGrad
+// GEMM and a WGrad GEMM): codes q [R][C] with scales s [C/128][R], and transposed codes qT [C][R] with scales
+// sT [R/128][C].  A 256-thread block owns a 128x128 tile, so each of its rows is one 1x128 group and each of its
+// columns one 128x1 group.  Lane l of DPP row k of wave w holds the 8x8 sub-tile of rows 8 (4w + k) .. +7 and
+// columns 8 l .. +7 (eight 16-byte loads; a DPP row reads 256 contiguous bytes of each of its rows):
+//   - a row's group lies in one DPP row: its amax is a 16-lane row reduction, and the 16 lanes write the row's
+//     128 codes as one contiguous run;
+//   - a column's group spans the whole block: per-lane maxima, then across the wave's four DPP rows, then
+//     across the four waves through LDS.  With T_VIA_LDS the transposed codes are staged in LDS and leave as
+//     whole 128-byte transposed rows; otherwise each lane writes its 8 bytes of each column directly.
+template <bool T_VIA_LDS>
+__global__ __launch_bounds__(256) void quant_dual_kernel(const uint16_t* __restrict__ x, int64_t R, int64_t C,
+                                                         uint8_t* __restrict__ q, float* __restrict__ s,
+                                                         uint8_t* __restrict__ qT, float* __restrict__ sT,
+                                                         uint32_t col_blocks) {
+    __shared__ uint32_t red[4][16][4];
+    __shared__ uint32_t tcodes[T_VIA_LDS ? 128 : 1][33];     // [column][4-row word], odd pitch
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int l16 = lane & 15, rs = lane >> 4, rb8 = 4 * wave + rs;
+    const uint32_t cb = blockIdx.x % col_blocks, rb = blockIdx.x / col_blocks;
+    const int64_t r0 = (int64_t)rb * 128, c0 = (int64_t)cb * 128;
+    const int64_t rr = r0 + 8 * rb8;        // first of this lane's 8 rows
+    const int64_t c = c0 + 8 * l16;         // first of this lane's 8 columns
+    uint4 v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = load16(x + (rr + i) * C + c);
+
+    // column maxima (two columns per word): this lane's 8 rows, then the wave's 4 DPP rows
+    uint32_t cm[4];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        auto word = [&](int i) { return w == 0 ? v[i].x : w == 1 ? v[i].y : w == 2 ? v[i].z : v[i].w; };
+        uint32_t m = max_mag2(max_mag2(max_mag2(word(0), word(1)), max_mag2(word(2), word(3))),
+                              max_mag2(max_mag2(word(4), word(5)), max_mag2(word(6), word(7))));
+        m = max_mag2(m, (uint32_t)__shfl_xor((int)m, 16, 64));
+        m = max_mag2(m, (uint32_t)__shfl_xor((int)m, 32, 64));
+        cm[w] = m;
+    }
+    if (rs == 0) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) red[wave][l16][w] = cm[w];
+    }
+
+    // 1x128 groups: one per row
+    float row_scale = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        float f[8];
+        unpack8(v[i], f);
+        const GroupScale gs = make_group_scale(bf16_to_f32(row16_max_u32(amax8_bits(v[i]))));
+        *reinterpret_cast<uint2*>(q + (rr + i) * C + c) = encode8(f, gs);
+        if (l16 == i) row_scale = gs.s;
+    }
+    if (l16 < 8) s[(c0 / 128) * R + rr + l16] = row_scale;
+
+    // 128x1 groups: one per column
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+        cm[w] = max_mag2(max_mag2(red[0][l16][w], red[1][l16][w]), max_mag2(red[2][l16][w], red[3][l16][w]));
+    auto elem = [&](int i, int j) -> float {
+        const uint32_t w = (j >> 1) == 0 ? v[i].x : (j >> 1) == 1 ? v[i].y : (j >> 1) == 2 ? v[i].z : v[i].w;
+        return bf16_to_f32((j & 1) ? (w >> 16) : (w & 0xFFFFu));
+    };
+    float col_scale_a = 0.0f, col_scale_b = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        float f[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) f[i] = elem(i, j);
+        const uint32_t half = (j & 1) ? (cm[j >> 1] >> 16) : (cm[j >> 1] & 0xFFFFu);
+        const GroupScale gs = make_group_scale(bf16_to_f32(half));
+        const uint2 out = encode8(f, gs);
+        if (T_VIA_LDS) {
+            tcodes[8 * l16 + j][2 * rb8] = out.x;
+            tcodes[8 * l16 + j][2 * rb8 + 1] = out.y;
+        } else {
+            *reinterpret_cast<uint2*>(qT + (c + j) * R + rr) = out;
+        }
+        if (j == rs) col_scale_a = gs.s;
+        if (j == rs + 4) col_scale_b = gs.s;
+    }
+    // wave 0 writes the tile's 128 column scales: lane (l, k) those of columns 8 l + k and 8 l + k + 4
+    if (wave == 0) {
+        sT[(int64_t)rb * C + c + rs] = col_scale_a;
+        sT[(int64_t)rb * C + c + rs + 4] = col_scale_b;
+    }
+    if (T_VIA_LDS) {
+        __syncthreads();
+        // thread t writes bytes 64 (t & 1) .. +63 of transposed row c0 + t / 2
+        const int oc = t >> 1, hf = t & 1;
+        uint4* dst = reinterpret_cast<uint4*>(qT + (c0 + oc) * R + r0 + 64 * hf);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint32_t* src = &tcodes[oc][16 * hf + 4 * k];
+            dst[k] = make_uint4(src[0], src[1], src[2], src[3]);
+        }
+    }
+}
+
 // One block owns one 128x128 block: 8 rows x 8 columns per thread, a block-wide amax, codes written in
 // place and, through an LDS transpose, to the transposed copy.
 __global__ __launch_bounds__(256) void quant_blocks_kernel(const uint16_t* __restrict__ x, int64_t R, int64_t C,
@@ -179,6 +283,16 @@ hipError_t launch_quant_cols_t(const uint16_t* x, int64_t R, int64_t C, uint8_t*
     if (col_blocks * row_blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(quant_cols_t_kernel, dim3((unsigned)(col_blocks * row_blocks)), dim3(256), 0, st, x, R, C, qT,
                        sT, (uint32_t)col_blocks);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_dual(const uint16_t* x, int64_t R, int64_t C, uint8_t* q, float* s, uint8_t* qT, float* sT,
+                             hipStream_t st) {
+    // R and C are multiples of 128 (whole groups both ways)
+    const int64_t col_blocks = C / 128, row_blocks = R / 128;
+    if (col_blocks * row_blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(quant_dual_kernel<JETFP8_DUAL_LDS>, dim3((unsigned)(col_blocks * row_blocks)), dim3(256), 0, st, x,
+                       R, C, q, s, qT, sT, (uint32_t)col_blocks);
     return hipGetLastError();
 }
 
