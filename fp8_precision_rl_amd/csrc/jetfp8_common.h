@@ -125,24 +125,45 @@ __device__ __forceinline__ uint2 pack8(const float q[8]) {
     return out;
 }
 
+// Midpoint of the E4M3 quantum cell that holds |q| (see encode8): q's pattern rounded to a multiple of 2^19 in
+// the normal range, (floor(512 |q|) + 1/2) / 512 below 2^-6.
+__device__ __forceinline__ float cell_midpoint(float q, bool small) {
+    const float aq = fabsf(q);
+    return small ? (floorf(aq * 512.0f) + 0.5f) * 0x1p-9f
+                 : __uint_as_float((__float_as_uint(aq) + 0x40000u) & 0xFFF80000u);
+}
+
 __device__ __forceinline__ uint2 encode8(const float x[8], const GroupScale& g) {
+    constexpr uint32_t kSmall = 2u * (0x3C800000u + 3u) - 2u;    // (2 |q| pattern - 2) <= kSmall: 0 < |q| <= 2^-6 + 3 ulps
     float q[8];
+    uint32_t smin = 0xFFFFFFFFu;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) q[i] = x[i] * g.rcp;
+    for (int i = 0; i < 8; ++i) {
+        q[i] = x[i] * g.rcp;
+        smin = min(smin, (__float_as_uint(q[i]) << 1) - 2u);    // +-0 wraps to the top
+    }
     if (g.tiny) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) q[i] = approx_quotient(x[i], g);
+        smin = 0;     // screen every element below
     }
+    // (pattern + 4 - 0x80000) << 12 with the constant held in a scalar register, so that each element's screen
+    // is one v_add_lshl_u32 (the compiler would otherwise rematerialize the literal into a vector register)
+    uint32_t k_mid;
+    asm("s_mov_b32 %0, 0xfff80004" : "=s"(k_mid));
+    if (smin <= kSmall) {
+        // rare: some quotient of this lane is at or below 2^-6 (or the scale is tiny)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const uint32_t b = __float_as_uint(q[i]);
-        const bool near_mid = ((b + (4u - 0x80000u)) << 12) <= (8u << 12);
-        const bool small = (b << 1) - 2u <= 2u * (0x3C800000u + 3u) - 2u;   // 0 < |q| <= 2^-6 + 3 ulps
-        if (near_mid || small) {
-            const float aq = fabsf(q[i]);
-            const float m = small ? (floorf(aq * 512.0f) + 0.5f) * 0x1p-9f
-                                  : __uint_as_float((__float_as_uint(aq) + 0x40000u) & 0xFFF80000u);
-            q[i] = resolve_at_midpoint(x[i], m, g);
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t b = __float_as_uint(q[i]);
+            const bool small = (b << 1) - 2u <= kSmall;
+            if (small || ((b + k_mid) << 12) <= (8u << 12)) q[i] = resolve_at_midpoint(x[i], cell_midpoint(q[i], small), g);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            if (((__float_as_uint(q[i]) + k_mid) << 12) <= (8u << 12))
+                q[i] = resolve_at_midpoint(x[i], cell_midpoint(q[i], false), g);
         }
     }
     return pack8(q);
