@@ -2,9 +2,10 @@
 """Benchmark of the FP8 group-quantize + block-scaled GEMM path on one MI355X.
 
 A step is one pass of the whole hot path over one batch of synthetic inputs, for every linear of the
-workload: 128x128 block quantization of the bf16 master weights (with the transposed copy), 1x128
-quantization of X, the forward GEMM, 1x128 quantization of dY, DGrad, 128x1 quantization of dY and X
-(transposed), WGrad.  Inputs are generated on the GPU and resident in HBM before timing starts; outputs
+workload: 128x128 block quantization of the bf16 master weights (with the transposed copy), 1x128 and
+128x1 (transposed) quantization of X from one read, the forward GEMM, 1x128 and 128x1 quantization of dY
+from one read, DGrad, WGrad.  --separate-quant runs the 1x128 and 128x1 quantizers as separate kernels
+(two reads of X and of dY) instead; the codes and scales are the same bits either way.  Inputs are generated on the GPU and resident in HBM before timing starts; outputs
 are preallocated.  The headline value is GEMM TFLOP/s over the whole step (GEMM flops / step time,
 quantization included).
 
@@ -39,6 +40,8 @@ def parse():
     p.add_argument("--cpu-sample-rows", type=int, default=128)
     p.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "gemm_traffic.json"),
                    help="per-launch HBM bytes measured by rocprofv3 for this workload (optional)")
+    p.add_argument("--separate-quant", action="store_true",
+                   help="quantize X and dY with the 1x128 and 128x1 kernels separately (two reads each)")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="first run a 1 GiB device-to-device copy (known bytes) to scale rocprofv3 byte counters")
     return p.parse_args()
@@ -106,13 +109,15 @@ class Linear:
     def quant_bytes(self):
         M, N, K = self.M, self.N, self.K
         rows = 2 + 1 + 4 / 128                      # bf16 in, code out, one fp32 scale per 128
+        dual = 2 + 2 + 8 / 128                      # bf16 in, both codes out, both scales
         return {"w_blocks_T": N * K * (2 + 1 + 1 + 4 / 16384), "x_rows": M * K * rows, "dy_rows": M * N * rows,
-                "dy_cols_t": M * N * rows, "x_cols_t": M * K * rows}
+                "dy_cols_t": M * N * rows, "x_cols_t": M * K * rows, "x_dual": M * K * dual, "dy_dual": M * N * dual}
 
 
-def run_step(L, jf, st, ev=None):
+def run_step(L, jf, st, ev=None, fused=True):
     """One pass of the hot path over one linear.  ev: optional list collecting (kind, name, flops_or_bytes,
-    start_event, end_event) around each launch."""
+    start_event, end_event) around each launch.  fused: X and dY are quantized in both groupings by one
+    kernel each (one read); otherwise by the 1x128 and the 128x1 kernels separately."""
     M, N, K = L.M, L.N, L.K
 
     def timed(kind, name, amount, fn):
@@ -129,15 +134,25 @@ def run_step(L, jf, st, ev=None):
     qb = L.quant_bytes()
     timed("quant", "w_blocks_T", qb["w_blocks_T"],
           lambda: jf.jetfp8_quantize(L.w, N, K, jf.BLOCKS_128x128, L.wq, L.ws, L.wqT, st))
-    timed("quant", "x_rows", qb["x_rows"], lambda: jf.jetfp8_quantize(L.x, M, K, jf.ROWS_1x128, L.xq, L.xs, None, st))
+    if fused:
+        timed("quant", "x_dual", qb["x_dual"],
+              lambda: jf.jetfp8_quantize_dual(L.x, M, K, L.xq, L.xs, L.xqT, L.xsT, st))
+    else:
+        timed("quant", "x_rows", qb["x_rows"],
+              lambda: jf.jetfp8_quantize(L.x, M, K, jf.ROWS_1x128, L.xq, L.xs, None, st))
     timed("gemm", "fwd", 2 * M * N * K, lambda: jf.jetfp8_gemm_fwd(L.xq, L.xs, L.wq, L.ws, L.y, M, N, K, st))
-    timed("quant", "dy_rows", qb["dy_rows"],
-          lambda: jf.jetfp8_quantize(L.dy, M, N, jf.ROWS_1x128, L.dyq, L.dys, None, st))
+    if fused:
+        timed("quant", "dy_dual", qb["dy_dual"],
+              lambda: jf.jetfp8_quantize_dual(L.dy, M, N, L.dyq, L.dys, L.dyqT, L.dysT, st))
+    else:
+        timed("quant", "dy_rows", qb["dy_rows"],
+              lambda: jf.jetfp8_quantize(L.dy, M, N, jf.ROWS_1x128, L.dyq, L.dys, None, st))
     timed("gemm", "dgrad", 2 * M * N * K, lambda: jf.jetfp8_gemm_dgrad(L.dyq, L.dys, L.wqT, L.ws, L.dx, M, N, K, st))
-    timed("quant", "dy_cols_t", qb["dy_cols_t"],
-          lambda: jf.jetfp8_quantize(L.dy, M, N, jf.COLS_128x1_T, L.dyqT, L.dysT, None, st))
-    timed("quant", "x_cols_t", qb["x_cols_t"],
-          lambda: jf.jetfp8_quantize(L.x, M, K, jf.COLS_128x1_T, L.xqT, L.xsT, None, st))
+    if not fused:
+        timed("quant", "dy_cols_t", qb["dy_cols_t"],
+              lambda: jf.jetfp8_quantize(L.dy, M, N, jf.COLS_128x1_T, L.dyqT, L.dysT, None, st))
+        timed("quant", "x_cols_t", qb["x_cols_t"],
+              lambda: jf.jetfp8_quantize(L.x, M, K, jf.COLS_128x1_T, L.xqT, L.xsT, None, st))
     timed("gemm", "wgrad", 2 * M * N * K, lambda: jf.jetfp8_gemm_wgrad(L.dyqT, L.dysT, L.xqT, L.xsT, L.dw, M, N, K, st))
 
 
@@ -194,7 +209,7 @@ def main():
 
     for _ in range(args.warmup):
         for L in layers:
-            run_step(L, jf, st)
+            run_step(L, jf, st, fused=not args.separate_quant)
     torch.cuda.synchronize()
     print(f"[bench] warmup {args.warmup} done", file=sys.stderr, flush=True)
 
@@ -205,7 +220,7 @@ def main():
     t_start.record()
     for _ in range(args.steps):
         for L in layers:
-            run_step(L, jf, st, ev)
+            run_step(L, jf, st, ev, fused=not args.separate_quant)
     t_end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
@@ -244,8 +259,10 @@ def main():
                 "W~N(0,0.02^2), dY~1e-3*Student-t(3))",
         "config": {"workload": wl.name, "tokens": wl.M,
                    "linears": [{"name": n, "K": K, "N": N} for n, K, N in wl.linears],
-                   "step": "per linear: W block quant(+T), X rows quant, fwd, dY rows quant, dgrad, "
-                           "dY/X cols quant (T), wgrad"},
+                   "step": ("per linear: W block quant(+T), X rows quant, fwd, dY rows quant, dgrad, "
+                            "dY/X cols quant (T), wgrad") if args.separate_quant else
+                           ("per linear: W block quant(+T), X rows+cols(T) quant in one read, fwd, "
+                            "dY rows+cols(T) quant in one read, dgrad, wgrad")},
         "pct_of_fp8_peak": round(100 * value / FP8_PEAK_TFLOPS, 2),
         "gemm_only_tflops": round(achieved, 2),
         "wall_s": round(wall, 4),

@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_HERE, "lib", "libjetfp8.so")
 
 OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_MODE, ERR_HIP = 0, -1, -2, -3, -4, -5
 ROWS_1x128, COLS_128x1_T, BLOCKS_128x128 = 0, 1, 2
-EXPORTED = ("jetfp8_quantize", "jetfp8_gemm_fwd", "jetfp8_gemm_dgrad", "jetfp8_gemm_wgrad",
+EXPORTED = ("jetfp8_quantize", "jetfp8_quantize_dual", "jetfp8_gemm_fwd", "jetfp8_gemm_dgrad", "jetfp8_gemm_wgrad",
             "jetfp8_status_string", "jetfp8_version")
 
 _lib = None
@@ -43,6 +43,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     vp, i64, c_int = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
     L.jetfp8_quantize.restype = c_int
     L.jetfp8_quantize.argtypes = [vp, i64, i64, c_int, vp, vp, vp, vp]
+    L.jetfp8_quantize_dual.restype = c_int
+    L.jetfp8_quantize_dual.argtypes = [vp, i64, i64, vp, vp, vp, vp, vp]
     for name in ("jetfp8_gemm_fwd", "jetfp8_gemm_dgrad", "jetfp8_gemm_wgrad"):
         f = getattr(L, name)
         f.restype = c_int
@@ -97,6 +99,14 @@ def jetfp8_quantize(src_bf16, rows: int, cols: int, mode: int, dst_codes, dst_sc
     _check("jetfp8_quantize", st)
 
 
+def jetfp8_quantize_dual(src_bf16, rows: int, cols: int, dst_codes, dst_scales, dst_codes_t, dst_scales_t,
+                         stream=None) -> None:
+    L = load_library()
+    st = L.jetfp8_quantize_dual(_ptr(src_bf16), int(rows), int(cols), _ptr(dst_codes), _ptr(dst_scales),
+                                _ptr(dst_codes_t), _ptr(dst_scales_t), _stream(stream))
+    _check("jetfp8_quantize_dual", st)
+
+
 def jetfp8_gemm_fwd(xq, xs, wq, ws, y_bf16, M: int, N: int, K: int, stream=None) -> None:
     L = load_library()
     _check("jetfp8_gemm_fwd", L.jetfp8_gemm_fwd(_ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws), _ptr(y_bf16),
@@ -138,6 +148,20 @@ def quantize_cols_t(x, stream=None):
     s = torch.empty((R // 128, C), dtype=torch.float32, device=x.device)
     jetfp8_quantize(x, R, C, COLS_128x1_T, q, s, None, stream)
     return q, s
+
+
+def quantize_dual(x, stream=None):
+    """Both groupings from one read: x bf16 [R, C] -> (codes [R, C], scales [C/128, R]) as quantize_rows and
+    (codes [C, R], scales [R/128, C]) as quantize_cols_t.  R and C multiples of 128."""
+    import torch
+    _dt(x, torch.bfloat16, "x")
+    R, C = x.shape
+    q = torch.empty((R, C), dtype=torch.uint8, device=x.device)
+    s = torch.empty((C // 128, R), dtype=torch.float32, device=x.device)
+    qT = torch.empty((C, R), dtype=torch.uint8, device=x.device)
+    sT = torch.empty((R // 128, C), dtype=torch.float32, device=x.device)
+    jetfp8_quantize_dual(x, R, C, q, s, qT, sT, stream)
+    return q, s, qT, sT
 
 
 def quantize_blocks(w, transposed: bool = True, stream=None):
@@ -187,9 +211,8 @@ def linear_forward(x, wq, ws, stream=None):
 
 def linear_backward(dy, x, wqT, ws, stream=None):
     """DGrad and WGrad of the FP8 linear: dY re-quantized along each GEMM's contraction axis."""
-    dyq, dys = quantize_rows(dy, stream)
+    dyq, dys, dyqT, dysT = quantize_dual(dy, stream)
     dx = gemm_dgrad(dyq, dys, wqT, ws, stream)
-    dyqT, dysT = quantize_cols_t(dy, stream)
     xqT, xsT = quantize_cols_t(x, stream)
     dw = gemm_wgrad(dyqT, dysT, xqT, xsT, stream)
     return dx, dw

@@ -36,7 +36,7 @@ int check_gemm_extent(int64_t I, int64_t J, int64_t Kc) {
 
 extern "C" {
 
-int jetfp8_version(void) { return 100; }
+int jetfp8_version(void) { return 200; }
 
 const char* jetfp8_status_string(int status) {
     switch (status) {
@@ -72,6 +72,18 @@ int jetfp8_quantize(const void* src_bf16, int64_t rows, int64_t cols, int mode, 
         case JETFP8_COLS_128x1_T: return hip_status(jetfp8::launch_quant_cols_t(x, rows, cols, dst_codes, dst_scales, st));
         default: return hip_status(jetfp8::launch_quant_blocks(x, rows, cols, dst_codes, dst_scales, dst_codes_t, st));
     }
+}
+
+int jetfp8_quantize_dual(const void* src_bf16, int64_t rows, int64_t cols, uint8_t* dst_codes, float* dst_scales,
+                         uint8_t* dst_codes_t, float* dst_scales_t, void* stream) {
+    if (!src_bf16 || !dst_codes || !dst_scales || !dst_codes_t || !dst_scales_t) return JETFP8_ERR_NULL;
+    if (!dim_ok(rows) || !dim_ok(cols) || rows % 128 || cols % 128) return JETFP8_ERR_SHAPE;
+    if (!aligned16(src_bf16) || !aligned16(dst_codes) || !aligned16(dst_scales) || !aligned16(dst_codes_t) ||
+        !aligned16(dst_scales_t))
+        return JETFP8_ERR_ALIGN;
+    return hip_status(jetfp8::launch_quant_dual(static_cast<const uint16_t*>(src_bf16), rows, cols, dst_codes,
+                                                dst_scales, dst_codes_t, dst_scales_t,
+                                                static_cast<hipStream_t>(stream)));
 }
 
 int jetfp8_gemm_fwd(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws, void* y_bf16, int64_t M,

@@ -9,11 +9,11 @@
 #include "jetfp8_common.h"
 #include "jetfp8_launch.h"
 
-#ifndef JETFP8_DUAL_LDS
-#define JETFP8_DUAL_LDS true
-#endif
-
 namespace jetfp8 {
+
+typedef __amdgpu_buffer_rsrc_t rsrc_q_t;
+typedef unsigned int u32x4_q __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_q __attribute__((ext_vector_type(2)));
 
 // 16-byte load (plain: measured faster than non-temporal loads for these access patterns on gfx950).
 __device__ __forceinline__ uint4 load16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
@@ -124,24 +124,39 @@ __global__ __launch_bounds__(256) void quant_cols_t_kernel(const uint16_t* __res
 //   - a row's group lies in one DPP row: its amax is a 16-lane row reduction, and the 16 lanes write the row's
 //     128 codes as one contiguous run;
 //   - a column's group spans the whole block: per-lane maxima, then across the wave's four DPP rows, then
-//     across the four waves through LDS.  With T_VIA_LDS the transposed codes are staged in LDS and leave as
-//     whole 128-byte transposed rows; otherwise each lane writes its 8 bytes of each column directly.
-template <bool T_VIA_LDS>
+//     across the four waves through LDS; the transposed codes are staged in LDS and leave as whole
+//     128-byte transposed rows.
+// Memory access goes through raw buffer descriptors built from block-uniform bases (scalar registers) with
+// 32-bit lane offsets, so no 64-bit address arithmetic runs on the vector unit.  A descriptor spans exactly
+// the bytes its accesses touch; the launcher checks that every span and offset fits in 31 bits.
+__device__ __forceinline__ rsrc_q_t span_rsrc(const void* base, int64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
 __global__ __launch_bounds__(256) void quant_dual_kernel(const uint16_t* __restrict__ x, int64_t R, int64_t C,
                                                          uint8_t* __restrict__ q, float* __restrict__ s,
                                                          uint8_t* __restrict__ qT, float* __restrict__ sT,
                                                          uint32_t col_blocks) {
     __shared__ uint32_t red[4][16][4];
-    __shared__ uint32_t tcodes[T_VIA_LDS ? 128 : 1][33];     // [column][4-row word], odd pitch
-    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    __shared__ uint32_t tcodes[128][33];     // [column][4-row word], odd pitch
+    const int t = threadIdx.x, lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int l16 = lane & 15, rs = lane >> 4, rb8 = 4 * wave + rs;
     const uint32_t cb = blockIdx.x % col_blocks, rb = blockIdx.x / col_blocks;
     const int64_t r0 = (int64_t)rb * 128, c0 = (int64_t)cb * 128;
-    const int64_t rr = r0 + 8 * rb8;        // first of this lane's 8 rows
-    const int64_t c = c0 + 8 * l16;         // first of this lane's 8 columns
+    // this wave's 32 rows start at wr; the lane's 8x8 sub-tile is rows wr + 8 rs .. +7, columns c0 + 8 l16 ..
+    const int64_t wr = r0 + 32 * wave;
+    const int Ci = (int)C;
+    const int64_t span = 31 * C + 128;                       // elements from (wr, c0) to (wr + 31, c0 + 127)
+    const rsrc_q_t rx = span_rsrc(x + wr * C + c0, 2 * span);
+    const rsrc_q_t rq = span_rsrc(q + wr * C + c0, span);
+    const int lo = 8 * rs * Ci + 8 * l16;                    // element offset of the lane's first row
     uint4 v[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = load16(x + (rr + i) * C + c);
+    for (int i = 0; i < 8; ++i) {
+        const u32x4_q w = __builtin_amdgcn_raw_buffer_load_b128(rx, 2 * lo, 2 * i * Ci, 0);
+        v[i] = make_uint4(w[0], w[1], w[2], w[3]);
+    }
 
     // column maxima (two columns per word): this lane's 8 rows, then the wave's 4 DPP rows
     uint32_t cm[4];
@@ -166,10 +181,12 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(const uint16_t* __restr
         float f[8];
         unpack8(v[i], f);
         const GroupScale gs = make_group_scale(bf16_to_f32(row16_max_u32(amax8_bits(v[i]))));
-        *reinterpret_cast<uint2*>(q + (rr + i) * C + c) = encode8(f, gs);
+        const uint2 out = encode8(f, gs);
+        const u32x2_q o = {out.x, out.y};
+        __builtin_amdgcn_raw_buffer_store_b64(o, rq, lo, i * Ci, 0);
         if (l16 == i) row_scale = gs.s;
     }
-    if (l16 < 8) s[(c0 / 128) * R + rr + l16] = row_scale;
+    if (l16 < 8) s[(c0 / 128) * R + wr + (8 * rs + l16)] = row_scale;
 
     // 128x1 groups: one per column
     __syncthreads();
@@ -189,30 +206,27 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(const uint16_t* __restr
         const uint32_t half = (j & 1) ? (cm[j >> 1] >> 16) : (cm[j >> 1] & 0xFFFFu);
         const GroupScale gs = make_group_scale(bf16_to_f32(half));
         const uint2 out = encode8(f, gs);
-        if (T_VIA_LDS) {
-            tcodes[8 * l16 + j][2 * rb8] = out.x;
-            tcodes[8 * l16 + j][2 * rb8 + 1] = out.y;
-        } else {
-            *reinterpret_cast<uint2*>(qT + (c + j) * R + rr) = out;
-        }
+        tcodes[8 * l16 + j][2 * rb8] = out.x;
+        tcodes[8 * l16 + j][2 * rb8 + 1] = out.y;
         if (j == rs) col_scale_a = gs.s;
         if (j == rs + 4) col_scale_b = gs.s;
     }
     // wave 0 writes the tile's 128 column scales: lane (l, k) those of columns 8 l + k and 8 l + k + 4
     if (wave == 0) {
-        sT[(int64_t)rb * C + c + rs] = col_scale_a;
-        sT[(int64_t)rb * C + c + rs + 4] = col_scale_b;
+        float* st = sT + (int64_t)rb * C + c0;
+        st[8 * l16 + rs] = col_scale_a;
+        st[8 * l16 + rs + 4] = col_scale_b;
     }
-    if (T_VIA_LDS) {
-        __syncthreads();
-        // thread t writes bytes 64 (t & 1) .. +63 of transposed row c0 + t / 2
-        const int oc = t >> 1, hf = t & 1;
-        uint4* dst = reinterpret_cast<uint4*>(qT + (c0 + oc) * R + r0 + 64 * hf);
+    __syncthreads();
+    // thread t writes bytes 64 (t & 1) .. +63 of transposed row c0 + t / 2 (rows r0 .. r0 + 127 of it)
+    const rsrc_q_t rqt = span_rsrc(qT + c0 * R + r0, 127 * R + 128);
+    const int oc = t >> 1, hf = t & 1;
+    const int to = oc * (int)R + 64 * hf;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const uint32_t* src = &tcodes[oc][16 * hf + 4 * k];
-            dst[k] = make_uint4(src[0], src[1], src[2], src[3]);
-        }
+    for (int k = 0; k < 4; ++k) {
+        const uint32_t* src = &tcodes[oc][16 * hf + 4 * k];
+        const u32x4_q o = {src[0], src[1], src[2], src[3]};
+        __builtin_amdgcn_raw_buffer_store_b128(o, rqt, to + 16 * k, 0, 0);
     }
 }
 
@@ -291,8 +305,10 @@ hipError_t launch_quant_dual(const uint16_t* x, int64_t R, int64_t C, uint8_t* q
     // R and C are multiples of 128 (whole groups both ways)
     const int64_t col_blocks = C / 128, row_blocks = R / 128;
     if (col_blocks * row_blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(quant_dual_kernel<JETFP8_DUAL_LDS>, dim3((unsigned)(col_blocks * row_blocks)), dim3(256), 0, st, x,
-                       R, C, q, s, qT, sT, (uint32_t)col_blocks);
+    // buffer spans and offsets in 31 bits: 32 bf16 rows (2 * (31 C + 128) bytes) and 128 transposed rows
+    if (64 * C + 256 >= ((int64_t)1 << 31) || 128 * R + 128 >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(quant_dual_kernel, dim3((unsigned)(col_blocks * row_blocks)), dim3(256), 0, st, x, R, C, q, s,
+                       qT, sT, (uint32_t)col_blocks);
     return hipGetLastError();
 }
 

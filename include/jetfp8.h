@@ -75,6 +75,17 @@ typedef enum {
 int jetfp8_quantize(const void* src_bf16, int64_t rows, int64_t cols, int mode,
                     uint8_t* dst_codes, float* dst_scales, uint8_t* dst_codes_t, void* stream);
 
+/* Both groupings of one bf16 matrix from a single read of it: the 1x128 codes and scales of
+ * JETFP8_ROWS_1x128 and the transposed 128x1 codes and scales of JETFP8_COLS_128x1_T, bit for bit the
+ * outputs of those two modes.  This serves a tensor that feeds a GEMM along its contiguous axis and the
+ * WGrad GEMM along its token axis (Jet-RL explainers, "Schema de Quantification" / "Passage Arriere": dY
+ * is quantized for DGrad and for WGrad; X for the forward and for WGrad): 4 bytes of codes written per
+ * 2 bytes read, instead of reading the matrix twice.
+ * src [rows][cols] -> dst_codes [rows][cols], dst_scales [cols/128][rows], dst_codes_t [cols][rows],
+ * dst_scales_t [rows/128][cols].  rows % 128 == 0 and cols % 128 == 0; all four outputs are required. */
+int jetfp8_quantize_dual(const void* src_bf16, int64_t rows, int64_t cols, uint8_t* dst_codes,
+                         float* dst_scales, uint8_t* dst_codes_t, float* dst_scales_t, void* stream);
+
 /* Forward FP8 linear (rollout decode, prefill, training forward):
  *   Y[m][n] = sum_g xs[g][m] * ws[n/128][g] * sum_{k in g} xq[m][k] * wq[n][k]
  * xq [M][K], xs [K/128][M] (JETFP8_ROWS_1x128 of X); wq [N][K], ws [N/128][K/128]

@@ -28,7 +28,7 @@ def _declared():
 
 def test_header_declares_the_four_calls_and_helpers():
     names = _declared()
-    for n in ("jetfp8_quantize", "jetfp8_gemm_fwd", "jetfp8_gemm_dgrad", "jetfp8_gemm_wgrad",
+    for n in ("jetfp8_quantize", "jetfp8_quantize_dual", "jetfp8_gemm_fwd", "jetfp8_gemm_dgrad", "jetfp8_gemm_wgrad",
               "jetfp8_status_string", "jetfp8_version"):
         assert n in names
 
@@ -48,7 +48,7 @@ def test_status_strings(lib):
     for st in (0, -1, -2, -3, -4, -5, 7):
         s = jf.status_string(st)
         assert isinstance(s, str) and s
-    assert lib.jetfp8_version() >= 100
+    assert lib.jetfp8_version() >= 200
 
 
 P = 0x10000        # a 16-byte aligned fake address: validation rejects every call below before any use
@@ -57,6 +57,27 @@ BAD = 0x10004      # misaligned
 
 def q(lib, src=P, rows=256, cols=256, mode=0, codes=P, scales=P, codes_t=None):
     return lib.jetfp8_quantize(src, rows, cols, mode, codes, scales, codes_t, None)
+
+
+def qd(lib, src=P, rows=256, cols=256, codes=P, scales=P, codes_t=P, scales_t=P):
+    return lib.jetfp8_quantize_dual(src, rows, cols, codes, scales, codes_t, scales_t, None)
+
+
+def test_quantize_dual_validation(lib):
+    assert qd(lib, src=None) == -1
+    assert qd(lib, codes=None) == -1
+    assert qd(lib, scales=None) == -1
+    assert qd(lib, codes_t=None) == -1
+    assert qd(lib, scales_t=None) == -1
+    assert qd(lib, rows=200) == -2                  # both axes are grouped: multiples of 128
+    assert qd(lib, cols=192) == -2
+    assert qd(lib, rows=0) == -2
+    assert qd(lib, cols=1 << 31) == -2
+    assert qd(lib, src=BAD) == -3
+    assert qd(lib, codes=BAD) == -3
+    assert qd(lib, scales=BAD) == -3
+    assert qd(lib, codes_t=BAD) == -3
+    assert qd(lib, scales_t=BAD) == -3
 
 
 def test_quantize_validation(lib):

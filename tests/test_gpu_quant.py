@@ -56,6 +56,38 @@ def test_cols_t_bit_exact(jf, orc, R, C):
     assert np.array_equal(q.cpu().numpy(), oq.T)
 
 
+def _special_columns(b, seed):
+    """Column groups (128x1 view) that are all zero with a negative zero, tiny (subnormal scale), or huge."""
+    rng = np.random.default_rng(seed)
+    R, C = b.shape
+    if R >= 256 and C >= 16:
+        b[:128, 5] = 0
+        b[3, 5] = 0x8000
+        b[128:256, 9] = f32_to_bits(rng.standard_normal(128).astype(np.float32) * np.float32(1e-38))
+        b[:128, 11] = f32_to_bits(rng.standard_normal(128).astype(np.float32) * np.float32(3e37))
+    return b
+
+
+@pytest.mark.parametrize("R,C", [(128, 128), (256, 384), (384, 1024), (640, 256)])
+def test_dual_bit_exact(jf, orc, R, C):
+    """One read, both groupings: equal to the oracle's 1x128 and 128x1 quantizers and to the GPU's two
+    single-grouping kernels, bit for bit."""
+    import torch
+    b = _special_columns(_special_matrix(R, C, 3 * R + C), R + 5 * C)
+    xd = bits_to_dev(b)
+    q, s, qT, sT = jf.quantize_dual(xd)
+    q1, s1 = jf.quantize_rows(xd)
+    qT1, sT1 = jf.quantize_cols_t(xd)
+    torch.cuda.synchronize()
+    oq, os_ = orc.quantize_rows(b)
+    oqc, osc = orc.quantize_cols(b)
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), os_.view(np.uint32))
+    assert np.array_equal(q.cpu().numpy(), oq)
+    assert np.array_equal(sT.cpu().numpy().view(np.uint32), osc.view(np.uint32))
+    assert np.array_equal(qT.cpu().numpy(), oqc.T)
+    assert torch.equal(q, q1) and torch.equal(s, s1) and torch.equal(qT, qT1) and torch.equal(sT, sT1)
+
+
 @pytest.mark.parametrize("R,C", [(128, 128), (256, 384), (512, 1024)])
 def test_blocks_bit_exact_with_transpose(jf, orc, R, C):
     import torch
