@@ -52,6 +52,10 @@ def lib():
         L.jo_f32_to_bf16.argtypes = [ctypes.c_float]
         L.jo_code_for.restype = ctypes.c_uint8
         L.jo_code_for.argtypes = [ctypes.c_uint16, ctypes.c_uint16]
+        L.jo_requantize_cols.argtypes = [_u8p, _f32p, _i64, _i64, _u8p, _f32p, ctypes.c_int]
+        L.jo_requantize_cols.restype = None
+        L.jo_dequantize_value.argtypes = [ctypes.c_uint8, ctypes.c_float]
+        L.jo_dequantize_value.restype = ctypes.c_float
         for name in ("jo_quantize_rows", "jo_quantize_cols", "jo_quantize_blocks"):
             f = getattr(L, name)
             f.restype = None
@@ -116,6 +120,20 @@ def quantize_cols(x, threads=None):
     s = np.empty((R // 128, C), np.float32)
     lib().jo_quantize_cols(x, R, C, q, s, threads or default_threads())
     return q, s
+
+
+def requantize_cols(q, s, threads=None):
+    """128x1 quantization of the dequantized 1x128 codes of a saved FP8 activation: q uint8 [R, C] with scales
+    s float32 [C/128, R] -> codes uint8 [R, C] (logical layout), scales float32 [R/128, C]."""
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    s = np.ascontiguousarray(s, dtype=np.float32)
+    R, C = q.shape
+    if R % 128 or C % 128 or s.shape != (C // 128, R):
+        raise ValueError("q [R, C] with R, C multiples of 128 and s [C/128, R] expected")
+    qo = np.empty((R, C), np.uint8)
+    so = np.empty((R // 128, C), np.float32)
+    lib().jo_requantize_cols(q, s, R, C, qo, so, threads or default_threads())
+    return qo, so
 
 
 def quantize_blocks(x, threads=None):

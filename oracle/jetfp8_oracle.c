@@ -26,6 +26,8 @@
  *   bf16 widen / narrow ........ pinned: exhaustive widen, RNE ties, comparison with numpy rounding.
  *   quantizers ................. pinned: hand-computed groups (tests/golden), exact-rational brute force,
  *                                invariants (max element -> +-448, 2^k scale equivariance, sign symmetry).
+ *   requantize from FP8 ........ pinned: with power-of-two saved scales x' is a bf16 value and the result
+ *                                equals the bf16 128x1 quantizer's; 2^k scale equivariance; sign symmetry.
  *   GEMM, exact group sums ..... pinned: fp64 brute force, K=128 closed form, lossless special case,
  *                                transpose and dgrad identities.
  *   GEMM, matrix-core group sums (JO_GROUPSUM_MFMA) ..... parity unpinned: this is a model of the FP8
@@ -245,6 +247,44 @@ void jo_quantize_cols(const uint16_t* x, int64_t R, int64_t C, uint8_t* q, float
 void jo_quantize_blocks(const uint16_t* x, int64_t R, int64_t C, uint8_t* q, float* s, int nthreads) {
     jo_qctx c = {x, R, C, q, s};
     jo_parallel(R / 128, nthreads, q_blocks_item, &c);
+}
+
+/* ------------------------------------------------------------------------------------------------
+ * WGrad operand from a saved FP8 activation.  The pages keep the activations saved for the backward pass
+ * in FP8 (Jet-RL explainers, "Schema de Quantification"), while WGrad groups X along the token axis.
+ * Reading: the saved 1x128 codes of X, q[R][C] with scales s[C/128][R] (the JETFP8_ROWS_1x128 layout), are
+ * dequantized to x' = fl32(decode(q) * s) -- one fp32 product, round to nearest even -- and x' is quantized
+ * in 128x1 groups along R exactly as C4 does for a bf16 input: amax exact, s' = fl32(amax / 448), code =
+ * nearest E4M3 value to the exact quotient x' / s'.  code_of's fp64 quotient argument holds for an fp32 x'
+ * as well: against a midpoint of at most 5 significant bits times a 24-bit s', a 24-bit x' is either an exact
+ * midpoint or at a relative distance of about 2^-30 or more, far above the fp64 rounding error.
+ * Outputs in the layout of jo_quantize_cols: codes qo[r][c], scales so[R/128][C].
+ * ---------------------------------------------------------------------------------------------- */
+typedef struct { const uint8_t* q; const float* s; int64_t R, C; uint8_t* qo; float* so; } jo_rqctx;
+
+float jo_dequantize_value(uint8_t code, float scale) {
+    const float d = (float)jo_e4m3_decode(code);      /* exact: at most 4 significant bits */
+    return d * scale;                                  /* one fp32 product */
+}
+
+static void rq_cols_item(void* p, int64_t col) {           /* one column: R/128 groups */
+    jo_rqctx* c = (jo_rqctx*)p;
+    float buf[128];
+    for (int64_t g = 0; g < c->R / 128; ++g) {
+        for (int i = 0; i < 128; ++i) {
+            const int64_t r = g * 128 + i;
+            buf[i] = jo_dequantize_value(c->q[r * c->C + col], c->s[(col / 128) * c->R + r]);
+        }
+        float sg = group_scale(buf, 128, 1);
+        c->so[g * c->C + col] = sg;
+        for (int i = 0; i < 128; ++i) c->qo[(g * 128 + i) * c->C + col] = code_of(buf[i], sg);
+    }
+}
+
+void jo_requantize_cols(const uint8_t* q, const float* s, int64_t R, int64_t C, uint8_t* qo, float* so,
+                        int nthreads) {
+    jo_rqctx c = {q, s, R, C, qo, so};
+    jo_parallel(C, nthreads, rq_cols_item, &c);
 }
 
 /* ------------------------------------------------------------------------------------------------
