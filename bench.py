@@ -40,6 +40,8 @@ def parse():
     p.add_argument("--cpu-sample-rows", type=int, default=128)
     p.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "gemm_traffic.json"),
                    help="per-launch HBM bytes measured by rocprofv3 for this workload (optional)")
+    p.add_argument("--x-from-fp8", action="store_true",
+                   help="WGrad's X from the saved 1x128 FP8 codes (dequantize, requantize 128x1) instead of bf16 X")
     p.add_argument("--separate-quant", action="store_true",
                    help="quantize X and dY with the 1x128 and 128x1 kernels separately (two reads each)")
     p.add_argument("--calibrate-copy", action="store_true",
@@ -110,14 +112,17 @@ class Linear:
         M, N, K = self.M, self.N, self.K
         rows = 2 + 1 + 4 / 128                      # bf16 in, code out, one fp32 scale per 128
         dual = 2 + 2 + 8 / 128                      # bf16 in, both codes out, both scales
+        requant = 1 + 1 + 8 / 128                   # codes in, codes out, both scales
         return {"w_blocks_T": N * K * (2 + 1 + 1 + 4 / 16384), "x_rows": M * K * rows, "dy_rows": M * N * rows,
-                "dy_cols_t": M * N * rows, "x_cols_t": M * K * rows, "x_dual": M * K * dual, "dy_dual": M * N * dual}
+                "dy_cols_t": M * N * rows, "x_cols_t": M * K * rows, "x_dual": M * K * dual, "dy_dual": M * N * dual,
+                "x_requant_t": M * K * requant}
 
 
-def run_step(L, jf, st, ev=None, fused=True):
+def run_step(L, jf, st, ev=None, fused=True, x_from_fp8=False):
     """One pass of the hot path over one linear.  ev: optional list collecting (kind, name, flops_or_bytes,
     start_event, end_event) around each launch.  fused: X and dY are quantized in both groupings by one
-    kernel each (one read); otherwise by the 1x128 and the 128x1 kernels separately."""
+    kernel each (one read); otherwise by the 1x128 and the 128x1 kernels separately.  x_from_fp8: WGrad's X
+    operand is requantized from the saved 1x128 FP8 codes of X instead of from bf16 X."""
     M, N, K = L.M, L.N, L.K
 
     def timed(kind, name, amount, fn):
@@ -134,7 +139,7 @@ def run_step(L, jf, st, ev=None, fused=True):
     qb = L.quant_bytes()
     timed("quant", "w_blocks_T", qb["w_blocks_T"],
           lambda: jf.jetfp8_quantize(L.w, N, K, jf.BLOCKS_128x128, L.wq, L.ws, L.wqT, st))
-    if fused:
+    if fused and not x_from_fp8:
         timed("quant", "x_dual", qb["x_dual"],
               lambda: jf.jetfp8_quantize_dual(L.x, M, K, L.xq, L.xs, L.xqT, L.xsT, st))
     else:
@@ -151,9 +156,21 @@ def run_step(L, jf, st, ev=None, fused=True):
     if not fused:
         timed("quant", "dy_cols_t", qb["dy_cols_t"],
               lambda: jf.jetfp8_quantize(L.dy, M, N, jf.COLS_128x1_T, L.dyqT, L.dysT, None, st))
+    if x_from_fp8:
+        timed("quant", "x_requant_t", qb["x_requant_t"],
+              lambda: jf.jetfp8_requantize_cols_t(L.xq, L.xs, M, K, L.xqT, L.xsT, st))
+    elif not fused:
         timed("quant", "x_cols_t", qb["x_cols_t"],
               lambda: jf.jetfp8_quantize(L.x, M, K, jf.COLS_128x1_T, L.xqT, L.xsT, None, st))
     timed("gemm", "wgrad", 2 * M * N * K, lambda: jf.jetfp8_gemm_wgrad(L.dyqT, L.dysT, L.xqT, L.xsT, L.dw, M, N, K, st))
+
+
+def step_description(args):
+    x = ("X rows quant, fwd" if args.x_from_fp8 or args.separate_quant else "X rows+cols(T) quant in one read, fwd")
+    dy = "dY rows quant, dgrad, dY cols quant (T)" if args.separate_quant else "dY rows+cols(T) quant in one read, dgrad"
+    xt = ", X cols (T) requantized from the saved FP8 X" if args.x_from_fp8 else (
+        ", X cols quant (T)" if args.separate_quant else "")
+    return f"per linear: W block quant(+T), {x}, {dy}{xt}, wgrad"
 
 
 def cpu_baseline(wl, rows, workloads):
@@ -209,7 +226,7 @@ def main():
 
     for _ in range(args.warmup):
         for L in layers:
-            run_step(L, jf, st, fused=not args.separate_quant)
+            run_step(L, jf, st, fused=not args.separate_quant, x_from_fp8=args.x_from_fp8)
     torch.cuda.synchronize()
     print(f"[bench] warmup {args.warmup} done", file=sys.stderr, flush=True)
 
@@ -220,7 +237,7 @@ def main():
     t_start.record()
     for _ in range(args.steps):
         for L in layers:
-            run_step(L, jf, st, ev, fused=not args.separate_quant)
+            run_step(L, jf, st, ev, fused=not args.separate_quant, x_from_fp8=args.x_from_fp8)
     t_end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
@@ -259,10 +276,7 @@ def main():
                 "W~N(0,0.02^2), dY~1e-3*Student-t(3))",
         "config": {"workload": wl.name, "tokens": wl.M,
                    "linears": [{"name": n, "K": K, "N": N} for n, K, N in wl.linears],
-                   "step": ("per linear: W block quant(+T), X rows quant, fwd, dY rows quant, dgrad, "
-                            "dY/X cols quant (T), wgrad") if args.separate_quant else
-                           ("per linear: W block quant(+T), X rows+cols(T) quant in one read, fwd, "
-                            "dY rows+cols(T) quant in one read, dgrad, wgrad")},
+                   "step": step_description(args)},
         "pct_of_fp8_peak": round(100 * value / FP8_PEAK_TFLOPS, 2),
         "gemm_only_tflops": round(achieved, 2),
         "wall_s": round(wall, 4),

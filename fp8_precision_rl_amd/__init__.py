@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_HERE, "lib", "libjetfp8.so")
 
 OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_MODE, ERR_HIP = 0, -1, -2, -3, -4, -5
 ROWS_1x128, COLS_128x1_T, BLOCKS_128x128 = 0, 1, 2
-EXPORTED = ("jetfp8_quantize", "jetfp8_quantize_dual", "jetfp8_gemm_fwd", "jetfp8_gemm_dgrad", "jetfp8_gemm_wgrad",
+EXPORTED = ("jetfp8_quantize", "jetfp8_quantize_dual", "jetfp8_requantize_cols_t", "jetfp8_gemm_fwd", "jetfp8_gemm_dgrad", "jetfp8_gemm_wgrad",
             "jetfp8_status_string", "jetfp8_version")
 
 _lib = None
@@ -45,6 +45,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.jetfp8_quantize.argtypes = [vp, i64, i64, c_int, vp, vp, vp, vp]
     L.jetfp8_quantize_dual.restype = c_int
     L.jetfp8_quantize_dual.argtypes = [vp, i64, i64, vp, vp, vp, vp, vp]
+    L.jetfp8_requantize_cols_t.restype = c_int
+    L.jetfp8_requantize_cols_t.argtypes = [vp, vp, i64, i64, vp, vp, vp]
     for name in ("jetfp8_gemm_fwd", "jetfp8_gemm_dgrad", "jetfp8_gemm_wgrad"):
         f = getattr(L, name)
         f.restype = c_int
@@ -107,6 +109,13 @@ def jetfp8_quantize_dual(src_bf16, rows: int, cols: int, dst_codes, dst_scales, 
     _check("jetfp8_quantize_dual", st)
 
 
+def jetfp8_requantize_cols_t(codes, scales, rows: int, cols: int, dst_codes_t, dst_scales_t, stream=None) -> None:
+    L = load_library()
+    st = L.jetfp8_requantize_cols_t(_ptr(codes), _ptr(scales), int(rows), int(cols), _ptr(dst_codes_t),
+                                    _ptr(dst_scales_t), _stream(stream))
+    _check("jetfp8_requantize_cols_t", st)
+
+
 def jetfp8_gemm_fwd(xq, xs, wq, ws, y_bf16, M: int, N: int, K: int, stream=None) -> None:
     L = load_library()
     _check("jetfp8_gemm_fwd", L.jetfp8_gemm_fwd(_ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws), _ptr(y_bf16),
@@ -162,6 +171,17 @@ def quantize_dual(x, stream=None):
     sT = torch.empty((R // 128, C), dtype=torch.float32, device=x.device)
     jetfp8_quantize_dual(x, R, C, q, s, qT, sT, stream)
     return q, s, qT, sT
+
+
+def requantize_cols_t(q, s, stream=None):
+    """128x1 groups along the rows from saved 1x128 codes: q uint8 [R, C] with scales fp32 [C/128, R] ->
+    codes [C, R], scales [R/128, C] (as quantize_cols_t of the dequantized values)."""
+    import torch
+    R, C = q.shape
+    qT = torch.empty((C, R), dtype=torch.uint8, device=q.device)
+    sT = torch.empty((R // 128, C), dtype=torch.float32, device=q.device)
+    jetfp8_requantize_cols_t(q, s, R, C, qT, sT, stream)
+    return qT, sT
 
 
 def quantize_blocks(w, transposed: bool = True, stream=None):

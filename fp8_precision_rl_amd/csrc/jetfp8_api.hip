@@ -86,6 +86,16 @@ int jetfp8_quantize_dual(const void* src_bf16, int64_t rows, int64_t cols, uint8
                                                 static_cast<hipStream_t>(stream)));
 }
 
+int jetfp8_requantize_cols_t(const uint8_t* codes, const float* scales, int64_t rows, int64_t cols,
+                             uint8_t* dst_codes_t, float* dst_scales_t, void* stream) {
+    if (!codes || !scales || !dst_codes_t || !dst_scales_t) return JETFP8_ERR_NULL;
+    if (!dim_ok(rows) || !dim_ok(cols) || rows % 128 || cols % 128) return JETFP8_ERR_SHAPE;
+    if (!aligned16(codes) || !aligned16(scales) || !aligned16(dst_codes_t) || !aligned16(dst_scales_t))
+        return JETFP8_ERR_ALIGN;
+    return hip_status(jetfp8::launch_quant_requant_cols(codes, scales, rows, cols, dst_codes_t, dst_scales_t,
+                                                        static_cast<hipStream_t>(stream)));
+}
+
 int jetfp8_gemm_fwd(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws, void* y_bf16, int64_t M,
                     int64_t N, int64_t K, void* stream) {
     int rc = check_gemm(xq, xs, wq, ws, y_bf16, M, N, K, false);

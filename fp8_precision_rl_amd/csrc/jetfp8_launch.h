@@ -13,6 +13,8 @@ hipError_t launch_quant_rows(const uint16_t* x, int64_t R, int64_t C, uint8_t* q
 hipError_t launch_quant_cols_t(const uint16_t* x, int64_t R, int64_t C, uint8_t* qT, float* sT, hipStream_t st);
 hipError_t launch_quant_dual(const uint16_t* x, int64_t R, int64_t C, uint8_t* q, float* s, uint8_t* qT, float* sT,
                              hipStream_t st);
+hipError_t launch_quant_requant_cols(const uint8_t* q, const float* s, int64_t R, int64_t C, uint8_t* qT,
+                                     float* sT, hipStream_t st);
 hipError_t launch_quant_blocks(const uint16_t* x, int64_t R, int64_t C, uint8_t* q, float* s, uint8_t* qT,
                                hipStream_t st);
 

@@ -230,6 +230,98 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(const uint16_t* __restr
     }
 }
 
+// 128x1 groups of a saved FP8 activation (the pages keep the activations saved for the backward pass in FP8;
+// WGrad groups X along the token axis): the 1x128 codes q [R][C] with their scales s [C/128][R] are
+// dequantized, x' = fl32(decode(code) * s) with one fp32 product, and x' is quantized in 128x1 groups along R
+// as the bf16 path does (the encode arithmetic and its exactness argument hold for any finite fp32 x').
+// Output: qT [C][R], sT [R/128][C].  Layout of the work as quant_dual_kernel: a 128x128 tile per 256-thread
+// block, an 8x8 sub-tile per lane (8 rows x 8 codes), column maxima across the wave's DPP rows and the
+// block's waves, transposed codes staged in LDS.  2 bytes of traffic per element instead of 3.
+__global__ __launch_bounds__(256) void quant_requant_cols_kernel(const uint8_t* __restrict__ q,
+                                                                 const float* __restrict__ s, int64_t R,
+                                                                 int64_t C, uint8_t* __restrict__ qT,
+                                                                 float* __restrict__ sT, uint32_t col_blocks) {
+    __shared__ uint32_t red[4][16][8];
+    __shared__ uint32_t tcodes[128][33];     // [column][4-row word], odd pitch
+    const int t = threadIdx.x, lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int l16 = lane & 15, rs = lane >> 4, rb8 = 4 * wave + rs;
+    const uint32_t cb = blockIdx.x % col_blocks, rb = blockIdx.x / col_blocks;
+    const int64_t r0 = (int64_t)rb * 128, c0 = (int64_t)cb * 128;
+    const int64_t wr = r0 + 32 * wave;
+    const int Ci = (int)C;
+    const rsrc_q_t rcodes = span_rsrc(q + wr * C + c0, 31 * C + 128);
+    const int lo = 8 * rs * Ci + 8 * l16;
+    u32x2_q cw[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) cw[i] = __builtin_amdgcn_raw_buffer_load_b64(rcodes, lo, i * Ci, 0);
+    // saved scales of the lane's 8 rows (group c0 / 128 of each row): 32 contiguous bytes
+    const float4* sp = reinterpret_cast<const float4*>(s + (c0 / 128) * R + wr + 8 * rs);
+    const float4 sa = sp[0], sb = sp[1];
+    const float sr[8] = {sa.x, sa.y, sa.z, sa.w, sb.x, sb.y, sb.z, sb.w};
+
+    // dequantize: element (i, j) is byte j of the lane's row i
+    float xv[8][8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int w = 0; w < 2; ++w) {
+            const auto lo2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)cw[i][w], false);   // bytes 0, 1 of the word
+            const auto hi2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)cw[i][w], true);    // bytes 2, 3
+            xv[i][4 * w] = lo2[0] * sr[i];
+            xv[i][4 * w + 1] = lo2[1] * sr[i];
+            xv[i][4 * w + 2] = hi2[0] * sr[i];
+            xv[i][4 * w + 3] = hi2[1] * sr[i];
+        }
+
+    // column maxima of the magnitude bits (fp32 patterns order like the magnitudes): this lane's 8 rows,
+    // then the wave's 4 DPP rows, then the block's 4 waves
+    uint32_t cm[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        uint32_t m = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) m = max(m, __float_as_uint(xv[i][j]) & 0x7FFFFFFFu);
+        m = max(m, (uint32_t)__shfl_xor((int)m, 16, 64));
+        m = max(m, (uint32_t)__shfl_xor((int)m, 32, 64));
+        cm[j] = m;
+    }
+    if (rs == 0) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) red[wave][l16][j] = cm[j];
+    }
+    __syncthreads();
+    float col_scale_a = 0.0f, col_scale_b = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const uint32_t m = max(max(red[0][l16][j], red[1][l16][j]), max(red[2][l16][j], red[3][l16][j]));
+        float f[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) f[i] = xv[i][j];
+        const GroupScale gs = make_group_scale(__uint_as_float(m));
+        const uint2 out = encode8(f, gs);
+        tcodes[8 * l16 + j][2 * rb8] = out.x;
+        tcodes[8 * l16 + j][2 * rb8 + 1] = out.y;
+        if (j == rs) col_scale_a = gs.s;
+        if (j == rs + 4) col_scale_b = gs.s;
+    }
+    if (wave == 0) {
+        float* st = sT + (int64_t)rb * C + c0;
+        st[8 * l16 + rs] = col_scale_a;
+        st[8 * l16 + rs + 4] = col_scale_b;
+    }
+    __syncthreads();
+    const rsrc_q_t rqt = span_rsrc(qT + c0 * R + r0, 127 * R + 128);
+    const int oc = t >> 1, hf = t & 1;
+    const int to = oc * (int)R + 64 * hf;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const uint32_t* src = &tcodes[oc][16 * hf + 4 * k];
+        const u32x4_q o = {src[0], src[1], src[2], src[3]};
+        __builtin_amdgcn_raw_buffer_store_b128(o, rqt, to + 16 * k, 0, 0);
+    }
+}
+
 // One block owns one 128x128 block: 8 rows x 8 columns per thread, a block-wide amax, codes written in
 // place and, through an LDS transpose, to the transposed copy.
 __global__ __launch_bounds__(256) void quant_blocks_kernel(const uint16_t* __restrict__ x, int64_t R, int64_t C,
@@ -309,6 +401,17 @@ hipError_t launch_quant_dual(const uint16_t* x, int64_t R, int64_t C, uint8_t* q
     if (64 * C + 256 >= ((int64_t)1 << 31) || 128 * R + 128 >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
     hipLaunchKernelGGL(quant_dual_kernel, dim3((unsigned)(col_blocks * row_blocks)), dim3(256), 0, st, x, R, C, q, s,
                        qT, sT, (uint32_t)col_blocks);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_requant_cols(const uint8_t* q, const float* s, int64_t R, int64_t C, uint8_t* qT,
+                                     float* sT, hipStream_t st) {
+    // R and C are multiples of 128; buffer spans and offsets in 31 bits (32 code rows, 128 transposed rows)
+    const int64_t col_blocks = C / 128, row_blocks = R / 128;
+    if (col_blocks * row_blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    if (32 * C + 128 >= ((int64_t)1 << 31) || 128 * R + 128 >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(quant_requant_cols_kernel, dim3((unsigned)(col_blocks * row_blocks)), dim3(256), 0, st, q, s,
+                       R, C, qT, sT, (uint32_t)col_blocks);
     return hipGetLastError();
 }
 

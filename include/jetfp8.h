@@ -86,6 +86,17 @@ int jetfp8_quantize(const void* src_bf16, int64_t rows, int64_t cols, int mode,
 int jetfp8_quantize_dual(const void* src_bf16, int64_t rows, int64_t cols, uint8_t* dst_codes,
                          float* dst_scales, uint8_t* dst_codes_t, float* dst_scales_t, void* stream);
 
+/* WGrad operand from a saved FP8 activation.  The pages keep the activations saved for the backward pass in
+ * FP8 (Jet-RL explainers, "Schema de Quantification"); WGrad needs X grouped along the token axis.  This
+ * takes the 1x128 codes of X and their scales (the JETFP8_ROWS_1x128 outputs), dequantizes each element as
+ * one fp32 product decode(code) * scale, and quantizes those values in 128x1 groups along the rows with the
+ * same scale and rounding rules as JETFP8_COLS_128x1_T, codes written transposed.  Reads 1 byte per element
+ * instead of the 2 of the bf16 matrix.  Finite codes only (0x7F / 0xFF are E4M3 NaN).
+ * codes [rows][cols], scales [cols/128][rows] -> dst_codes_t [cols][rows], dst_scales_t [rows/128][cols].
+ * rows % 128 == 0 and cols % 128 == 0. */
+int jetfp8_requantize_cols_t(const uint8_t* codes, const float* scales, int64_t rows, int64_t cols,
+                             uint8_t* dst_codes_t, float* dst_scales_t, void* stream);
+
 /* Forward FP8 linear (rollout decode, prefill, training forward):
  *   Y[m][n] = sum_g xs[g][m] * ws[n/128][g] * sum_{k in g} xq[m][k] * wq[n][k]
  * xq [M][K], xs [K/128][M] (JETFP8_ROWS_1x128 of X); wq [N][K], ws [N/128][K/128]

@@ -28,7 +28,7 @@ def _declared():
 
 def test_header_declares_the_four_calls_and_helpers():
     names = _declared()
-    for n in ("jetfp8_quantize", "jetfp8_quantize_dual", "jetfp8_gemm_fwd", "jetfp8_gemm_dgrad", "jetfp8_gemm_wgrad",
+    for n in ("jetfp8_quantize", "jetfp8_quantize_dual", "jetfp8_requantize_cols_t", "jetfp8_gemm_fwd", "jetfp8_gemm_dgrad", "jetfp8_gemm_wgrad",
               "jetfp8_status_string", "jetfp8_version"):
         assert n in names
 
@@ -78,6 +78,24 @@ def test_quantize_dual_validation(lib):
     assert qd(lib, scales=BAD) == -3
     assert qd(lib, codes_t=BAD) == -3
     assert qd(lib, scales_t=BAD) == -3
+
+
+def rq(lib, codes=P, scales=P, rows=256, cols=256, codes_t=P, scales_t=P):
+    return lib.jetfp8_requantize_cols_t(codes, scales, rows, cols, codes_t, scales_t, None)
+
+
+def test_requantize_validation(lib):
+    assert rq(lib, codes=None) == -1
+    assert rq(lib, scales=None) == -1
+    assert rq(lib, codes_t=None) == -1
+    assert rq(lib, scales_t=None) == -1
+    assert rq(lib, rows=200) == -2
+    assert rq(lib, cols=64) == -2
+    assert rq(lib, rows=-128) == -2
+    assert rq(lib, codes=BAD) == -3
+    assert rq(lib, scales=BAD) == -3
+    assert rq(lib, codes_t=BAD) == -3
+    assert rq(lib, scales_t=BAD) == -3
 
 
 def test_quantize_validation(lib):

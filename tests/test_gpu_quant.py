@@ -88,6 +88,32 @@ def test_dual_bit_exact(jf, orc, R, C):
     assert torch.equal(q, q1) and torch.equal(s, s1) and torch.equal(qT, qT1) and torch.equal(sT, sT1)
 
 
+@pytest.mark.parametrize("R,C", [(128, 128), (256, 384), (640, 256)])
+def test_requantize_cols_bit_exact(jf, orc, R, C):
+    """Saved 1x128 codes -> 128x1 codes along the rows: equal to the oracle bit for bit, on codes of LLM-like
+    data (from the GPU's own 1x128 quantizer, which is bit-exact) and on arbitrary finite codes with
+    arbitrary scales, including tiny scales and all-zero columns."""
+    import torch
+    b = _special_columns(_special_matrix(R, C, 5 * R + C), 3 * R + C)
+    q, s = jf.quantize_rows(bits_to_dev(b))
+    qT, sT = jf.requantize_cols_t(q, s)
+    torch.cuda.synchronize()
+    oq, os_ = orc.requantize_cols(q.cpu().numpy(), s.cpu().numpy())
+    assert np.array_equal(sT.cpu().numpy().view(np.uint32), os_.view(np.uint32))
+    assert np.array_equal(qT.cpu().numpy(), oq.T)
+    rng = np.random.default_rng(R + C)
+    codes = rng.integers(0, 0x7F, (R, C), dtype=np.uint8) | (rng.integers(0, 2, (R, C), dtype=np.uint8) << 7)
+    codes[:, 3] = 0                                                   # all-zero columns
+    scales = (rng.random((C // 128, R)) * 10.0 ** rng.integers(-30, 3, (C // 128, R))).astype(np.float32)
+    scales[0, :128] = np.float32(1e-41)                              # subnormal saved scales: tiny groups
+    qd, sd = torch.from_numpy(codes).cuda(), torch.from_numpy(scales).cuda()
+    qT, sT = jf.requantize_cols_t(qd, sd)
+    torch.cuda.synchronize()
+    oq, os_ = orc.requantize_cols(codes, scales)
+    assert np.array_equal(sT.cpu().numpy().view(np.uint32), os_.view(np.uint32))
+    assert np.array_equal(qT.cpu().numpy(), oq.T)
+
+
 @pytest.mark.parametrize("R,C", [(128, 128), (256, 384), (512, 1024)])
 def test_blocks_bit_exact_with_transpose(jf, orc, R, C):
     import torch
