@@ -274,29 +274,62 @@ __global__ __launch_bounds__(L_THREADS, 1) void gemm_large_kernel(
 #pragma unroll
             for (int tn = 0; tn < 4; ++tn) asm volatile("" : "+v"(acc[tm][tn]));
         };
-        // software pipeline over the 8 row tiles: the matrix ops of tile tm+1 run while tile tm is promoted
-        v4f pa[4], pb[4];
-        v8i af = a_frag(0);
+        // software pipeline over the 8 row tiles: the matrix ops of tile tm+1 run while tile tm is promoted.
+        // Block-scaled B: one product buffer -- tile (tm-1, tn) is promoted right before (tm, tn) is issued
+        // into the same registers (the other wave of the SIMD keeps the matrix unit busy meanwhile).
+        // Row-scaled B: two buffers, a whole row of tiles issued before the previous row is promoted.
+        if (!ROW_SCALED_B) {
+            v4f pp[4];
+            v8i af = a_frag(0);
 #pragma unroll
-        for (int tn = 0; tn < 4; ++tn) pa[tn] = mfma_group(bfr[tn], af);
+            for (int tn = 0; tn < 4; ++tn) pp[tn] = mfma_group(bfr[tn], af);
 #pragma unroll
-        for (int tm = 1; tm < 8; ++tm) {
-            af = a_frag(tm);
-            if (tm <= 4 && refill_next) issue_part(tm - 1, iss, ig, refill);
-            __builtin_amdgcn_sched_barrier(0);
-            if (tm & 1) {
+            for (int tm = 1; tm < 8; ++tm) {
+                af = a_frag(tm);
+                if (tm <= 4 && refill_next) issue_part(tm - 1, iss, ig, refill);
+                __builtin_amdgcn_sched_barrier(0);
+                if (flush) store_row(tm - 1, prev_i0, prev_j0);
 #pragma unroll
-                for (int tn = 0; tn < 4; ++tn) pb[tn] = mfma_group(bfr[tn], af);
-                promote(tm - 1, pa);
-            } else {
+                for (int tn = 0; tn < 4; ++tn) {
 #pragma unroll
-                for (int tn = 0; tn < 4; ++tn) pa[tn] = mfma_group(bfr[tn], af);
-                promote(tm - 1, pb);
+                    for (int v = 0; v < 4; ++v) acc[tm - 1][tn][v] = fmaf(pp[tn][v], s1[tm - 1], acc[tm - 1][tn][v]);
+                    asm volatile("" : "+v"(acc[tm - 1][tn]));
+                    pp[tn] = mfma_group(bfr[tn], af);
+                }
             }
+            __builtin_amdgcn_sched_barrier(0);
+            if (flush) store_row(7, prev_i0, prev_j0);
+#pragma unroll
+            for (int tn = 0; tn < 4; ++tn) {
+#pragma unroll
+                for (int v = 0; v < 4; ++v) acc[7][tn][v] = fmaf(pp[tn][v], s1[7], acc[7][tn][v]);
+                asm volatile("" : "+v"(acc[7][tn]));
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        } else {
+            v4f pa[4], pb[4];
+            v8i af = a_frag(0);
+#pragma unroll
+            for (int tn = 0; tn < 4; ++tn) pa[tn] = mfma_group(bfr[tn], af);
+#pragma unroll
+            for (int tm = 1; tm < 8; ++tm) {
+                af = a_frag(tm);
+                if (tm <= 4 && refill_next) issue_part(tm - 1, iss, ig, refill);
+                __builtin_amdgcn_sched_barrier(0);
+                if (tm & 1) {
+#pragma unroll
+                    for (int tn = 0; tn < 4; ++tn) pb[tn] = mfma_group(bfr[tn], af);
+                    promote(tm - 1, pa);
+                } else {
+#pragma unroll
+                    for (int tn = 0; tn < 4; ++tn) pa[tn] = mfma_group(bfr[tn], af);
+                    promote(tm - 1, pb);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            promote(7, pb);
+            __builtin_amdgcn_sched_barrier(0);
         }
-        __builtin_amdgcn_sched_barrier(0);
-        promote(7, pb);
-        __builtin_amdgcn_sched_barrier(0);
         if (refill_next) advance_issue();
         // advance the compute cursor
         if (++cg == G) {
