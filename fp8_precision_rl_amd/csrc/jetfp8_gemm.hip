@@ -209,6 +209,7 @@ __global__ __launch_bounds__(L_THREADS, 1) void gemm_large_kernel(
         __builtin_amdgcn_sched_barrier(0);   // keep each group's code in place (bounded register pressure)
         // this wave's loads of this group landed, its LDS reads of the previous one returned and its
         // stores of the previous tile completed; then every wave of the block is past that point
+        __builtin_amdgcn_s_setprio(0);
         __builtin_amdgcn_s_waitcnt(0);
         __builtin_amdgcn_s_barrier();
         const bool refill_next = s + 1 < nsteps;   // the next step's group goes into the other stage
@@ -288,6 +289,12 @@ __global__ __launch_bounds__(L_THREADS, 1) void gemm_large_kernel(
                 af = a_frag(tm);
                 if (tm <= 4 && refill_next) issue_part(tm - 1, iss, ig, refill);
                 __builtin_amdgcn_sched_barrier(0);
+                // Each SIMD runs one wave of each half (wm = 0, 1).  Issue arbitration favours the older wave
+                // (wm = 0), which then reaches the step's barrier well before its partner and leaves the matrix
+                // unit to a single wave; raising the younger wave's priority for the first half of the step
+                // evens out their progress.
+                if (wm == 1 && tm < 4) __builtin_amdgcn_s_setprio(1);
+                else __builtin_amdgcn_s_setprio(0);
                 if (flush) store_row(tm - 1, prev_i0, prev_j0);
 #pragma unroll
                 for (int tn = 0; tn < 4; ++tn) {
@@ -316,6 +323,8 @@ __global__ __launch_bounds__(L_THREADS, 1) void gemm_large_kernel(
                 af = a_frag(tm);
                 if (tm <= 4 && refill_next) issue_part(tm - 1, iss, ig, refill);
                 __builtin_amdgcn_sched_barrier(0);
+                if (wm == 1 && tm < 4) __builtin_amdgcn_s_setprio(1);
+                else __builtin_amdgcn_s_setprio(0);
                 if (tm & 1) {
 #pragma unroll
                     for (int tn = 0; tn < 4; ++tn) pb[tn] = mfma_group(bfr[tn], af);
