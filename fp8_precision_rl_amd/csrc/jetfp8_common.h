@@ -51,19 +51,20 @@ __device__ __forceinline__ float row16_max(float a) {
     return a;
 }
 
-// Lane-wise magnitude maximum of two pairs of bf16 values (bit patterns packed two to a word).  For finite
-// values the order of the 15 magnitude bits is the order of the magnitudes, so the maximum is taken on
-// 16-bit integers, two per instruction.
+// Magnitudes of two bf16 values packed in a word (sign bits cleared), and the lane-wise maximum of two such
+// words.  For finite values the order of the 15 magnitude bits is the order of the magnitudes, so maxima are
+// taken on 16-bit integers, two per instruction.
 typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ uint32_t max_mag2(uint32_t a, uint32_t b) {
-    const u16x2_t m = __builtin_elementwise_max(__builtin_bit_cast(u16x2_t, a & 0x7FFF7FFFu),
-                                                __builtin_bit_cast(u16x2_t, b & 0x7FFF7FFFu));
-    return __builtin_bit_cast(uint32_t, m);
+__device__ __forceinline__ uint32_t mag2(uint32_t w) { return w & 0x7FFF7FFFu; }
+__device__ __forceinline__ uint32_t pkmax16(uint32_t a, uint32_t b) {
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2_t, a),
+                                                                  __builtin_bit_cast(u16x2_t, b)));
 }
+__device__ __forceinline__ uint32_t max_mag2(uint32_t a, uint32_t b) { return pkmax16(mag2(a), mag2(b)); }
 
 // Largest magnitude among the eight bf16 values of v, as a bf16 bit pattern.
 __device__ __forceinline__ uint32_t amax8_bits(const uint4& v) {
-    const uint32_t m = max_mag2(max_mag2(v.x, v.y), max_mag2(v.z, v.w));
+    const uint32_t m = pkmax16(max_mag2(v.x, v.y), max_mag2(v.z, v.w));
     return max(m & 0xFFFFu, m >> 16);
 }
 
@@ -119,9 +120,11 @@ __device__ __forceinline__ uint32_t cvt2_e4m3(float a, float b, uint32_t old) {
 // A screened element (about 0.5 % of LLM-like bf16 data, where x and amax share 8-bit significands) takes
 // resolve_at_midpoint in a branch of its own, so a wave pays for the element positions its lanes flagged.
 __device__ __forceinline__ uint2 pack8(const float q[8]) {
+    // the low-half conversions write into the register of their second operand (its old bits are replaced
+    // by the high-half conversion), so no register has to be cleared first
     uint2 out;
-    out.x = cvt2_e4m3<true>(q[2], q[3], cvt2_e4m3<false>(q[0], q[1], 0u));
-    out.y = cvt2_e4m3<true>(q[6], q[7], cvt2_e4m3<false>(q[4], q[5], 0u));
+    out.x = cvt2_e4m3<true>(q[2], q[3], cvt2_e4m3<false>(q[0], q[1], __float_as_uint(q[1])));
+    out.y = cvt2_e4m3<true>(q[6], q[7], cvt2_e4m3<false>(q[4], q[5], __float_as_uint(q[5])));
     return out;
 }
 

@@ -97,8 +97,8 @@ __global__ __launch_bounds__(256) void quant_cols_t_kernel(const uint16_t* __res
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
         auto word = [&](int i) { return w == 0 ? v[i].x : w == 1 ? v[i].y : w == 2 ? v[i].z : v[i].w; };
-        cm[w] = max_mag2(max_mag2(max_mag2(word(0), word(1)), max_mag2(word(2), word(3))),
-                         max_mag2(max_mag2(word(4), word(5)), max_mag2(word(6), word(7))));
+        cm[w] = pkmax16(pkmax16(max_mag2(word(0), word(1)), max_mag2(word(2), word(3))),
+                        pkmax16(max_mag2(word(4), word(5)), max_mag2(word(6), word(7))));
     }
     float my_scale = 0.0f;
 #pragma unroll
@@ -158,16 +158,23 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(const uint16_t* __restr
         v[i] = make_uint4(w[0], w[1], w[2], w[3]);
     }
 
-    // column maxima (two columns per word): this lane's 8 rows, then the wave's 4 DPP rows
-    uint32_t cm[4];
+    // magnitude maxima from the sign-cleared words: per row of the sub-tile (8 values) and per column (two
+    // columns per word, over the 8 rows); the column maxima then over the wave's 4 DPP rows
+    uint32_t cm[4] = {0u, 0u, 0u, 0u}, rmax[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint32_t m0 = mag2(v[i].x), m1 = mag2(v[i].y), m2 = mag2(v[i].z), m3 = mag2(v[i].w);
+        cm[0] = pkmax16(cm[0], m0);
+        cm[1] = pkmax16(cm[1], m1);
+        cm[2] = pkmax16(cm[2], m2);
+        cm[3] = pkmax16(cm[3], m3);
+        const uint32_t r = pkmax16(pkmax16(m0, m1), pkmax16(m2, m3));
+        rmax[i] = max(r & 0xFFFFu, r >> 16);
+    }
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-        auto word = [&](int i) { return w == 0 ? v[i].x : w == 1 ? v[i].y : w == 2 ? v[i].z : v[i].w; };
-        uint32_t m = max_mag2(max_mag2(max_mag2(word(0), word(1)), max_mag2(word(2), word(3))),
-                              max_mag2(max_mag2(word(4), word(5)), max_mag2(word(6), word(7))));
-        m = max_mag2(m, (uint32_t)__shfl_xor((int)m, 16, 64));
-        m = max_mag2(m, (uint32_t)__shfl_xor((int)m, 32, 64));
-        cm[w] = m;
+        cm[w] = pkmax16(cm[w], (uint32_t)__shfl_xor((int)cm[w], 16, 64));
+        cm[w] = pkmax16(cm[w], (uint32_t)__shfl_xor((int)cm[w], 32, 64));
     }
     if (rs == 0) {
 #pragma unroll
@@ -180,7 +187,7 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(const uint16_t* __restr
     for (int i = 0; i < 8; ++i) {
         float f[8];
         unpack8(v[i], f);
-        const GroupScale gs = make_group_scale(bf16_to_f32(row16_max_u32(amax8_bits(v[i]))));
+        const GroupScale gs = make_group_scale(bf16_to_f32(row16_max_u32(rmax[i])));
         const uint2 out = encode8(f, gs);
         const u32x2_q o = {out.x, out.y};
         __builtin_amdgcn_raw_buffer_store_b64(o, rq, lo, i * Ci, 0);
@@ -192,7 +199,7 @@ __global__ __launch_bounds__(256) void quant_dual_kernel(const uint16_t* __restr
     __syncthreads();
 #pragma unroll
     for (int w = 0; w < 4; ++w)
-        cm[w] = max_mag2(max_mag2(red[0][l16][w], red[1][l16][w]), max_mag2(red[2][l16][w], red[3][l16][w]));
+        cm[w] = pkmax16(pkmax16(red[0][l16][w], red[1][l16][w]), pkmax16(red[2][l16][w], red[3][l16][w]));
     auto elem = [&](int i, int j) -> float {
         const uint32_t w = (j >> 1) == 0 ? v[i].x : (j >> 1) == 1 ? v[i].y : (j >> 1) == 2 ? v[i].z : v[i].w;
         return bf16_to_f32((j & 1) ? (w >> 16) : (w & 0xFFFFu));
