@@ -145,6 +145,26 @@ def _backward_checks(jf, orc, d, wqT, ws, rng, tag):
     _quant_cols_check(orc, dy, dyqT, dysT, mgroups, f"{tag} dY")
     _quant_cols_check(orc, x, xqT, xsT, mgroups, f"{tag} X")
 
+    # the fused one-read quantizer: every output equal to the two single-grouping kernels' (full size)
+    for t, q1, s1, qT1, sT1, what in ((dy, dyq, dys, dyqT, dysT, "dY"), (x, None, None, xqT, xsT, "X")):
+        q2, s2, qT2, sT2 = jf.quantize_dual(t)
+        if q1 is None:
+            q1, s1 = jf.quantize_rows(t)
+        torch.cuda.synchronize()
+        assert torch.equal(q2, q1) and torch.equal(s2, s1), f"{tag} {what}: fused 1x128 outputs"
+        assert torch.equal(qT2, qT1) and torch.equal(sT2, sT1), f"{tag} {what}: fused 128x1 outputs"
+        del q2, s2, qT2, sT2
+    # WGrad's X from the saved 1x128 codes of X: sampled 128-row groups against the oracle
+    xq, xs = jf.quantize_rows(x)
+    rqT, rsT = jf.requantize_cols_t(xq, xs)
+    torch.cuda.synchronize()
+    for g in mgroups:
+        sl = slice(g * 128, (g + 1) * 128)
+        oq, os_ = orc.requantize_cols(xq[sl].cpu().numpy(), xs[:, sl].contiguous().cpu().numpy())
+        assert np.array_equal(rqT[:, sl].cpu().numpy(), oq.T), f"{tag} X requantized codes, group {g}"
+        assert np.array_equal(rsT[g:g + 1].cpu().numpy(), os_), f"{tag} X requantized scales, group {g}"
+    del xq, xs, rqT, rsT
+
     # DGrad: rows of dX x one 128-column slab of K; W's 128x128 blocks over that slab
     odq, ods = orc.quantize_rows(dev_to_bits(_take(dy, rows)))
     for b in _slabs(K, rng):
