@@ -377,7 +377,7 @@ static int device_cu_count() {
     return cache[dev];
 }
 
-// ---- small-M kernel (rollout decode: I <= 16 * RT rows) -----------------------------------------------
+// ---- small-M kernel (rollout decode batches: I <= 16 * RT rows, RT = 1, 2, 4) --------------------------
 // The large tiles would leave most of the machine idle and stream each weight row through LDS for a handful
 // of output rows, so the decode shape gets its own schedule with the same per-element operation sequence:
 //   - the output is cut into slices of 16 columns (16 rows of B) by all I rows; persistent 512-thread blocks
@@ -389,9 +389,9 @@ static int device_cu_count() {
 //   - after a barrier every wave runs the promotion acc = fma(p, fl32(sa * sb), acc) for its share of the
 //     outputs over the chunk's groups in ascending order -- the same chain the large kernel runs, so every
 //     output row is bitwise the same whichever kernel computed it;
-//   - operand fragments go straight from global memory into registers, D_AHEAD chunks ahead (range-checked
-//     buffer loads: rows past I and groups past the contraction read as zero and are never promoted); the
-//     A-row scales of all groups sit in LDS for the block's lifetime.
+//   - operand fragments go straight from global memory into registers, D_AHEAD chunks ahead (2 for RT = 4, to
+//     fit the registers; range-checked buffer loads: rows past I and groups past the contraction read as zero
+//     and are never promoted); the A-row scales of all groups sit in LDS for the block's lifetime.
 constexpr int D_WAVES = 8, D_THREADS = 64 * D_WAVES, D_AHEAD = 3;
 constexpr int D_SA_MAX = 8192;     // A-row scales kept in LDS: (contraction / 128) * rows <= 8192
 
@@ -402,6 +402,7 @@ __global__ __launch_bounds__(D_THREADS) void gemm_decode_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ As, const uint8_t* __restrict__ B,
     const float* __restrict__ Bs, uint16_t* __restrict__ Cout, int64_t I, int64_t J, int64_t Kc, int64_t sbj,
     int64_t sbg) {
+    constexpr int AHEAD = RT >= 4 ? 2 : D_AHEAD;             // chunks in flight (register budget)
     constexpr int PAIRS = RT * 4;                             // (row tile, lane component) pairs of outputs
     constexpr int EPW = (PAIRS + D_WAVES - 1) / D_WAVES;      // pairs per wave in the promotion chain
     __shared__ v4f pbuf[2][D_WAVES][RT][64];
@@ -428,7 +429,7 @@ __global__ __launch_bounds__(D_THREADS) void gemm_decode_kernel(
 #pragma unroll
     for (int e = 0; e < EPW; ++e) acc[e] = 0.0f;
 
-    u32x4 wf[D_AHEAD][2], af[D_AHEAD][RT][2];
+    u32x4 wf[AHEAD][2], af[AHEAD][RT][2];
     // stream position c -> slice c / nchunks (B rows of that slice only: 16 x Kc bytes), group chunk
     // c % nchunks.  Positions past the block's stream load unconditionally (a conditional load would make
     // the compiler wait for it where the paths join) through an empty descriptor: they read zeros.
@@ -469,7 +470,7 @@ __global__ __launch_bounds__(D_THREADS) void gemm_decode_kernel(
     // first operand loads are issued, so waiting for it does not wait for them
     for (int i = t; i < G * Ii; i += D_THREADS) sa_tab[i] = As[i];
 #pragma unroll
-    for (int k = 0; k < D_AHEAD; ++k) load_chunk(k, wf[k], af[k]);
+    for (int k = 0; k < AHEAD; ++k) load_chunk(k, wf[k], af[k]);
     float sb_cur[D_WAVES];
     load_sb(0, sb_cur);
     // LDS writes done, then every wave is here (a plain barrier: the operand loads stay in flight)
@@ -488,7 +489,7 @@ __global__ __launch_bounds__(D_THREADS) void gemm_decode_kernel(
                                     (int)a[rt][1][0], (int)a[rt][1][1], (int)a[rt][1][2], (int)a[rt][1][3]};
             p[rt] = mfma_group(bfrag, afrag);
         }
-        load_chunk(c + D_AHEAD, w, a);
+        load_chunk(c + AHEAD, w, a);
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) pbuf[c & 1][wave][rt][lane] = p[rt];
         // this wave's products (and its chain reads of two chunks ago) are in LDS, then every wave is here;
@@ -517,12 +518,12 @@ __global__ __launch_bounds__(D_THREADS) void gemm_decode_kernel(
         for (int gi = 0; gi < D_WAVES; ++gi) sb_cur[gi] = sb_nxt[gi];
     };
     int c = 0;
-    for (; c + D_AHEAD <= nstream; c += D_AHEAD) {
+    for (; c + AHEAD <= nstream; c += AHEAD) {
 #pragma unroll
-        for (int k = 0; k < D_AHEAD; ++k) chunk(c + k, wf[k], af[k]);
+        for (int k = 0; k < AHEAD; ++k) chunk(c + k, wf[k], af[k]);
     }
 #pragma unroll
-    for (int k = 0; k < D_AHEAD; ++k)
+    for (int k = 0; k < AHEAD; ++k)
         if (c + k < nstream) chunk(c + k, wf[k], af[k]);
 }
 
@@ -551,9 +552,10 @@ hipError_t launch_gemm_block_scaled_b(const uint8_t* A, const float* As, const u
                                       uint16_t* C, int64_t I, int64_t J, int64_t Kc, int64_t sbj, int64_t sbg,
                                       hipStream_t st) {
     // decode sizes: the small-M schedule (same per-element sequence, so the same bits)
-    if (I <= 32 && (Kc / BK) * I <= D_SA_MAX) {
+    if (I <= 64 && (Kc / BK) * I <= D_SA_MAX) {
         if (I <= 16) return launch_decode<1>(A, As, B, Bs, C, I, J, Kc, sbj, sbg, st);
-        return launch_decode<2>(A, As, B, Bs, C, I, J, Kc, sbj, sbg, st);
+        if (I <= 32) return launch_decode<2>(A, As, B, Bs, C, I, J, Kc, sbj, sbg, st);
+        return launch_decode<4>(A, As, B, Bs, C, I, J, Kc, sbj, sbg, st);
     }
     return launch_large<false>(A, As, B, Bs, C, I, J, Kc, sbj, sbg, st);
 }

@@ -106,18 +106,20 @@ def test_wgrad_parity(jf, orc, M, N, K):
 
 
 def test_rows_are_bitwise_independent_of_M(jf):
-    """Decode (M=1), a small batch (M=32) and a training batch produce bitwise identical rows."""
+    """Decode (M=1), decode batches (M=20, 32, 48, 64: the small-M kernel with 1, 2 and 4 row tiles) and a
+    training batch (the large-tile kernel) produce bitwise identical rows."""
     import torch
     M, N, K = 300, 256, 512
     xb, wb = _x(M, K, 41), _w(N, K, 42)
     wq, ws, _ = jf.quantize_blocks(bits_to_dev(wb))
     x = bits_to_dev(xb)
     y_all, _ = jf.linear_forward(x, wq, ws)
-    y32, _ = jf.linear_forward(x[100:132].contiguous(), wq, ws)
+    batches = {m: jf.linear_forward(x[100:100 + m].contiguous(), wq, ws)[0] for m in (20, 32, 48, 64)}
     ones = [jf.linear_forward(x[r:r + 1].contiguous(), wq, ws)[0] for r in (0, 131, 299)]
     torch.cuda.synchronize()
     full = dev_to_bits(y_all)
-    assert np.array_equal(dev_to_bits(y32), full[100:132])
+    for m, yb in batches.items():
+        assert np.array_equal(dev_to_bits(yb), full[100:100 + m]), f"M={m}"
     for r, y1 in zip((0, 131, 299), ones):
         assert np.array_equal(dev_to_bits(y1)[0], full[r])
 
