@@ -18,9 +18,10 @@ from typing import Optional, Tuple
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "lib", "libjetfp8.so")
 
-OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_MODE, ERR_HIP = 0, -1, -2, -3, -4, -5
+OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_MODE, ERR_HIP, ERR_VALUE = 0, -1, -2, -3, -4, -5, -6
 ROWS_1x128, COLS_128x1_T, BLOCKS_128x128 = 0, 1, 2
-EXPORTED = ("jetfp8_quantize", "jetfp8_quantize_dual", "jetfp8_requantize_cols_t", "jetfp8_gemm_fwd", "jetfp8_gemm_dgrad", "jetfp8_gemm_wgrad",
+EXPORTED = ("jetfp8_quantize", "jetfp8_quantize_dual", "jetfp8_requantize_cols_t", "jetfp8_rmsnorm_quantize",
+            "jetfp8_swiglu_quantize", "jetfp8_gemm_fwd", "jetfp8_gemm_dgrad", "jetfp8_gemm_wgrad",
             "jetfp8_status_string", "jetfp8_version")
 
 _lib = None
@@ -47,6 +48,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.jetfp8_quantize_dual.argtypes = [vp, i64, i64, vp, vp, vp, vp, vp]
     L.jetfp8_requantize_cols_t.restype = c_int
     L.jetfp8_requantize_cols_t.argtypes = [vp, vp, i64, i64, vp, vp, vp]
+    L.jetfp8_rmsnorm_quantize.restype = c_int
+    L.jetfp8_rmsnorm_quantize.argtypes = [vp, vp, i64, i64, ctypes.c_float, vp, vp, vp, vp, vp]
+    L.jetfp8_swiglu_quantize.restype = c_int
+    L.jetfp8_swiglu_quantize.argtypes = [vp, i64, i64, vp, vp, vp, vp]
     for name in ("jetfp8_gemm_fwd", "jetfp8_gemm_dgrad", "jetfp8_gemm_wgrad"):
         f = getattr(L, name)
         f.restype = c_int
@@ -116,6 +121,23 @@ def jetfp8_requantize_cols_t(codes, scales, rows: int, cols: int, dst_codes_t, d
     _check("jetfp8_requantize_cols_t", st)
 
 
+def jetfp8_rmsnorm_quantize(x_bf16, weight_bf16, rows: int, cols: int, eps: float, dst_codes, dst_scales,
+                            dst_rstd=None, dst_y_bf16=None, stream=None) -> None:
+    L = load_library()
+    st = L.jetfp8_rmsnorm_quantize(_ptr(x_bf16), _ptr(weight_bf16), int(rows), int(cols), float(eps),
+                                   _ptr(dst_codes), _ptr(dst_scales), _ptr(dst_rstd), _ptr(dst_y_bf16),
+                                   _stream(stream))
+    _check("jetfp8_rmsnorm_quantize", st)
+
+
+def jetfp8_swiglu_quantize(gate_up_bf16, rows: int, cols: int, dst_codes, dst_scales, dst_h_bf16=None,
+                           stream=None) -> None:
+    L = load_library()
+    st = L.jetfp8_swiglu_quantize(_ptr(gate_up_bf16), int(rows), int(cols), _ptr(dst_codes), _ptr(dst_scales),
+                                  _ptr(dst_h_bf16), _stream(stream))
+    _check("jetfp8_swiglu_quantize", st)
+
+
 def jetfp8_gemm_fwd(xq, xs, wq, ws, y_bf16, M: int, N: int, K: int, stream=None) -> None:
     L = load_library()
     _check("jetfp8_gemm_fwd", L.jetfp8_gemm_fwd(_ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws), _ptr(y_bf16),
@@ -182,6 +204,35 @@ def requantize_cols_t(q, s, stream=None):
     sT = torch.empty((R // 128, C), dtype=torch.float32, device=q.device)
     jetfp8_requantize_cols_t(q, s, R, C, qT, sT, stream)
     return qT, sT
+
+
+def rmsnorm_quantize(x, weight, eps: float, return_y: bool = False, stream=None):
+    """Fused RMSNorm -> 1x128: x bf16 [R, C], weight bf16 [C] -> (codes [R, C], scales [C/128, R], rstd [R])
+    and, with return_y, the bf16 normalized activation [R, C] as well."""
+    import torch
+    _dt(x, torch.bfloat16, "x")
+    _dt(weight, torch.bfloat16, "weight")
+    R, C = x.shape
+    q = torch.empty((R, C), dtype=torch.uint8, device=x.device)
+    s = torch.empty((C // 128, R), dtype=torch.float32, device=x.device)
+    r = torch.empty((R,), dtype=torch.float32, device=x.device)
+    y = torch.empty((R, C), dtype=torch.bfloat16, device=x.device) if return_y else None
+    jetfp8_rmsnorm_quantize(x, weight, R, C, eps, q, s, r, y, stream)
+    return (q, s, r, y) if return_y else (q, s, r)
+
+
+def swiglu_quantize(gate_up, return_h: bool = False, stream=None):
+    """Fused SwiGLU -> 1x128: gate_up bf16 [R, 2F] (gate first, then up) -> (codes [R, F], scales [F/128, R])
+    and, with return_h, the bf16 activation h [R, F] as well."""
+    import torch
+    _dt(gate_up, torch.bfloat16, "gate_up")
+    R, F2 = gate_up.shape
+    F = F2 // 2
+    q = torch.empty((R, F), dtype=torch.uint8, device=gate_up.device)
+    s = torch.empty((F // 128, R), dtype=torch.float32, device=gate_up.device)
+    h = torch.empty((R, F), dtype=torch.bfloat16, device=gate_up.device) if return_h else None
+    jetfp8_swiglu_quantize(gate_up, R, F, q, s, h, stream)
+    return (q, s, h) if return_h else (q, s)
 
 
 def quantize_blocks(w, transposed: bool = True, stream=None):

@@ -1,5 +1,6 @@
 // C ABI of libjetfp8: host-side validation, then kernel launches on the caller's stream.
 // Validation touches no HIP API, so every error path can be exercised without a GPU.
+#include <float.h>
 #include <stdint.h>
 
 #include "../../include/jetfp8.h"
@@ -36,7 +37,7 @@ int check_gemm_extent(int64_t I, int64_t J, int64_t Kc) {
 
 extern "C" {
 
-int jetfp8_version(void) { return 200; }
+int jetfp8_version(void) { return 300; }
 
 const char* jetfp8_status_string(int status) {
     switch (status) {
@@ -46,6 +47,7 @@ const char* jetfp8_status_string(int status) {
         case JETFP8_ERR_ALIGN: return "a pointer is not 16-byte aligned";
         case JETFP8_ERR_MODE: return "unknown grouping mode, or a transposed-code output given for a mode without one";
         case JETFP8_ERR_HIP: return "the HIP runtime rejected a kernel launch";
+        case JETFP8_ERR_VALUE: return "a scalar argument is outside its domain";
         default: return "unknown status";
     }
 }
@@ -94,6 +96,32 @@ int jetfp8_requantize_cols_t(const uint8_t* codes, const float* scales, int64_t 
         return JETFP8_ERR_ALIGN;
     return hip_status(jetfp8::launch_quant_requant_cols(codes, scales, rows, cols, dst_codes_t, dst_scales_t,
                                                         static_cast<hipStream_t>(stream)));
+}
+
+int jetfp8_rmsnorm_quantize(const void* x_bf16, const void* weight_bf16, int64_t rows, int64_t cols, float eps,
+                            uint8_t* dst_codes, float* dst_scales, float* dst_rstd, void* dst_y_bf16, void* stream) {
+    if (!x_bf16 || !weight_bf16 || !dst_codes || !dst_scales) return JETFP8_ERR_NULL;
+    if (!dim_ok(rows) || !dim_ok(cols) || cols % 128 || cols > jetfp8::kRmsNormMaxCols) return JETFP8_ERR_SHAPE;
+    if (!(eps > 0.0f && eps <= FLT_MAX)) return JETFP8_ERR_VALUE;
+    if (!aligned16(x_bf16) || !aligned16(weight_bf16) || !aligned16(dst_codes) || !aligned16(dst_scales) ||
+        (dst_rstd && !aligned16(dst_rstd)) || (dst_y_bf16 && !aligned16(dst_y_bf16)))
+        return JETFP8_ERR_ALIGN;
+    return hip_status(jetfp8::launch_rmsnorm_quant(static_cast<const uint16_t*>(x_bf16),
+                                                   static_cast<const uint16_t*>(weight_bf16), rows, cols, eps,
+                                                   dst_codes, dst_scales, dst_rstd, static_cast<uint16_t*>(dst_y_bf16),
+                                                   static_cast<hipStream_t>(stream)));
+}
+
+int jetfp8_swiglu_quantize(const void* gate_up_bf16, int64_t rows, int64_t cols, uint8_t* dst_codes,
+                           float* dst_scales, void* dst_h_bf16, void* stream) {
+    if (!gate_up_bf16 || !dst_codes || !dst_scales) return JETFP8_ERR_NULL;
+    if (!dim_ok(rows) || !dim_ok(cols) || !dim_ok(2 * cols) || cols % 128) return JETFP8_ERR_SHAPE;
+    if (!aligned16(gate_up_bf16) || !aligned16(dst_codes) || !aligned16(dst_scales) ||
+        (dst_h_bf16 && !aligned16(dst_h_bf16)))
+        return JETFP8_ERR_ALIGN;
+    return hip_status(jetfp8::launch_swiglu_quant(static_cast<const uint16_t*>(gate_up_bf16), rows, cols, dst_codes,
+                                                  dst_scales, static_cast<uint16_t*>(dst_h_bf16),
+                                                  static_cast<hipStream_t>(stream)));
 }
 
 int jetfp8_gemm_fwd(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws, void* y_bf16, int64_t M,

@@ -15,6 +15,13 @@ hipError_t launch_quant_dual(const uint16_t* x, int64_t R, int64_t C, uint8_t* q
                              hipStream_t st);
 hipError_t launch_quant_requant_cols(const uint8_t* q, const float* s, int64_t R, int64_t C, uint8_t* qT,
                                      float* sT, hipStream_t st);
+// Fused producers (1x128 codes of the produced bf16 activation).  RMSNorm holds a row in registers: at most
+// kRmsNormMaxCols columns.
+constexpr int64_t kRmsNormMaxCols = 8192;
+hipError_t launch_rmsnorm_quant(const uint16_t* x, const uint16_t* w, int64_t R, int64_t C, float eps, uint8_t* q,
+                                float* s, float* rstd, uint16_t* y, hipStream_t st);
+hipError_t launch_swiglu_quant(const uint16_t* gu, int64_t R, int64_t F, uint8_t* q, float* s, uint16_t* h,
+                               hipStream_t st);
 hipError_t launch_quant_blocks(const uint16_t* x, int64_t R, int64_t C, uint8_t* q, float* s, uint8_t* qT,
                                hipStream_t st);
 

@@ -1,0 +1,257 @@
+// Fused producers of 1x128 FP8 activations for gfx950: RMSNorm -> quantize and SwiGLU -> quantize.
+//
+// The 1x128 activation quantization is fused with the operator that produces the activation (Jet-RL
+// explainers, "Schema de Quantification"), so the bf16 activation is never written and read back: each
+// kernel reads its bf16 inputs once and writes E4M3 codes, fp32 group scales and (optionally) the bf16
+// activation itself.  The codes and scales are those of the 1x128 quantizer applied to the bf16 activation,
+// bit for bit (same scale and rounding helpers).
+//
+// Numerics (the producers are not spelled out by the pages; plain readings):
+//   RMSNorm: r = fp32 nearest to 1 / sqrt(mean(x^2) + eps); y = bf16(fl32(fl32(x * r) * w)).
+//            The sum of squares is formed in fp64 (order-free to ~2^-48 relative), then mean, +eps, sqrt
+//            and the reciprocal in fp64 (each correctly rounded), then one rounding to fp32.  That is the
+//            nearest fp32 unless the exact value lies within ~2^-47 (relative) of an fp32 rounding midpoint.
+//   SwiGLU:  h = bf16 nearest to g * u / (1 + exp(-g)), the exact real value (gate = first half of the
+//            columns, up = second half).  An fp32 evaluation is within a few ulps; results within 16 fp32
+//            ulps of a bf16 rounding midpoint, tiny (< 2^-100) or huge (>= 2^127) results go through fp64,
+//            which decides the rounding unless the exact value lies within ~2^-50 of a midpoint.
+#include "jetfp8_common.h"
+#include "jetfp8_launch.h"
+
+namespace jetfp8 {
+
+namespace {
+
+__device__ __forceinline__ uint4 ld16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
+
+__device__ __forceinline__ uint32_t word_of(const uint4& v, int i) {
+    return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+__device__ __forceinline__ float elem_of(const uint4& v, int i) {
+    const uint32_t w = word_of(v, i >> 1);
+    return bf16_to_f32((i & 1) ? (w >> 16) : (w & 0xFFFFu));
+}
+
+// Codes of the 8 bf16 values held by a lane (bit patterns in hv), as the 1x128 quantizer forms them: the
+// group's amax from the 16 lanes of the DPP row, then the scale and the codes of the lane's 8 values.
+__device__ __forceinline__ uint2 quantize_lane8(const uint4& hv, float& scale) {
+    float f[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = elem_of(hv, i);
+    const GroupScale gs = make_group_scale(bf16_to_f32(row16_max_u32(amax8_bits(hv))));
+    scale = gs.s;
+    return encode8(f, gs);
+}
+
+// Wave-wide sum of a double (xor butterfly over the 64 lanes; every lane ends with the total).
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+    return v;
+}
+
+// fp32 bit pattern of v rounded to odd: the nearest fp32 toward zero, with its last bit set when that is
+// not v itself.  Rounding this pattern to bf16 (16 bits shorter) to nearest even gives the correct rounding
+// of v; |v| beyond the fp32 range becomes the largest fp32 with the sticky bit (so bf16 gives infinity).
+__device__ __forceinline__ uint32_t f64_to_f32_odd_bits(double v) {
+    const float f = (float)v;
+    uint32_t b = __float_as_uint(f);
+    const double av = fabs(v);
+    if (fabs((double)f) > av) b -= 1u;                       // step toward zero (|f| > |v| >= 0, so |f| > 0)
+    if (fabs((double)__uint_as_float(b)) != av) b |= 1u;
+    return b;
+}
+
+__device__ __forceinline__ uint32_t f32_bits_to_bf16_rne(uint32_t u) { return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16; }
+
+// exp(-g) for the SwiGLU fast path: 2^t with t = -g log2(e) split as t_hi + t_lo, where t_hi is the fp32
+// product and t_lo its rounding error (exact by fma) plus the low part of log2(e); then
+// 2^t = 2^t_hi * (1 + t_lo ln 2 + O(t_lo^2)), |t_lo| <= 2^-17.  Relative error: that of the hardware exp2
+// plus about one ulp.  Over- and underflow follow 2^t_hi (the callers screen those ranges).
+__device__ __forceinline__ float exp_neg(float g) {
+    constexpr float kLog2eHi = 1.44269502162933349609375f;      // fl32(log2 e)
+    constexpr float kLog2eLo = 1.925963033500011079e-8f;        // log2 e - kLog2eHi
+    constexpr float kLn2 = 0.693147180559945309f;
+    const float t_hi = -g * kLog2eHi;
+    const float t_lo = fmaf(-g, kLog2eHi, -t_hi) + (-g) * kLog2eLo;
+    return __builtin_amdgcn_exp2f(t_hi) * fmaf(t_lo, kLn2, 1.0f);
+}
+
+// The exact-rounding path of SwiGLU: fp64 evaluation (relative error ~2^-50), rounded to bf16 through a
+// round-to-odd fp32.  An fp64 value that is exactly a bf16 midpoint comes from a gate at one end of the range,
+// where exp(-g) is below fp64 resolution relative to 1 + exp(-g):
+//   - a large gate: h = g u / (1 + exp(-g)) lies just below |g u| in magnitude;
+//   - a tiny gate (1 + exp(-g) rounds to 2): h = (g u / 2)(1 + g / 2 + O(g^2)) lies just above |g u / 2| in
+//     magnitude for g > 0 and just below for g < 0.
+// The midpoint is then stepped by one fp32 ulp to the side of the exact value.
+__device__ __noinline__ uint32_t swiglu_bf16_exact(float g, float u) {
+    const double gd = g, ud = u;
+    const double hd = gd / (1.0 + exp(-gd)) * ud;
+    uint32_t b = f64_to_f32_odd_bits(hd);
+    if ((b & 0xFFFFu) == 0x8000u) b = (g > 0.0f && g < 1.0f) ? b + 1u : b - 1u;
+    return f32_bits_to_bf16_rne(b);
+}
+
+// bf16 bits of the correctly rounded silu(g) * u.
+__device__ __forceinline__ uint32_t swiglu_bf16(float g, float u) {
+    const float sil = g * __builtin_amdgcn_rcpf(1.0f + exp_neg(g));
+    const float h = sil * u;
+    const uint32_t hb = __float_as_uint(h) & 0x7FFFFFFFu, sb = __float_as_uint(sil) & 0x7FFFFFFFu;
+    // 0x19800000 = 2^-100, 0x7F000000 = 2^127; low 16 bits within 16 of 0x8000 = within 16 fp32 ulps of a bf16
+    // midpoint.  The fast silu(g) is within 3.23 * 2^-24 (relative) of the exact one for every finite bf16 gate
+    // outside the screened tiny range (measured over all of them), so the fast h is within 4.3 fp32 ulps of
+    // silu(g) u, a quarter of the screened window.
+    const bool exact = hb < 0x19800000u || sb < 0x19800000u || hb >= 0x7F000000u || ((hb - 0x7FF0u) & 0xFFFFu) <= 0x20u;
+    if (__builtin_expect(exact, 0)) return swiglu_bf16_exact(g, u);
+    return f32_bits_to_bf16_rne(__float_as_uint(h));
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------------------------------------
+// RMSNorm -> 1x128.  A block of 8 waves owns 32 consecutive rows, 4 per wave (rows r0 + 8 p + wave).  A wave
+// holds its row in registers: chunk c covers columns 512 c .. +511, lane l columns 512 c + 8 l .. +7, so the
+// 16 lanes of a DPP row hold one 128-column group.  The group scales of the 32 rows are staged in LDS and
+// written as whole 128-byte runs per group.
+constexpr int RN_ROWS = 32, RN_WAVES = 8, RN_PASSES = RN_ROWS / RN_WAVES;
+
+template <int NCH>
+__global__ __launch_bounds__(RN_WAVES * 64) void rmsnorm_quant_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, int64_t R, int64_t C, float eps,
+    uint8_t* __restrict__ q, float* __restrict__ s, float* __restrict__ rstd, uint16_t* __restrict__ y) {
+    __shared__ float sc[NCH * 4][RN_ROWS];
+    const int t = threadIdx.x, wave = t >> 6, lane = t & 63, lane16 = lane & 15, gl = lane >> 4;
+    const int64_t r0 = (int64_t)blockIdx.x * RN_ROWS;
+    const double eps_d = (double)eps;
+
+    for (int p = 0; p < RN_PASSES; ++p) {
+        const int rr = p * RN_WAVES + wave;
+        const int64_t row = r0 + rr;
+        if (row >= R) break;                                     // wave-uniform
+        uint4 v[NCH];
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            const int64_t col = (int64_t)c * 512 + lane * 8;
+            v[c] = ld16(x + row * C + (col < C ? col : 0));       // in-bounds stand-in past C: not used
+        }
+        // sum of squares in fp64 (8 partial sums per lane, then the wave)
+        double part[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            if ((int64_t)c * 512 + lane * 8 < C) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const double f = (double)elem_of(v[c], i);
+                    part[i] = fma(f, f, part[i]);
+                }
+            }
+        }
+        const double ss = wave_sum(((part[0] + part[1]) + (part[2] + part[3])) + ((part[4] + part[5]) + (part[6] + part[7])));
+        const float r = (float)(1.0 / sqrt(ss / (double)C + eps_d));
+        if (rstd && lane == 0) rstd[row] = r;
+
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            const int64_t col = (int64_t)c * 512 + lane * 8;
+            if (c * 512 >= C) break;                              // whole chunk past the row (uniform)
+            const bool ok = col < C;
+            const uint4 wv = ld16(w + (ok ? col : 0));
+            uint32_t hw[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const float y0 = (elem_of(v[c], 2 * k) * r) * elem_of(wv, 2 * k);
+                const float y1 = (elem_of(v[c], 2 * k + 1) * r) * elem_of(wv, 2 * k + 1);
+                hw[k] = f32_to_bf16_rne(y0) | (f32_to_bf16_rne(y1) << 16);
+            }
+            const uint4 yv = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+            float scale;
+            const uint2 codes = quantize_lane8(yv, scale);
+            if (ok) {
+                *reinterpret_cast<uint2*>(q + row * C + col) = codes;
+                if (y) *reinterpret_cast<uint4*>(y + row * C + col) = yv;
+                if (lane16 == 0) sc[c * 4 + gl][rr] = scale;
+            }
+        }
+    }
+    __syncthreads();
+    const int G = (int)(C / 128);
+    for (int i = t; i < G * RN_ROWS; i += RN_WAVES * 64) {
+        const int g = i / RN_ROWS, rr = i % RN_ROWS;
+        if (r0 + rr < R) s[(int64_t)g * R + r0 + rr] = sc[g][rr];
+    }
+}
+
+// ---------------------------------------------------------------------------------------------------------
+// SwiGLU -> 1x128.  gate_up [R][2F] -> codes [R][F], scales [F/128][R], optional h [R][F].  A block of 8 waves
+// owns 32 rows x 512 output columns (4 groups per row); lane l of a wave covers output columns
+// c0 + 8 l .. +7 of one row per pass, reading the matching 16 bytes of gate and of up.  All loads of a thread
+// are issued first (lanes past the last row or column load an in-bounds stand-in and store nothing).
+constexpr int SG_ROWS = 32, SG_COLS = 512, SG_WAVES = 8, SG_PASSES = SG_ROWS / SG_WAVES;
+
+__global__ __launch_bounds__(SG_WAVES * 64) void swiglu_quant_kernel(const uint16_t* __restrict__ gu, int64_t R,
+                                                                      int64_t F, uint8_t* __restrict__ q,
+                                                                      float* __restrict__ s, uint16_t* __restrict__ h,
+                                                                      uint32_t col_blocks) {
+    __shared__ float sc[4][SG_ROWS];
+    const int t = threadIdx.x, wave = t >> 6, lane = t & 63, gl = lane >> 4, lane16 = lane & 15;
+    const uint32_t cb = blockIdx.x % col_blocks, rb = blockIdx.x / col_blocks;
+    const int64_t c0 = (int64_t)cb * SG_COLS, r0 = (int64_t)rb * SG_ROWS;
+    const int64_t col = c0 + lane * 8;
+    const bool col_ok = col < F;                                 // F is a multiple of 128
+    const int64_t lcol = col_ok ? col : 0;
+    uint4 gv[SG_PASSES], uv[SG_PASSES];
+#pragma unroll
+    for (int p = 0; p < SG_PASSES; ++p) {
+        const int64_t row = min(r0 + p * SG_WAVES + wave, R - 1);
+        gv[p] = ld16(gu + row * 2 * F + lcol);
+        uv[p] = ld16(gu + row * 2 * F + F + lcol);
+    }
+#pragma unroll
+    for (int p = 0; p < SG_PASSES; ++p) {
+        const int64_t row = r0 + p * SG_WAVES + wave;
+        uint32_t hw[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint32_t lo = swiglu_bf16(elem_of(gv[p], 2 * k), elem_of(uv[p], 2 * k));
+            const uint32_t hi = swiglu_bf16(elem_of(gv[p], 2 * k + 1), elem_of(uv[p], 2 * k + 1));
+            hw[k] = lo | (hi << 16);
+        }
+        const uint4 hv = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+        float scale;
+        const uint2 codes = quantize_lane8(hv, scale);
+        if (col_ok && row < R) {
+            *reinterpret_cast<uint2*>(q + row * F + col) = codes;
+            if (h) *reinterpret_cast<uint4*>(h + row * F + col) = hv;
+        }
+        if (lane16 == 0) sc[gl][p * SG_WAVES + wave] = scale;
+    }
+    __syncthreads();
+    if (t < 4 * SG_ROWS) {
+        const int g = t / SG_ROWS, r = t % SG_ROWS;
+        const int64_t gg = c0 / 128 + g;
+        if (gg * 128 < F && r0 + r < R) s[gg * R + r0 + r] = sc[g][r];
+    }
+}
+
+hipError_t launch_rmsnorm_quant(const uint16_t* x, const uint16_t* w, int64_t R, int64_t C, float eps, uint8_t* q,
+                                float* s, float* rstd, uint16_t* y, hipStream_t st) {
+    if (C > kRmsNormMaxCols) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)((R + RN_ROWS - 1) / RN_ROWS)), block(RN_WAVES * 64);
+    const int nch = (int)((C + 511) / 512);
+    if (nch <= 2) hipLaunchKernelGGL(rmsnorm_quant_kernel<2>, grid, block, 0, st, x, w, R, C, eps, q, s, rstd, y);
+    else if (nch <= 4) hipLaunchKernelGGL(rmsnorm_quant_kernel<4>, grid, block, 0, st, x, w, R, C, eps, q, s, rstd, y);
+    else if (nch <= 8) hipLaunchKernelGGL(rmsnorm_quant_kernel<8>, grid, block, 0, st, x, w, R, C, eps, q, s, rstd, y);
+    else hipLaunchKernelGGL(rmsnorm_quant_kernel<16>, grid, block, 0, st, x, w, R, C, eps, q, s, rstd, y);
+    return hipGetLastError();
+}
+
+hipError_t launch_swiglu_quant(const uint16_t* gu, int64_t R, int64_t F, uint8_t* q, float* s, uint16_t* h,
+                               hipStream_t st) {
+    const int64_t col_blocks = (F + SG_COLS - 1) / SG_COLS, row_blocks = (R + SG_ROWS - 1) / SG_ROWS;
+    if (col_blocks * row_blocks >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(swiglu_quant_kernel, dim3((unsigned)(col_blocks * row_blocks)), dim3(SG_WAVES * 64), 0, st,
+                       gu, R, F, q, s, h, (uint32_t)col_blocks);
+    return hipGetLastError();
+}
+
+}  // namespace jetfp8

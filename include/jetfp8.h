@@ -51,7 +51,8 @@ typedef enum {
     JETFP8_ERR_SHAPE = -2,  /* a dimension < 1, >= 2^31, or a grouped/contraction axis not a multiple of 128 */
     JETFP8_ERR_ALIGN = -3,  /* a pointer is not 16-byte aligned */
     JETFP8_ERR_MODE = -4,   /* unknown grouping mode, or dst_codes_t given for a mode without it */
-    JETFP8_ERR_HIP = -5     /* the HIP runtime rejected a launch */
+    JETFP8_ERR_HIP = -5,    /* the HIP runtime rejected a launch */
+    JETFP8_ERR_VALUE = -6   /* a scalar argument is outside its domain (e.g. eps <= 0) */
 } jetfp8_status;
 
 typedef enum {
@@ -96,6 +97,31 @@ int jetfp8_quantize_dual(const void* src_bf16, int64_t rows, int64_t cols, uint8
  * rows % 128 == 0 and cols % 128 == 0. */
 int jetfp8_requantize_cols_t(const uint8_t* codes, const float* scales, int64_t rows, int64_t cols,
                              uint8_t* dst_codes_t, float* dst_scales_t, void* stream);
+
+/* Fused RMSNorm -> 1x128 quantization.  The activation quantization is fused with the operator that produces
+ * the activation (Jet-RL explainers, "Schema de Quantification"), here the RMSNorm in front of a linear layer:
+ *   r[i]    = fp32 nearest to 1 / sqrt(mean_k x[i][k]^2 + eps)      (formed in fp64; see below)
+ *   y[i][k] = bf16( fl32( fl32(x[i][k] * r[i]) * weight[k] ) )       (round to nearest even)
+ *   dst_codes, dst_scales = the JETFP8_ROWS_1x128 quantization of y, bit for bit.
+ * x [rows][cols] bf16, weight [cols] bf16 -> dst_codes [rows][cols], dst_scales [cols/128][rows];
+ * optional (NULL = not written): dst_rstd [rows] fp32 (r, for the backward), dst_y_bf16 [rows][cols] (y).
+ * r is the correctly rounded value unless the exact value lies within about 2^-47 (relative) of a point
+ * where its fp32 rounding changes; there either neighbour may be returned.  cols % 128 == 0 and
+ * cols <= 8192 (a row is held in registers); 0 < eps <= FLT_MAX (JETFP8_ERR_VALUE otherwise).
+ * Finite inputs whose y overflows bf16 give unspecified codes for that group. */
+int jetfp8_rmsnorm_quantize(const void* x_bf16, const void* weight_bf16, int64_t rows, int64_t cols, float eps,
+                            uint8_t* dst_codes, float* dst_scales, float* dst_rstd, void* dst_y_bf16, void* stream);
+
+/* Fused SwiGLU -> 1x128 quantization (the activation in front of the down projection, quantized by the
+ * operator that produces it; Jet-RL explainers, "Schema de Quantification"):
+ *   h[i][j] = bf16 nearest to silu(g) * u = g * u / (1 + exp(-g)) of the exact real value, with
+ *             g = gate_up[i][j] (gate: columns 0 .. cols-1) and u = gate_up[i][cols + j] (up: cols .. 2cols-1);
+ *   dst_codes, dst_scales = the JETFP8_ROWS_1x128 quantization of h, bit for bit.
+ * gate_up [rows][2 cols] bf16 -> dst_codes [rows][cols], dst_scales [cols/128][rows]; optional
+ * dst_h_bf16 [rows][cols] (h; NULL = not written).  cols % 128 == 0.  Finite inputs; inputs whose h
+ * overflows bf16 give unspecified codes for that group. */
+int jetfp8_swiglu_quantize(const void* gate_up_bf16, int64_t rows, int64_t cols, uint8_t* dst_codes,
+                           float* dst_scales, void* dst_h_bf16, void* stream);
 
 /* Forward FP8 linear (rollout decode, prefill, training forward):
  *   Y[m][n] = sum_g xs[g][m] * ws[n/128][g] * sum_{k in g} xq[m][k] * wq[n][k]

@@ -151,3 +151,58 @@ def device_linear(workload: Workload, index: int, device="cuda", M: Optional[int
 
 def list_workloads() -> List[str]:
     return list(WORKLOADS)
+
+
+# ------------------------------------------------------------------------------------------------
+# Inputs of the fused producers (RMSNorm -> 1x128 and SwiGLU -> 1x128): same recipes on the host (numpy) and
+# on the device (torch), seeded.
+# ------------------------------------------------------------------------------------------------
+def host_rmsnorm_inputs(seed: int, R: int, C: int, outlier_frac: float = 0.01):
+    """Residual-stream rows for an RMSNorm: x = N(0,1) * 2^U(-4,4) per row, outlier channels x50; the norm's
+    weight = 1 + 0.1 N(0,1).  Returns (x bits [R,C], w bits [C])."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed)))
+    x = rng.standard_normal((R, C), dtype=np.float32)
+    x *= np.exp2(rng.uniform(-4, 4, size=(R, 1))).astype(np.float32)
+    cols = rng.choice(C, size=outlier_count(outlier_frac, C), replace=False)
+    x[:, cols] *= np.float32(50.0)
+    w = (1.0 + 0.1 * rng.standard_normal(C)).astype(np.float32)
+    return _to_bf16_bits(x), _to_bf16_bits(w)
+
+
+def host_gate_up(seed: int, R: int, F: int, outlier_frac: float = 0.01):
+    """Output of a gate/up projection for a SwiGLU: gate = 2 N(0,1) with outlier channels x20 (large positive and
+    negative gates, the tails of silu), up = N(0,1).  Returns bits [R, 2F] (gate columns first)."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed)))
+    g = rng.standard_normal((R, F), dtype=np.float32) * np.float32(2.0)
+    cols = rng.choice(F, size=outlier_count(outlier_frac, F), replace=False)
+    g[:, cols] *= np.float32(20.0)
+    u = rng.standard_normal((R, F), dtype=np.float32)
+    return _to_bf16_bits(np.concatenate([g, u], axis=1))
+
+
+def device_rmsnorm_inputs(seed: int, R: int, C: int, device="cuda", outlier_frac: float = 0.01):
+    """Device version of host_rmsnorm_inputs (same recipe, torch generator): (x [R,C], w [C]) bf16."""
+    import torch
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    x = torch.randn((R, C), device=device, generator=gen)
+    x *= torch.exp2(torch.rand((R, 1), device=device, generator=gen) * 8 - 4)
+    cols = torch.randperm(C, device=device, generator=gen)[:outlier_count(outlier_frac, C)]
+    x[:, cols] *= 50.0
+    w = 1.0 + 0.1 * torch.randn((C,), device=device, generator=gen)
+    return x.to(torch.bfloat16), w.to(torch.bfloat16)
+
+
+def device_gate_up(seed: int, R: int, F: int, device="cuda", outlier_frac: float = 0.01):
+    """Device version of host_gate_up: bf16 [R, 2F]."""
+    import torch
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    gu = torch.empty((R, 2 * F), device=device, dtype=torch.bfloat16)
+    g = torch.randn((R, F), device=device, generator=gen) * 2.0
+    cols = torch.randperm(F, device=device, generator=gen)[:outlier_count(outlier_frac, F)]
+    g[:, cols] *= 20.0
+    gu[:, :F] = g.to(torch.bfloat16)
+    del g
+    gu[:, F:] = torch.randn((R, F), device=device, generator=gen).to(torch.bfloat16)
+    return gu
