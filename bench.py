@@ -15,6 +15,9 @@ Prints one JSON line.  Besides the contract fields it carries
                 traffic = HBM bytes per launch from rocprofv3 counters when supplied (--traffic-json).
   roofline_quant the quantize kernels: algorithmic bytes / time against 8 TB/s.
   cpu_baseline  the CPU oracle timed on this host on a bounded sample of the same workload.
+
+--producers prints a separate line for the fused producers that emit 1x128 FP8 directly (RMSNorm and SwiGLU):
+algorithmic bytes (bf16 read, codes and scales written, rstd) / kernel time against 8 TB/s, per kernel.
 """
 import argparse
 import json
@@ -44,6 +47,9 @@ def parse():
                    help="WGrad's X from the saved 1x128 FP8 codes (dequantize, requantize 128x1) instead of bf16 X")
     p.add_argument("--separate-quant", action="store_true",
                    help="quantize X and dY with the 1x128 and 128x1 kernels separately (two reads each)")
+    p.add_argument("--producers", action="store_true",
+                   help="instead of the GEMM step, time the fused producers of one layer (2 RMSNorm -> 1x128 and "
+                        "1 SwiGLU -> 1x128 at the workload's token count) and print their own JSON line")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="first run a 1 GiB device-to-device copy (known bytes) to scale rocprofv3 byte counters")
     return p.parse_args()
@@ -202,6 +208,119 @@ def cpu_baseline(wl, rows, workloads):
             "seconds": elapsed}
 
 
+def producer_bytes(R, C, F):
+    """Algorithmic bytes of the fused producers: RMSNorm reads x and the weight, writes codes, scales and rstd;
+    SwiGLU reads gate and up, writes codes and scales."""
+    return {"rmsnorm": R * C * 2 + C * 2 + R * C + (C // 128) * R * 4 + R * 4,
+            "swiglu": R * 2 * F * 2 + R * F + (F // 128) * R * 4}
+
+
+def producers_cpu_baseline(C, F, rows_rn, rows_sg, workloads):
+    import oracle
+    from oracle import producers
+    oracle.lib()
+    xb, wb = workloads.host_rmsnorm_inputs(21, rows_rn, C)
+    gub = workloads.host_gate_up(22, rows_sg, F)
+    t0 = time.perf_counter()
+    producers.rmsnorm_quantize(xb, wb, 1e-5)
+    t1 = time.perf_counter()
+    producers.swiglu_quantize(gub)
+    t2 = time.perf_counter()
+    b = producer_bytes(rows_rn, C, F)["rmsnorm"] + producer_bytes(rows_sg, C, F)["swiglu"]
+    return {"value": round(b / (t2 - t0) / 1e9, 4), "unit": "GB/s", "cores": oracle.default_threads(), "kind": "oracle",
+            "sample": (f"oracle/producers.py: RMSNorm->1x128 of {rows_rn} rows x {C} ({t1 - t0:.1f} s, exact "
+                       f"rational rstd) and SwiGLU->1x128 of {rows_sg} rows x {F} ({t2 - t1:.1f} s, numpy float64); "
+                       "algorithmic bytes / time; the Python and numpy steps run on one core, the 1x128 quantizer "
+                       "on the oracle's thread pool"),
+            "seconds": round(t2 - t0, 2)}
+
+
+PRODUCER_SOURCES = [os.path.join(ROOT, "fp8_precision_rl_amd", "csrc", f) for f in ("jetfp8_producers.hip", "jetfp8_common.h")]
+
+
+def producer_traffic(path=os.path.join(ROOT, "profiles", "producers_traffic.json")):
+    """Per-launch HBM bytes of the producer kernels from rocprofv3 FETCH_SIZE / WRITE_SIZE (scaled by a 1 GiB
+    copy), or None when the record is missing or was taken on other kernel sources."""
+    import hashlib
+    try:
+        rec = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    digest = hashlib.sha256(b"".join(open(f, "rb").read() for f in PRODUCER_SOURCES)).hexdigest()
+    if rec.get("source_sha256") != digest:
+        return None
+    return {k: v["bytes"] for k, v in rec["kernels"].items()}
+
+
+def run_producers(args, torch, jf, workloads, wl):
+    lin = {n: (K, N) for n, K, N in wl.linears}
+    C, F, R = lin["qkv"][0], lin["down"][0], wl.M
+    x, w = workloads.device_rmsnorm_inputs(31, R, C)
+    gu = workloads.device_gate_up(32, R, F)
+    u8, f32 = torch.uint8, torch.float32
+    q_rn = torch.empty((R, C), dtype=u8, device=x.device)
+    s_rn = torch.empty((C // 128, R), dtype=f32, device=x.device)
+    r_rn = torch.empty((R,), dtype=f32, device=x.device)
+    q_sg = torch.empty((R, F), dtype=u8, device=x.device)
+    s_sg = torch.empty((F // 128, R), dtype=f32, device=x.device)
+    st = torch.cuda.current_stream()
+    byts = producer_bytes(R, C, F)
+
+    def step(ev=None):
+        for kind in ("rmsnorm", "swiglu", "rmsnorm"):           # attention norm, MLP activation, MLP norm
+            a = b = None
+            if ev is not None:
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(st)
+            if kind == "rmsnorm":
+                jf.jetfp8_rmsnorm_quantize(x, w, R, C, 1e-5, q_rn, s_rn, r_rn, None, st)
+            else:
+                jf.jetfp8_swiglu_quantize(gu, R, F, q_sg, s_sg, None, st)
+            if ev is not None:
+                b.record(st)
+                ev.append((kind, a, b))
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = []
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(st)
+    for _ in range(args.steps):
+        step(ev)
+    t1.record(st)
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / args.steps
+    per = {}
+    for kind, a, b in ev:
+        per.setdefault(kind, [0.0, 0])
+        per[kind][0] += a.elapsed_time(b)
+        per[kind][1] += 1
+    total_bytes = 2 * byts["rmsnorm"] + byts["swiglu"]
+    kern = {k: {"mean_launch_us": round(1e3 * v[0] / v[1], 2), "bytes_per_launch": byts[k],
+                "achieved": round(byts[k] / (v[0] / v[1] * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(byts[k] / (v[0] / v[1] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)} for k, v in per.items()}
+    traffic = producer_traffic()
+    for k in kern:
+        kern[k]["traffic"] = traffic.get(k) if traffic else None
+    dom = max(kern, key=lambda k: per[k][0])
+    out = {
+        "metric": "fused RMSNorm/SwiGLU -> 1x128 FP8 producers, algorithmic GB/s",
+        "value": round(total_bytes / (ms_step * 1e-3) / 1e9, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16 in, fp32/fp64 math, fp8_e4m3 out",
+        "data": "synthetic (seeded torch generator on device: residual rows N(0,1) * 2^U(-4,4) with 1% outlier "
+                "channels x50, norm weight 1+0.1N(0,1); gate 2N(0,1) with 1% outlier channels x20, up N(0,1))",
+        "config": {"workload": f"{wl.name} producers", "tokens": R, "hidden": C, "ffn": F,
+                   "step": "2 x RMSNorm->1x128 [tokens x hidden] + 1 x SwiGLU->1x128 [tokens x 2 ffn -> ffn]"},
+        "roofline": dict(kern[dom], bound="hbm", kernel=f"{dom}_quant_kernel"),
+        "per_kernel": kern,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = producers_cpu_baseline(C, F, 2048, 6144, workloads)
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -219,6 +338,9 @@ def main():
     wl = workloads.WORKLOADS[args.workload]
     if args.calibrate_copy:
         copy_calibration(torch)
+    if args.producers:
+        run_producers(args, torch, jf, workloads, wl)
+        return
     layers = [Linear(wl, i, torch, workloads) for i in range(len(wl.linears))]
     torch.cuda.synchronize()
     st = torch.cuda.current_stream()

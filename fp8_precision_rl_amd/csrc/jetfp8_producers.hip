@@ -92,28 +92,31 @@ __device__ __noinline__ uint32_t swiglu_bf16_exact(float g, float u) {
     return f32_bits_to_bf16_rne(b);
 }
 
-// bf16 bits of the correctly rounded silu(g) * u.
-__device__ __forceinline__ uint32_t swiglu_bf16(float g, float u) {
+// bf16 bits of silu(g) * u from the fast fp32 evaluation, and whether that value must instead be taken from
+// swiglu_bf16_exact (the fast one is then not used).
+__device__ __forceinline__ uint32_t swiglu_bf16_fast(float g, float u, bool& exact) {
     const float sil = g * __builtin_amdgcn_rcpf(1.0f + exp_neg(g));
     const float h = sil * u;
-    const uint32_t hb = __float_as_uint(h) & 0x7FFFFFFFu, sb = __float_as_uint(sil) & 0x7FFFFFFFu;
-    // 0x19800000 = 2^-100, 0x7F000000 = 2^127; low 16 bits within 16 of 0x8000 = within 16 fp32 ulps of a bf16
-    // midpoint.  The fast silu(g) is within 3.23 * 2^-24 (relative) of the exact one for every finite bf16 gate
-    // outside the screened tiny range (measured over all of them), so the fast h is within 4.3 fp32 ulps of
-    // silu(g) u, a quarter of the screened window.
-    const bool exact = hb < 0x19800000u || sb < 0x19800000u || hb >= 0x7F000000u || ((hb - 0x7FF0u) & 0xFFFFu) <= 0x20u;
-    if (__builtin_expect(exact, 0)) return swiglu_bf16_exact(g, u);
+    const uint32_t hb = __float_as_uint(h) & 0x7FFFFFFFu;
+    // Exact path for: g < -87 (1 + exp(-g) > 2^125.5: the reciprocal nears the subnormal range); h outside
+    // [2^-120, 2^127) (0x03800000, 0x7F000000: fp32 subnormal products, overflow); low 16 bits of h within 16 of
+    // 0x8000, i.e. within 16 fp32 ulps of a bf16 rounding midpoint.  For every finite bf16 gate >= -87 the fast
+    // silu(g) is within 3.23 * 2^-24 (relative) of the exact value (measured over all of them; for tiny gates
+    // it is g / 2, exact to far below that), so the fast h is within 4.3 ulps of silu(g) u: a quarter of the
+    // screened window.
+    exact = (g < -87.0f) | (hb - 0x03800000u >= 0x7F000000u - 0x03800000u) | (((hb - 0x7FF0u) & 0xFFFFu) <= 0x20u);
     return f32_bits_to_bf16_rne(__float_as_uint(h));
 }
 
 }  // namespace
 
 // ---------------------------------------------------------------------------------------------------------
-// RMSNorm -> 1x128.  A block of 8 waves owns 32 consecutive rows, 4 per wave (rows r0 + 8 p + wave).  A wave
-// holds its row in registers: chunk c covers columns 512 c .. +511, lane l columns 512 c + 8 l .. +7, so the
-// 16 lanes of a DPP row hold one 128-column group.  The group scales of the 32 rows are staged in LDS and
-// written as whole 128-byte runs per group.
-constexpr int RN_ROWS = 32, RN_WAVES = 8, RN_PASSES = RN_ROWS / RN_WAVES;
+// RMSNorm -> 1x128.  A block of 8 waves owns 8 consecutive rows, one per wave.  A wave holds its row in
+// registers: chunk c covers columns 512 c .. +511, lane l columns 512 c + 8 l .. +7, so the 16 lanes of a DPP
+// row hold one 128-column group.  The group scales of the 8 rows are staged in LDS and written as 32-byte runs
+// per group.  (One row per wave measured fastest: 4 rows per wave, with or without the next row's loads issued
+// ahead, left all blocks loading, then all computing, in step.)
+constexpr int RN_ROWS = 8, RN_WAVES = 8, RN_PASSES = RN_ROWS / RN_WAVES;
 
 template <int NCH>
 __global__ __launch_bounds__(RN_WAVES * 64) void rmsnorm_quant_kernel(
@@ -124,6 +127,7 @@ __global__ __launch_bounds__(RN_WAVES * 64) void rmsnorm_quant_kernel(
     const int64_t r0 = (int64_t)blockIdx.x * RN_ROWS;
     const double eps_d = (double)eps;
 
+#pragma unroll
     for (int p = 0; p < RN_PASSES; ++p) {
         const int rr = p * RN_WAVES + wave;
         const int64_t row = r0 + rr;
@@ -209,13 +213,22 @@ __global__ __launch_bounds__(SG_WAVES * 64) void swiglu_quant_kernel(const uint1
 #pragma unroll
     for (int p = 0; p < SG_PASSES; ++p) {
         const int64_t row = r0 + p * SG_WAVES + wave;
+        // fast values of the lane's 8 elements without branches, then one rarely taken branch that replaces the
+        // flagged ones by the exact path
+        uint32_t hb[8], need = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            bool ex;
+            hb[i] = swiglu_bf16_fast(elem_of(gv[p], i), elem_of(uv[p], i), ex);
+            need |= (uint32_t)ex << i;
+        }
+        if (__builtin_expect(need != 0, 0)) {
+            for (int i = 0; i < 8; ++i)
+                if ((need >> i) & 1u) hb[i] = swiglu_bf16_exact(elem_of(gv[p], i), elem_of(uv[p], i));
+        }
         uint32_t hw[4];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const uint32_t lo = swiglu_bf16(elem_of(gv[p], 2 * k), elem_of(uv[p], 2 * k));
-            const uint32_t hi = swiglu_bf16(elem_of(gv[p], 2 * k + 1), elem_of(uv[p], 2 * k + 1));
-            hw[k] = lo | (hi << 16);
-        }
+        for (int k = 0; k < 4; ++k) hw[k] = hb[2 * k] | (hb[2 * k + 1] << 16);
         const uint4 hv = make_uint4(hw[0], hw[1], hw[2], hw[3]);
         float scale;
         const uint2 codes = quantize_lane8(hv, scale);

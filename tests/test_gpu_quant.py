@@ -156,6 +156,7 @@ def test_all_x_amax_pairs_sampled(jf, orc):
     amax = all_a if full else np.unique(np.concatenate([all_a[::29], [1, 2, 0x7F, 0x80, 0x81, 0x3F80, 0x43E0, 0x7F7F]]))
     chunk = 2048 if not full else 1024
     for i in range(0, amax.size, chunk):
+        print(f"pairs: amax values {i} .. {min(i + chunk, amax.size)} of {amax.size}", flush=True)
         g = _pair_groups(amax[i:i + chunk].astype(np.uint16))
         q, s = jf.quantize_rows(bits_to_dev(g))
         torch.cuda.synchronize()

@@ -1,11 +1,12 @@
-"""Unified precision flow at the level of a stack of FP8 MLP blocks (Jet-RL explainers, "Architecture
+"""Unified precision flow at the level of a stack of FP8 pre-norm MLP blocks (Jet-RL explainers, "Architecture
 Centrale": the rollout graph is a subgraph of the training forward graph, with the same quantization and
-precision).  Each block is h = x + down(SwiGLU(gate_up(x))): both linears are this library's FP8 path (1x128
-activations, 128x128 weights); SwiGLU and the residual add are row-local bf16 elementwise glue.
+precision).  Each block is x + down(SwiGLU(gate_up(RMSNorm(x)))), all on this library's kernels: the fused
+RMSNorm->1x128 producer, the FP8 gate/up GEMM (128x128 weight blocks), the fused SwiGLU->1x128 producer and the
+FP8 down GEMM; only the residual add is torch (row-local bf16).
 
   * A token decoded alone (M = 1) or in a decode batch (M = 32) gets bitwise the same hidden state at every
     depth as the same token inside a prefill of the whole sequence (M = 96): no rollout/training mismatch.
-  * Against a bf16 reference of the same stack (fp32 matmuls of the bf16 tensors), each FP8 block adds a
+  * Against a bf16 reference of the same stack (fp32 math on the bf16 tensors), each FP8 block adds a
     quantization error of a few percent that does not grow with depth.
 Weights are random and seeded; no trained model is involved.
 """
@@ -29,26 +30,40 @@ def stack():
     for _ in range(LAYERS):
         w_gu = (torch.randn((2 * F, D), device="cuda", generator=g) * D ** -0.5).to(torch.bfloat16)
         w_dn = (torch.randn((D, F), device="cuda", generator=g) * F ** -0.5).to(torch.bfloat16)
+        w_nm = (1.0 + 0.1 * torch.randn((D,), device="cuda", generator=g)).to(torch.bfloat16)
         gq, gs, _ = jf.quantize_blocks(w_gu)
         dq, ds, _ = jf.quantize_blocks(w_dn)
-        layers.append(dict(w_gu=w_gu, w_dn=w_dn, gq=gq, gs=gs, dq=dq, ds=ds))
+        layers.append(dict(w_gu=w_gu, w_dn=w_dn, w_nm=w_nm, gq=gq, gs=gs, dq=dq, ds=ds))
     x0 = torch.randn((S, D), device="cuda", generator=g).to(torch.bfloat16)
     x0[:, 17] *= 30                                                   # an outlier channel
     return jf, layers, x0
 
 
-def _swiglu(gu):
+EPS = 1e-5
+
+
+def _fp8_block(jf, L, x):
+    """FP8 branch y of one block (the residual is added by the caller)."""
+    xq, xs, _ = jf.rmsnorm_quantize(x, L["w_nm"], EPS)
+    gu = jf.gemm_fwd(xq, xs, L["gq"], L["gs"])
+    hq, hs = jf.swiglu_quantize(gu)
+    return jf.gemm_fwd(hq, hs, L["dq"], L["ds"])
+
+
+def _bf16_block(L, x):
     import torch
+    xf = x.float()
+    n = (xf * torch.rsqrt(xf.pow(2).mean(dim=1, keepdim=True) + EPS) * L["w_nm"].float()).to(torch.bfloat16)
+    gu = (n.float() @ L["w_gu"].float().t()).to(torch.bfloat16)
     g, u = gu.float().chunk(2, dim=-1)
-    return (torch.nn.functional.silu(g) * u).to(torch.bfloat16)
+    h = (torch.nn.functional.silu(g) * u).to(torch.bfloat16)
+    return h.float() @ L["w_dn"].float().t()
 
 
 def _fp8_stack(jf, layers, x):
     outs = []
     for L in layers:
-        gu, _ = jf.linear_forward(x, L["gq"], L["gs"])
-        y, _ = jf.linear_forward(_swiglu(gu), L["dq"], L["ds"])
-        x = (x.float() + y.float()).to(x.dtype)
+        x = (x.float() + _fp8_block(jf, L, x).float()).to(x.dtype)
         outs.append(x)
     return outs
 
@@ -56,9 +71,7 @@ def _fp8_stack(jf, layers, x):
 def _bf16_stack(layers, x):
     outs = []
     for L in layers:
-        gu = (x.float() @ L["w_gu"].float().t()).to(x.dtype)
-        y = (_swiglu(gu).float() @ L["w_dn"].float().t()).to(x.dtype)
-        x = (x.float() + y.float()).to(x.dtype)
+        x = (x.float() + _bf16_block(L, x)).to(x.dtype)
         outs.append(x)
     return outs
 
@@ -88,11 +101,8 @@ def test_fp8_block_error_against_bf16(stack):
     per_block = []
     x = x0
     for L in layers:
-        gu, _ = jf.linear_forward(x, L["gq"], L["gs"])
-        y8, _ = jf.linear_forward(_swiglu(gu), L["dq"], L["ds"])
-        gu_r = (x.float() @ L["w_gu"].float().t()).to(x.dtype)
-        y_r = (_swiglu(gu_r).float() @ L["w_dn"].float().t())
-        per_block.append(float((y8.float() - y_r).norm() / y_r.norm()))
+        y8, y_r = _fp8_block(jf, L, x).float(), _bf16_block(L, x)
+        per_block.append(float((y8 - y_r).norm() / y_r.norm()))
         x = (x.float() + y_r).to(x.dtype)                              # continue on the bf16 trajectory
     free = [float((a.float() - b.float()).norm() / b.float().norm())
             for a, b in zip(_fp8_stack(jf, layers, x0), _bf16_stack(layers, x0))]
