@@ -1,13 +1,20 @@
-"""Unified precision flow at the level of a stack of FP8 pre-norm MLP blocks (Jet-RL explainers, "Architecture
+"""Unified precision flow at the level of a stack of FP8 pre-norm decoder blocks (Jet-RL explainers, "Architecture
 Centrale": the rollout graph is a subgraph of the training forward graph, with the same quantization and
-precision).  Each block is x + down(SwiGLU(gate_up(RMSNorm(x)))), all on this library's kernels: the fused
-RMSNorm->1x128 producer, the FP8 gate/up GEMM (128x128 weight blocks), the fused SwiGLU->1x128 producer and the
-FP8 down GEMM; only the residual add is torch (row-local bf16).
+precision).  Each block is
 
-  * A token decoded alone (M = 1) or in a decode batch (M = 32) gets bitwise the same hidden state at every
-    depth as the same token inside a prefill of the whole sequence (M = 96): no rollout/training mismatch.
-  * Against a bf16 reference of the same stack (fp32 math on the bf16 tensors), each FP8 block adds a
-    quantization error of a few percent that does not grow with depth.
+    h  = x + O(attn(QKV(RMSNorm(x))))
+    x' = h + down(SwiGLU(gate_up(RMSNorm(h))))
+
+with every linear and producer on this library's kernels: the fused RMSNorm->1x128 and SwiGLU->1x128 producers,
+the 1x128 quantizer for the attention output, and the FP8 GEMMs with 128x128 weight blocks.  The attention
+mixing itself (causal softmax over the cached keys) is a deterministic fp64 CPU stand-in that computes each query
+row with the same call whatever the mode, so any difference between the modes can only come from the FP8 path.
+
+  * Prefill of 96 tokens (M = 96), incremental decode of the same tokens one at a time (M = 1, with a key/value
+    cache) and chunked decode (M = 32 per step) give bitwise the same hidden state for every token at every depth:
+    no rollout/training mismatch.
+  * Against a bf16 reference of the same stack (fp32 math on the bf16 tensors, same attention stand-in), each FP8
+    block adds a quantization error of a few percent that does not grow with depth (teacher forcing).
 Weights are random and seeded; no trained model is involved.
 """
 import numpy as np
@@ -15,7 +22,9 @@ import pytest
 
 pytestmark = pytest.mark.gpu
 
-D, F, LAYERS, S = 1024, 2816, 4, 96
+D, HEADS, F, LAYERS, S = 1024, 8, 2816, 3, 96
+HD = D // HEADS
+EPS = 1e-5
 
 
 @pytest.fixture(scope="module")
@@ -26,86 +35,133 @@ def stack():
     jf.load_library()
     g = torch.Generator(device="cuda")
     g.manual_seed(7)
+
+    def lin(n, k):
+        return (torch.randn((n, k), device="cuda", generator=g) * k ** -0.5).to(torch.bfloat16)
+
+    def norm_w():
+        return (1.0 + 0.1 * torch.randn((D,), device="cuda", generator=g)).to(torch.bfloat16)
+
     layers = []
     for _ in range(LAYERS):
-        w_gu = (torch.randn((2 * F, D), device="cuda", generator=g) * D ** -0.5).to(torch.bfloat16)
-        w_dn = (torch.randn((D, F), device="cuda", generator=g) * F ** -0.5).to(torch.bfloat16)
-        w_nm = (1.0 + 0.1 * torch.randn((D,), device="cuda", generator=g)).to(torch.bfloat16)
-        gq, gs, _ = jf.quantize_blocks(w_gu)
-        dq, ds, _ = jf.quantize_blocks(w_dn)
-        layers.append(dict(w_gu=w_gu, w_dn=w_dn, w_nm=w_nm, gq=gq, gs=gs, dq=dq, ds=ds))
+        L = dict(w_qkv=lin(3 * D, D), w_o=lin(D, D), w_gu=lin(2 * F, D), w_dn=lin(D, F), n1=norm_w(), n2=norm_w())
+        for k in ("qkv", "o", "gu", "dn"):
+            L[k + "_q"], L[k + "_s"], _ = jf.quantize_blocks(L["w_" + k])
+        layers.append(L)
     x0 = torch.randn((S, D), device="cuda", generator=g).to(torch.bfloat16)
     x0[:, 17] *= 30                                                   # an outlier channel
     return jf, layers, x0
 
 
-EPS = 1e-5
+# --------------------------------------------------------------------------- attention stand-in (CPU, fp64)
+
+def _attn_row(q, K, V):
+    """One query row against its visible keys: q [D], K, V [t+1, D] (float64) -> [D].  Per head: softmax of
+    q.k / sqrt(HD) over the keys, then the weighted sum of the values."""
+    out = np.empty(D)
+    for h in range(HEADS):
+        sl = slice(h * HD, (h + 1) * HD)
+        s = K[:, sl] @ q[sl] / np.sqrt(HD)
+        p = np.exp(s - s.max())
+        out[sl] = (p / p.sum()) @ V[:, sl]
+    return out
 
 
-def _fp8_block(jf, L, x):
-    """FP8 branch y of one block (the residual is added by the caller)."""
-    xq, xs, _ = jf.rmsnorm_quantize(x, L["w_nm"], EPS)
-    gu = jf.gemm_fwd(xq, xs, L["gq"], L["gs"])
-    hq, hs = jf.swiglu_quantize(gu)
-    return jf.gemm_fwd(hq, hs, L["dq"], L["ds"])
+def _attention(qkv_rows, cache, start):
+    """qkv_rows: bf16 [m, 3D] for tokens start .. start+m-1; cache: dict of K, V float64 lists (appended here).
+    Returns the attention output rows as bf16 [m, D]."""
+    import torch
+    a = qkv_rows.float().cpu().numpy().astype(np.float64)
+    outs = []
+    for i in range(a.shape[0]):
+        cache["K"].append(a[i, D:2 * D])
+        cache["V"].append(a[i, 2 * D:])
+        t = start + i
+        outs.append(_attn_row(a[i, :D], np.array(cache["K"][:t + 1]), np.array(cache["V"][:t + 1])))
+    return torch.from_numpy(np.array(outs, dtype=np.float32)).to("cuda").to(torch.bfloat16)
 
 
-def _bf16_block(L, x):
+# --------------------------------------------------------------------------------------------- blocks
+
+def _fp8_block(jf, L, x, cache, start):
+    import torch
+    xq, xs, _ = jf.rmsnorm_quantize(x, L["n1"], EPS)
+    qkv = jf.gemm_fwd(xq, xs, L["qkv_q"], L["qkv_s"])
+    att = _attention(qkv, cache, start)
+    aq, as_ = jf.quantize_rows(att)
+    h = (x.float() + jf.gemm_fwd(aq, as_, L["o_q"], L["o_s"]).float()).to(torch.bfloat16)
+    hq, hs, _ = jf.rmsnorm_quantize(h, L["n2"], EPS)
+    gu = jf.gemm_fwd(hq, hs, L["gu_q"], L["gu_s"])
+    sq, ss = jf.swiglu_quantize(gu)
+    return (h.float() + jf.gemm_fwd(sq, ss, L["dn_q"], L["dn_s"]).float()).to(torch.bfloat16)
+
+
+def _rmsnorm_ref(x, w):
     import torch
     xf = x.float()
-    n = (xf * torch.rsqrt(xf.pow(2).mean(dim=1, keepdim=True) + EPS) * L["w_nm"].float()).to(torch.bfloat16)
-    gu = (n.float() @ L["w_gu"].float().t()).to(torch.bfloat16)
+    return (xf * torch.rsqrt(xf.pow(2).mean(dim=1, keepdim=True) + EPS) * w.float()).to(torch.bfloat16)
+
+
+def _mm(a, w):
+    import torch
+    return (a.float() @ w.float().t()).to(torch.bfloat16)
+
+
+def _bf16_block(L, x, cache, start):
+    import torch
+    qkv = _mm(_rmsnorm_ref(x, L["n1"]), L["w_qkv"])
+    h = (x.float() + _mm(_attention(qkv, cache, start), L["w_o"]).float()).to(torch.bfloat16)
+    gu = _mm(_rmsnorm_ref(h, L["n2"]), L["w_gu"])
     g, u = gu.float().chunk(2, dim=-1)
-    h = (torch.nn.functional.silu(g) * u).to(torch.bfloat16)
-    return h.float() @ L["w_dn"].float().t()
+    act = (torch.nn.functional.silu(g) * u).to(torch.bfloat16)
+    return (h.float() + _mm(act, L["w_dn"]).float()).to(torch.bfloat16)
 
 
-def _fp8_stack(jf, layers, x):
-    outs = []
-    for L in layers:
-        x = (x.float() + _fp8_block(jf, L, x).float()).to(x.dtype)
-        outs.append(x)
-    return outs
-
-
-def _bf16_stack(layers, x):
-    outs = []
-    for L in layers:
-        x = (x.float() + _bf16_block(L, x)).to(x.dtype)
-        outs.append(x)
-    return outs
+def _run_fp8(jf, layers, x0, chunk):
+    """Hidden states [layer][token] of the stack fed `chunk` tokens per call (S = prefill, 1 = decode)."""
+    import torch
+    caches = [{"K": [], "V": []} for _ in layers]
+    outs = [[] for _ in layers]
+    for start in range(0, S, chunk):
+        x = x0[start:start + chunk].contiguous()
+        for li, L in enumerate(layers):
+            x = _fp8_block(jf, L, x, caches[li], start)
+            outs[li].append(x)
+    torch.cuda.synchronize()
+    return [torch.cat(o).view(torch.int16).cpu().numpy() for o in outs]
 
 
 def test_decode_and_prefill_hidden_states_are_bitwise_equal(stack):
-    import torch
     jf, layers, x0 = stack
-    prefill = _fp8_stack(jf, layers, x0)
-    batch = _fp8_stack(jf, layers, x0[32:64].contiguous())
-    singles = {t: _fp8_stack(jf, layers, x0[t:t + 1].contiguous()) for t in (0, 33, 95)}
-    torch.cuda.synchronize()
-    for depth in range(LAYERS):
-        full = prefill[depth].view(torch.int16)
-        assert torch.equal(batch[depth].view(torch.int16), full[32:64]), f"decode batch, depth {depth}"
-        for t, outs in singles.items():
-            assert torch.equal(outs[depth].view(torch.int16)[0], full[t]), f"token {t}, depth {depth}"
+    prefill = _run_fp8(jf, layers, x0, S)
+    for chunk in (32, 1):
+        print(f"unified flow: {S // chunk} calls of M = {chunk} against one prefill of M = {S}", flush=True)
+        dec = _run_fp8(jf, layers, x0, chunk)
+        for depth in range(LAYERS):
+            diff = np.flatnonzero((dec[depth] != prefill[depth]).any(axis=1))
+            assert diff.size == 0, f"M = {chunk}: tokens {diff[:8]} differ at depth {depth}"
 
 
 def test_fp8_block_error_against_bf16(stack):
-    """Each block fed the same input on both sides (teacher forcing): the FP8 block's output branch y differs
-    from the bf16 one by the quantization error of two GEMMs, a few percent in relative Frobenius norm (E4M3
-    keeps 3 fraction bits: a relative rounding error of at most 2^-4 per operand element, about 2^-4 / sqrt(3)
-    in rms), and that error does not grow with depth.  Run free, a random stack amplifies perturbations, so
-    the end-to-end distance grows with depth; it is printed, not bounded."""
+    """Each block fed the same input on both sides (teacher forcing): the FP8 block's residual update differs
+    from the bf16 one by the quantization error of its FP8 linears, a few percent in relative Frobenius norm
+    (E4M3 keeps 3 fraction bits: a relative rounding error of at most 2^-4 per operand element), and that
+    error does not grow with depth.  Run free, the end-to-end distance is printed, not bounded."""
     import torch
     jf, layers, x0 = stack
     per_block = []
     x = x0
     for L in layers:
-        y8, y_r = _fp8_block(jf, L, x).float(), _bf16_block(L, x)
-        per_block.append(float((y8 - y_r).norm() / y_r.norm()))
-        x = (x.float() + y_r).to(x.dtype)                              # continue on the bf16 trajectory
-    free = [float((a.float() - b.float()).norm() / b.float().norm())
-            for a, b in zip(_fp8_stack(jf, layers, x0), _bf16_stack(layers, x0))]
+        y8 = _fp8_block(jf, L, x, {"K": [], "V": []}, 0).float() - x.float()
+        yr = _bf16_block(L, x, {"K": [], "V": []}, 0).float() - x.float()
+        per_block.append(float((y8 - yr).norm() / yr.norm()))
+        x = (x.float() + yr).to(torch.bfloat16)                        # continue on the bf16 trajectory
+    x8, xr = x0, x0
+    free = []
+    for L in layers:
+        x8 = _fp8_block(jf, L, x8, {"K": [], "V": []}, 0)
+        xr = _bf16_block(L, xr, {"K": [], "V": []}, 0)
+        free.append(float((x8.float() - xr.float()).norm() / xr.float().norm()))
     print("per-block relative error (teacher-forced):", [f"{r:.3e}" for r in per_block], flush=True)
     print("free-running relative distance by depth:", [f"{r:.3e}" for r in free], flush=True)
     assert all(np.isfinite(per_block)) and all(np.isfinite(free))
