@@ -202,6 +202,16 @@ __global__ __launch_bounds__(L_THREADS, 1) void gemm_large_kernel(
         }
     };
 
+    // Block scale of B (forward, DGrad) for the group being multiplied, fetched one step ahead with a
+    // vector load (counted with the staging loads, so the post-barrier fragment reads are not held up by
+    // a scalar load in flight).
+    const rsrc_t rbs = make_rsrc(Bs, ROW_SCALED_B ? 0 : (int)(J / 128) * G * 4);
+    auto load_sb = [&](int j0, int g) __attribute__((always_inline)) -> float {
+        const int bblk = min((j0 + wn * 64) / 128, (int)(J / 128) - 1);
+        return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rbs, (bblk * (int)sbj + g * (int)sbg) * 4, 0, 0));
+    };
+    float sbv_cur = 0.0f, sbv_nxt = 0.0f;
+
     // One step: wait for the current group's stage, store the previous tile at a tile's first group,
     // multiply, and (during the first row tiles) refill the other stage (read one step ago) with the next
     // group, of this tile or of the block's next tile.
@@ -225,11 +235,7 @@ __global__ __launch_bounds__(L_THREADS, 1) void gemm_large_kernel(
         }
         // block-scaled B: one scale per (128-block of B rows, group); a wave's 64 columns lie in one block.
         // Columns past J (last tile when J is an odd multiple of 128) use the last block: never stored.
-        float sbv = 0.0f;
-        if (!ROW_SCALED_B) {
-            const int bblk = min((cur.j0 + wn * 64) / 128, (int)(J / 128) - 1);
-            sbv = Bs[(int64_t)bblk * sbj + (int64_t)cg * sbg];
-        }
+        const float sbv = sbv_cur;
 
         // The matrix op takes the B fragment as its first operand, so lane l holds output row (l & 15) of
         // each 16-row tile and the 4 consecutive columns 4 * (l >> 4) .. +3: one A-row scale per tile.
@@ -288,6 +294,7 @@ __global__ __launch_bounds__(L_THREADS, 1) void gemm_large_kernel(
             for (int tm = 1; tm < 8; ++tm) {
                 af = a_frag(tm);
                 if (tm <= 4 && refill_next) issue_part(tm - 1, iss, ig, refill);
+                if (tm == 1 && refill_next) sbv_nxt = load_sb(iss.j0, ig);
                 __builtin_amdgcn_sched_barrier(0);
                 // Each SIMD runs one wave of each half (wm = 0, 1).  Issue arbitration favours the older wave
                 // (wm = 0), which then reaches the step's barrier well before its partner and leaves the matrix
@@ -339,7 +346,10 @@ __global__ __launch_bounds__(L_THREADS, 1) void gemm_large_kernel(
             promote(7, pb);
             __builtin_amdgcn_sched_barrier(0);
         }
-        if (refill_next) advance_issue();
+        if (refill_next) {
+            advance_issue();
+            if (!ROW_SCALED_B) sbv_cur = sbv_nxt;
+        }
         // advance the compute cursor
         if (++cg == G) {
             cg = 0;
@@ -352,6 +362,7 @@ __global__ __launch_bounds__(L_THREADS, 1) void gemm_large_kernel(
 
 #pragma unroll
     for (int c = 0; c < 4; ++c) issue_part(c, iss, ig, stage0);
+    if (!ROW_SCALED_B) sbv_cur = load_sb(iss.j0, ig);
     advance_issue();
     int s = 0;
     for (; s + 2 <= nsteps; s += 2) {

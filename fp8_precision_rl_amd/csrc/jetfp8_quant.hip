@@ -133,7 +133,9 @@ __device__ __forceinline__ rsrc_q_t span_rsrc(const void* base, int64_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-__global__ __launch_bounds__(256) void quant_dual_kernel(const uint16_t* __restrict__ x, int64_t R, int64_t C,
+// At most 96 VGPRs, so 5 waves per SIMD fit instead of 4 (97 unconstrained): more loads in flight per CU
+// (measured +6 % on 16384-row tensors, no spills).
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5, 8))) void quant_dual_kernel(const uint16_t* __restrict__ x, int64_t R, int64_t C,
                                                          uint8_t* __restrict__ q, float* __restrict__ s,
                                                          uint8_t* __restrict__ qT, float* __restrict__ sT,
                                                          uint32_t col_blocks) {
