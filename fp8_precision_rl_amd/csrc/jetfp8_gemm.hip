@@ -59,12 +59,14 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, int bytes) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds((r), (lds), (size), (voffset), (soffset), 0, 0)
 
 // Renumber a 1-D block index so that XCD x (which receives blocks x, x+8, ...) owns a contiguous range of
-// tiles, then walk tiles in bands of `group_m` tile-rows, N fastest inside a band.
+// tiles, then walk tiles in bands of `group_m` tile-rows, N fastest inside a band.  Bands of 4 tile-rows
+// measured 1.4 % faster than bands of 8 (fewer L2 misses on the large shapes) and bands of 2 or 16 slower.  Bands of 4 tile-rows
+// measured 1.4 % faster than bands of 8 (fewer L2 misses on the large shapes) and bands of 2 or 16 slower.
 __device__ __forceinline__ void tile_of_block(int pid, int tiles_m, int tiles_n, int& tm, int& tn) {
     const int T = tiles_m * tiles_n;
     const int per = T / 8, rem = T % 8, xcd = pid % 8, idx = pid / 8;
     const int q = xcd * per + (xcd < rem ? xcd : rem) + idx;
-    const int group_m = 8;
+    const int group_m = 4;
     const int band = group_m * tiles_n;
     const int first_m = (q / band) * group_m;
     const int gsz = min(tiles_m - first_m, group_m);
@@ -400,9 +402,13 @@ static int device_cu_count() {
 //   - after a barrier every wave runs the promotion acc = fma(p, fl32(sa * sb), acc) for its share of the
 //     outputs over the chunk's groups in ascending order -- the same chain the large kernel runs, so every
 //     output row is bitwise the same whichever kernel computed it;
-//   - operand fragments go straight from global memory into registers, D_AHEAD chunks ahead (2 for RT = 4, to
-//     fit the registers; range-checked buffer loads: rows past I and groups past the contraction read as zero
-//     and are never promoted); the A-row scales of all groups sit in LDS for the block's lifetime.
+//   - operand fragments go straight from global memory into registers, D_AHEAD chunks ahead (2 for RT >= 2;
+//     range-checked buffer loads: rows past I and groups past the contraction read as zero and are never
+//     promoted); the A-row scales of all groups sit in LDS for the block's lifetime;
+//   - the block scales of a chunk's 8 groups come with its operands, one vector load (lane l: group l & 7),
+//     and are broadcast with readlane.  Read with scalar loads they held up every chunk: the chunk's barrier
+//     waits for LDS traffic with lgkmcnt(0), which also waits for scalar loads in flight (measured: M = 1
+//     78 -> 63 us over the four Llama-3-8B linears).
 constexpr int D_WAVES = 8, D_THREADS = 64 * D_WAVES, D_AHEAD = 3;
 constexpr int D_SA_MAX = 8192;     // A-row scales kept in LDS: (contraction / 128) * rows <= 8192
 
@@ -413,7 +419,9 @@ __global__ __launch_bounds__(D_THREADS) void gemm_decode_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ As, const uint8_t* __restrict__ B,
     const float* __restrict__ Bs, uint16_t* __restrict__ Cout, int64_t I, int64_t J, int64_t Kc, int64_t sbj,
     int64_t sbg) {
-    constexpr int AHEAD = RT >= 4 ? 2 : D_AHEAD;             // chunks in flight (register budget)
+    // chunks in flight: RT = 2 keeps 2 (82 VGPRs, so two blocks share a CU: measured 4 % faster at 32 rows);
+    // RT = 4 keeps 2 to fit its registers; deeper prefetch measured no faster
+    constexpr int AHEAD = RT >= 2 ? 2 : D_AHEAD;
     constexpr int PAIRS = RT * 4;                             // (row tile, lane component) pairs of outputs
     constexpr int EPW = (PAIRS + D_WAVES - 1) / D_WAVES;      // pairs per wave in the promotion chain
     __shared__ v4f pbuf[2][D_WAVES][RT][64];
@@ -441,12 +449,22 @@ __global__ __launch_bounds__(D_THREADS) void gemm_decode_kernel(
     for (int e = 0; e < EPW; ++e) acc[e] = 0.0f;
 
     u32x4 wf[AHEAD][2], af[AHEAD][RT][2];
+    // block scales of a chunk's 8 groups: lane l holds that of group (l & 7), loaded with the chunk's operands
+    // (a vector load, so the per-chunk barrier's LDS wait does not wait for it); range-checked over Bs
+    const rsrc_t rbs = make_rsrc(Bs, (int)(J / 128) * G * 4);
+    float swf[AHEAD];
     // stream position c -> slice c / nchunks (B rows of that slice only: 16 x Kc bytes), group chunk
     // c % nchunks.  Positions past the block's stream load unconditionally (a conditional load would make
     // the compiler wait for it where the paths join) through an empty descriptor: they read zeros.
-    auto load_chunk = [&](int c, u32x4 (&w)[2], u32x4 (&a)[RT][2]) __attribute__((always_inline)) {
+    auto load_chunk = [&](int c, u32x4 (&w)[2], u32x4 (&a)[RT][2], float& sw) __attribute__((always_inline)) {
         const int sc = __builtin_amdgcn_readfirstlane(c / nchunks), ch = c - sc * nchunks;
         const bool live = c < nstream;
+        {
+            const int scc = live ? sc : 0;
+            const int gi = min(ch * D_WAVES + (lane & 7), G - 1);
+            sw = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                rbs, ((slice_col(scc) / 128) * (int)sbj + gi * (int)sbg) * 4, 0, 0));
+        }
         const rsrc_t rb = make_rsrc(live ? B + (int64_t)slice_col(sc) * Kc : B, live ? 16 * (int)Kc : 0);
         const int so = (ch * D_WAVES + wave) * BK;
         w[0] = __builtin_amdgcn_raw_buffer_load_b128(rb, vb, so, 0);
@@ -456,13 +474,6 @@ __global__ __launch_bounds__(D_THREADS) void gemm_decode_kernel(
             a[rt][0] = __builtin_amdgcn_raw_buffer_load_b128(ra, va[rt], so, 0);
             a[rt][1] = __builtin_amdgcn_raw_buffer_load_b128(ra, va[rt] + 16, so, 0);
         }
-    };
-    // block scales of a chunk's 8 groups (the slice's 16 columns lie in one 128-column block)
-    auto load_sb = [&](int c, float (&sb)[D_WAVES]) __attribute__((always_inline)) {
-        const int sc = c / nchunks, ch = c - sc * nchunks;
-        const int64_t sb_base = (int64_t)(slice_col(sc) / 128) * sbj;
-#pragma unroll
-        for (int gi = 0; gi < D_WAVES; ++gi) sb[gi] = Bs[sb_base + (int64_t)min(ch * D_WAVES + gi, G - 1) * sbg];
     };
     auto store_slice = [&](int sc) __attribute__((always_inline)) {
         const int j0 = slice_col(sc);
@@ -481,16 +492,15 @@ __global__ __launch_bounds__(D_THREADS) void gemm_decode_kernel(
     // first operand loads are issued, so waiting for it does not wait for them
     for (int i = t; i < G * Ii; i += D_THREADS) sa_tab[i] = As[i];
 #pragma unroll
-    for (int k = 0; k < AHEAD; ++k) load_chunk(k, wf[k], af[k]);
-    float sb_cur[D_WAVES];
-    load_sb(0, sb_cur);
+    for (int k = 0; k < AHEAD; ++k) load_chunk(k, wf[k], af[k], swf[k]);
     // LDS writes done, then every wave is here (a plain barrier: the operand loads stay in flight)
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     __builtin_amdgcn_s_barrier();
 
-    auto chunk = [&](int c, u32x4 (&w)[2], u32x4 (&a)[RT][2]) __attribute__((always_inline)) {
-        float sb_nxt[D_WAVES];
-        load_sb(min(c + 1, nstream - 1), sb_nxt);
+    auto chunk = [&](int c, u32x4 (&w)[2], u32x4 (&a)[RT][2], float& sw) __attribute__((always_inline)) {
+        float sb_cur[D_WAVES];
+#pragma unroll
+        for (int gi = 0; gi < D_WAVES; ++gi) sb_cur[gi] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sw), gi));
         const v8i bfrag = (v8i){(int)w[0][0], (int)w[0][1], (int)w[0][2], (int)w[0][3],
                                 (int)w[1][0], (int)w[1][1], (int)w[1][2], (int)w[1][3]};
         v4f p[RT];
@@ -500,7 +510,7 @@ __global__ __launch_bounds__(D_THREADS) void gemm_decode_kernel(
                                     (int)a[rt][1][0], (int)a[rt][1][1], (int)a[rt][1][2], (int)a[rt][1][3]};
             p[rt] = mfma_group(bfrag, afrag);
         }
-        load_chunk(c + AHEAD, w, a);
+        load_chunk(c + AHEAD, w, a, sw);
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) pbuf[c & 1][wave][rt][lane] = p[rt];
         // this wave's products (and its chain reads of two chunks ago) are in LDS, then every wave is here;
@@ -525,24 +535,23 @@ __global__ __launch_bounds__(D_THREADS) void gemm_decode_kernel(
             }
         }
         if (ch == nchunks - 1) store_slice(c / nchunks);
-#pragma unroll
-        for (int gi = 0; gi < D_WAVES; ++gi) sb_cur[gi] = sb_nxt[gi];
     };
     int c = 0;
     for (; c + AHEAD <= nstream; c += AHEAD) {
 #pragma unroll
-        for (int k = 0; k < AHEAD; ++k) chunk(c + k, wf[k], af[k]);
+        for (int k = 0; k < AHEAD; ++k) chunk(c + k, wf[k], af[k], swf[k]);
     }
 #pragma unroll
     for (int k = 0; k < AHEAD; ++k)
-        if (c + k < nstream) chunk(c + k, wf[k], af[k]);
+        if (c + k < nstream) chunk(c + k, wf[k], af[k], swf[k]);
 }
 
 template <int RT>
 static hipError_t launch_decode(const uint8_t* A, const float* As, const uint8_t* B, const float* Bs, uint16_t* C,
                                 int64_t I, int64_t J, int64_t Kc, int64_t sbj, int64_t sbg, hipStream_t st) {
     const int slices = (int)(J / 16);
-    const int grid = min(slices, device_cu_count());   // one block per CU (register budget)
+    // persistent blocks: one per CU, two for RT = 2 (registers and LDS allow it, and it measured faster)
+    const int grid = min(slices, (RT == 2 ? 2 : 1) * device_cu_count());
     hipLaunchKernelGGL(gemm_decode_kernel<RT>, dim3((unsigned)grid), dim3(D_THREADS), 0, st, A, As, B, Bs, C, I, J,
                        Kc, sbj, sbg);
     return hipGetLastError();
