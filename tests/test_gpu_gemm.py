@@ -145,3 +145,33 @@ def test_repeat_runs_are_bitwise_identical(jf):
     outs = [dev_to_bits(jf.linear_forward(x, wq, ws)[0]) for _ in range(3)]
     torch.cuda.synchronize()
     assert all(np.array_equal(outs[0], o) for o in outs[1:])
+
+
+@pytest.mark.parametrize("m_small", [1, 17, 33])
+def test_decode_ragged_chunks_many_slices(jf, orc, m_small):
+    """Small-M kernel (1, 2 and 4 row tiles) on a contraction of 11 groups (a full chunk of 8 and a partial
+    one of 3) and 520 column slices (more than the persistent blocks, so the operand stream crosses slice
+    boundaries): forward and DGrad rows are bitwise equal to the same rows from the large-tile kernel, and the
+    forward matches the oracle within the stated tolerance."""
+    import torch
+    big, n_wide, k_ragged = 300, 8320, 1408
+    xb, wb = _x(big, k_ragged, 71), _w(n_wide, k_ragged, 72)
+    wq, ws, _ = jf.quantize_blocks(bits_to_dev(wb))
+    x = bits_to_dev(xb)
+    y_big, _ = jf.linear_forward(x, wq, ws)
+    y_small, _ = jf.linear_forward(x[:m_small].contiguous(), wq, ws)
+    # DGrad: the contraction (N) is the ragged one, the output columns (K) the wide one
+    dyb, w2b = _dy(big, k_ragged, 73), _w(k_ragged, n_wide, 74)
+    w2q, w2s, w2qT = jf.quantize_blocks(bits_to_dev(w2b))
+    dyq, dys = jf.quantize_rows(bits_to_dev(dyb))
+    dx_big = jf.gemm_dgrad(dyq, dys, w2qT, w2s)
+    dyq_s, dys_s = jf.quantize_rows(bits_to_dev(dyb[:m_small]))
+    dx_small = jf.gemm_dgrad(dyq_s, dys_s, w2qT, w2s)
+    torch.cuda.synchronize()
+    assert np.array_equal(dev_to_bits(y_small), dev_to_bits(y_big)[:m_small])
+    assert np.array_equal(dev_to_bits(dx_small), dev_to_bits(dx_big)[:m_small])
+    oxq, oxs = orc.quantize_rows(xb[:m_small])
+    owq, ows = orc.quantize_blocks(wb)
+    m, e = _report(f"decode fwd {m_small}x{n_wide}x{k_ragged}", dev_to_bits(y_small),
+                   orc.gemm_fwd(oxq, oxs, owq, ows, mode=orc.MFMA), orc.gemm_fwd(oxq, oxs, owq, ows, mode=orc.EXACT))
+    _assert_tol("decode fwd", m, e)
