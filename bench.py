@@ -50,6 +50,12 @@ def parse():
     p.add_argument("--producers", action="store_true",
                    help="instead of the GEMM step, time the fused producers of one layer (2 RMSNorm -> 1x128 and "
                         "1 SwiGLU -> 1x128 at the workload's token count) and print their own JSON line")
+    p.add_argument("--decode", action="store_true",
+                   help="instead of the training step, time rollout decode (workload llama3_8b_decode_m32: per step the "
+                        "tokens' 1x128 activation quantization and the forward GEMM of the four linears against FP8 "
+                        "weights quantized beforehand) and print its own JSON line")
+    p.add_argument("--decode-rows", type=int, default=None,
+                   help="token rows of a decode step (default: the workload's 32)")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="first run a 1 GiB device-to-device copy (known bytes) to scale rocprofv3 byte counters")
     return p.parse_args()
@@ -321,6 +327,127 @@ def run_producers(args, torch, jf, workloads, wl):
     print(json.dumps(out), flush=True)
 
 
+DECODE_COPIES = 3     # weight copies cycled by --decode: 3 x 218 MB of FP8 codes, beyond the 256 MB MALL
+
+
+def decode_gemm_bytes(M, N, K):
+    """Algorithmic bytes of one decode GEMM launch: FP8 weight codes and block scales, the activation codes and
+    row scales, the bf16 output."""
+    return N * K + (N // 128) * (K // 128) * 4 + M * K + (K // 128) * M * 4 + 2 * M * N
+
+
+def decode_cpu_baseline(wl, M, workloads):
+    """The oracle (unchanged) on the decode step itself, all four linears at M rows: 1x128 quantization of the
+    activations and the forward GEMM (MFMA mode).  The weights are quantized by the oracle beforehand, outside
+    the timed region, as the GPU path's are."""
+    import oracle
+    threads = oracle.default_threads()
+    byts, elapsed = 0, 0.0
+    for i, (name, K, N) in enumerate(wl.linears):
+        h = workloads.host_linear(wl, i, M=M)
+        wq, ws = oracle.quantize_blocks(h["w"], threads)
+        t0 = time.perf_counter()
+        xq, xs = oracle.quantize_rows(h["x"], threads)
+        oracle.gemm_fwd(xq, xs, wq, ws, mode=oracle.MFMA, threads=threads)
+        elapsed += time.perf_counter() - t0
+        byts += decode_gemm_bytes(M, N, K) + (2 * M * K + M * K + (K // 128) * M * 4)
+    return {"value": round(byts / elapsed / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"the whole decode step ({M} rows, four linears: activation quantization + forward GEMM) "
+                      f"in {elapsed:.1f} s", "seconds": elapsed}
+
+
+def decode_traffic(path=os.path.join(ROOT, "profiles", "decode_traffic.json")):
+    """HBM bytes per decode GEMM launch recorded from rocprofv3 FETCH_SIZE / WRITE_SIZE runs of the 32-row decode
+    workload, or None when absent or taken on a different kernel source."""
+    try:
+        tj = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    if tj.get("kernel_source_sha256") != source_digest():
+        return None
+    return tj.get("decode_bytes_per_launch")
+
+
+def run_decode(args, torch, jf, workloads):
+    wl = workloads.WORKLOADS["llama3_8b_decode_m32"]
+    M = args.decode_rows or wl.M
+    u8, f32, bf = torch.uint8, torch.float32, torch.bfloat16
+    lin = []
+    for i, (name, K, N) in enumerate(wl.linears):
+        d = workloads.device_linear(wl, i, M=M)
+        dev = d["x"].device
+        copies = []
+        for _ in range(DECODE_COPIES):
+            wq = torch.empty((N, K), dtype=u8, device=dev)
+            ws = torch.empty((N // 128, K // 128), dtype=f32, device=dev)
+            jf.jetfp8_quantize(d["w"], N, K, jf.BLOCKS_128x128, wq, ws, None)
+            copies.append((wq, ws))
+        del d["w"]
+        lin.append(dict(name=name, K=K, N=N, x=d["x"], copies=copies,
+                        xq=torch.empty((M, K), dtype=u8, device=dev), xs=torch.empty((K // 128, M), dtype=f32, device=dev),
+                        y=torch.empty((M, N), dtype=bf, device=dev)))
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+
+    def step(c, ev=None):
+        for L in lin:
+            K, N = L["K"], L["N"]
+            wq, ws = L["copies"][c % DECODE_COPIES]
+            jf.jetfp8_quantize(L["x"], M, K, jf.ROWS_1x128, L["xq"], L["xs"], None, st)
+            a = b = None
+            if ev is not None:
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(st)
+            jf.jetfp8_gemm_fwd(L["xq"], L["xs"], wq, ws, L["y"], M, N, K, st)
+            if ev is not None:
+                b.record(st)
+                ev.append((L["name"], decode_gemm_bytes(M, N, K), a, b))
+
+    for c in range(args.warmup):
+        step(c)
+    torch.cuda.synchronize()
+    ev = []
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(st)
+    for c in range(args.steps):
+        step(c, ev)
+    t1.record(st)
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / args.steps
+    step_bytes = sum(decode_gemm_bytes(M, L["N"], L["K"]) + 3 * M * L["K"] + (L["K"] // 128) * M * 4 for L in lin)
+    gemm_ms = sum(a.elapsed_time(b) for _, _, a, b in ev)
+    gemm_bytes = sum(n for _, n, _, _ in ev)
+    per = {}
+    for name, n, a, b in ev:
+        per.setdefault(name, [0.0, 0, n])
+        per[name][0] += a.elapsed_time(b)
+        per[name][1] += 1
+    rt = 1 if M <= 16 else (2 if M <= 32 else 4)
+    out = {
+        "metric": "rollout decode (FP8 activation quantize + forward GEMM over FP8 weights), algorithmic GB/s",
+        "value": round(step_bytes / (ms_step * 1e-3) / 1e9, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3 (fp32 accumulate, bf16 out)",
+        "data": f"synthetic (seeded torch generator on device: X~N(0,1) with 0.1% outlier channels x50, "
+                f"W~N(0,0.02^2)); {DECODE_COPIES} weight copies cycled past the 256 MB MALL",
+        "config": {"workload": wl.name if M == wl.M else f"llama3_8b_decode_m{M}", "tokens": M,
+                   "linears": [{"name": n, "K": K, "N": N} for n, K, N in wl.linears],
+                   "step": "per linear: X rows quant (1x128), fwd GEMM against FP8 weights quantized beforehand"},
+        "roofline": {"bound": "hbm", "kernel": f"gemm_decode_kernel<{rt}>",
+                     "achieved": round(gemm_bytes / (gemm_ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gemm_bytes / (gemm_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "traffic": decode_traffic() if M == wl.M else None,
+                     "launches": len(ev), "mean_launch_us": round(1e3 * gemm_ms / len(ev), 2),
+                     "bytes_per_launch_mean": round(gemm_bytes / len(ev))},
+        "per_linear": {k: {"mean_launch_us": round(1e3 * v[0] / v[1], 2),
+                           "gbs": round(v[2] / (v[0] / v[1] * 1e-3) / 1e9, 1)} for k, v in per.items()},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on the decode step", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = decode_cpu_baseline(wl, M, workloads)
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -340,6 +467,9 @@ def main():
         copy_calibration(torch)
     if args.producers:
         run_producers(args, torch, jf, workloads, wl)
+        return
+    if args.decode:
+        run_decode(args, torch, jf, workloads)
         return
     layers = [Linear(wl, i, torch, workloads) for i in range(len(wl.linears))]
     torch.cuda.synchronize()
