@@ -118,8 +118,10 @@ __device__ __forceinline__ uint32_t swiglu_bf16_fast(float g, float u, bool& exa
 // ahead, left all blocks loading, then all computing, in step.)
 constexpr int RN_ROWS = 8, RN_WAVES = 8, RN_PASSES = RN_ROWS / RN_WAVES;
 
+// NCH = 8 (rows of 4096) is capped at 80 VGPRs (81 unconstrained), so 6 waves per SIMD fit instead of 5: measured
+// 12 % faster, no spills, the same bits.  The other widths are left to the compiler (a cap spills them).
 template <int NCH>
-__global__ __launch_bounds__(RN_WAVES * 64) void rmsnorm_quant_kernel(
+__global__ __launch_bounds__(RN_WAVES * 64) __attribute__((amdgpu_waves_per_eu(NCH == 8 ? 6 : 1, 8))) void rmsnorm_quant_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, int64_t R, int64_t C, float eps,
     uint8_t* __restrict__ q, float* __restrict__ s, float* __restrict__ rstd, uint16_t* __restrict__ y) {
     __shared__ float sc[NCH * 4][RN_ROWS];
@@ -192,6 +194,8 @@ __global__ __launch_bounds__(RN_WAVES * 64) void rmsnorm_quant_kernel(
 // are issued first (lanes past the last row or column load an in-bounds stand-in and store nothing).
 constexpr int SG_ROWS = 32, SG_COLS = 512, SG_WAVES = 8, SG_PASSES = SG_ROWS / SG_WAVES;
 
+// Not register-capped: at 64 VGPRs (8 waves per SIMD instead of 7) it spills 3 registers, and the scratch traffic
+// adds 10 % to its HBM bytes for a 1 % gain on the bench data.
 __global__ __launch_bounds__(SG_WAVES * 64) void swiglu_quant_kernel(const uint16_t* __restrict__ gu, int64_t R,
                                                                       int64_t F, uint8_t* __restrict__ q,
                                                                       float* __restrict__ s, uint16_t* __restrict__ h,
