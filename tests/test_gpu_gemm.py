@@ -175,3 +175,43 @@ def test_decode_ragged_chunks_many_slices(jf, orc, m_small):
     m, e = _report(f"decode fwd {m_small}x{n_wide}x{k_ragged}", dev_to_bits(y_small),
                    orc.gemm_fwd(oxq, oxs, owq, ows, mode=orc.MFMA), orc.gemm_fwd(oxq, oxs, owq, ows, mode=orc.EXACT))
     _assert_tol("decode fwd", m, e)
+
+
+def test_degenerate_groups_fwd_dgrad_wgrad(jf, orc):
+    """All-zero activation rows and groups (scale 0), an all-zero 128x128 weight block, negative zeros and
+    full-scale groups (every element +-amax) in the forward, DGrad and WGrad GEMMs on the large-tile and the
+    small-M kernels: outputs equal the oracle's (matrix-instruction mode) bit for bit, and rows whose
+    activations are all zero come out as +0."""
+    import torch
+    M, N, K = 200, 384, 512
+    x = np.random.default_rng(81).standard_normal((M, K)).astype(np.float32)
+    x[5] = 0.0                                   # an all-zero row
+    x[7, 128:256] = -0.0                         # a group of negative zeros
+    x[9, 256:384] = np.where(np.arange(128) % 2 == 0, 3.0, -3.0)   # every element at +-amax
+    x[:, 384:512][x[:, 384:512] < -1.0] = 0.0    # sparse tail groups
+    w = (np.random.default_rng(82).standard_normal((N, K)) * 0.02).astype(np.float32)
+    w[128:256, 0:128] = 0.0                      # an all-zero weight block
+    xb, wb = f32_to_bits(x), f32_to_bits(w)
+    dyb = f32_to_bits(np.where(np.arange(N) < 128, 0.0, np.random.default_rng(83).standard_t(3, (M, N)) * 1e-3)
+                      .astype(np.float32))       # dY's first 128 columns all zero (one zero group per row)
+    wq, ws, wqT = jf.quantize_blocks(bits_to_dev(wb))
+    owq, ows = orc.quantize_blocks(wb)
+    for m in (M, 24):                            # large-tile kernel, then the small-M kernel
+        y, _ = jf.linear_forward(bits_to_dev(xb[:m]), wq, ws)
+        dyq, dys = jf.quantize_rows(bits_to_dev(dyb[:m]))
+        dx = jf.gemm_dgrad(dyq, dys, wqT, ws)
+        torch.cuda.synchronize()
+        oxq, oxs = orc.quantize_rows(xb[:m])
+        odq, ods = orc.quantize_rows(dyb[:m])
+        assert np.array_equal(dev_to_bits(y), orc.gemm_fwd(oxq, oxs, owq, ows, mode=orc.MFMA)), m
+        assert np.array_equal(dev_to_bits(dx), orc.gemm_dgrad(odq, ods, owq, ows, mode=orc.MFMA)), m
+        assert not dev_to_bits(y)[5].any()
+    xqT, xsT = jf.quantize_cols_t(bits_to_dev(xb[:M // 128 * 128]))
+    dyqT, dysT = jf.quantize_cols_t(bits_to_dev(dyb[:M // 128 * 128]))
+    dw = jf.gemm_wgrad(dyqT, dysT, xqT, xsT)
+    torch.cuda.synchronize()
+    odc, odsc = orc.quantize_cols(dyb[:M // 128 * 128])
+    oxc, oxsc = orc.quantize_cols(xb[:M // 128 * 128])
+    got = dev_to_bits(dw)
+    assert np.array_equal(got, orc.gemm_wgrad(odc, odsc, oxc, oxsc, mode=orc.MFMA))
+    assert not got[:128].any()                   # dW rows of the all-zero dY columns
