@@ -140,7 +140,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5, 8))) voi
                                                          uint8_t* __restrict__ qT, float* __restrict__ sT,
                                                          uint32_t col_blocks) {
     __shared__ uint32_t red[4][16][4];
-    __shared__ uint32_t tcodes[128][33];     // [column][4-row word], odd pitch
+    // [column][4-row word]; a 36-word pitch keeps each row 16-byte aligned, so a lane's two code words go in as
+    // one 8-byte write and the transposed rows come out as 16-byte reads (measured 3.7 % faster than the odd
+    // 33-word pitch with 4-byte accesses)
+    __shared__ __attribute__((aligned(16))) uint32_t tcodes[128][36];
     const int t = threadIdx.x, lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int l16 = lane & 15, rs = lane >> 4, rb8 = 4 * wave + rs;
@@ -215,8 +218,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5, 8))) voi
         const uint32_t half = (j & 1) ? (cm[j >> 1] >> 16) : (cm[j >> 1] & 0xFFFFu);
         const GroupScale gs = make_group_scale(bf16_to_f32(half));
         const uint2 out = encode8(f, gs);
-        tcodes[8 * l16 + j][2 * rb8] = out.x;
-        tcodes[8 * l16 + j][2 * rb8 + 1] = out.y;
+        *reinterpret_cast<uint2*>(&tcodes[8 * l16 + j][2 * rb8]) = out;
         if (j == rs) col_scale_a = gs.s;
         if (j == rs + 4) col_scale_b = gs.s;
     }
@@ -233,8 +235,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5, 8))) voi
     const int to = oc * (int)R + 64 * hf;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-        const uint32_t* src = &tcodes[oc][16 * hf + 4 * k];
-        const u32x4_q o = {src[0], src[1], src[2], src[3]};
+        const uint4 w4 = *reinterpret_cast<const uint4*>(&tcodes[oc][16 * hf + 4 * k]);
+        const u32x4_q o = {w4.x, w4.y, w4.z, w4.w};
         __builtin_amdgcn_raw_buffer_store_b128(o, rqt, to + 16 * k, 0, 0);
     }
 }
@@ -251,7 +253,10 @@ __global__ __launch_bounds__(256) void quant_requant_cols_kernel(const uint8_t* 
                                                                  int64_t C, uint8_t* __restrict__ qT,
                                                                  float* __restrict__ sT, uint32_t col_blocks) {
     __shared__ uint32_t red[4][16][8];
-    __shared__ uint32_t tcodes[128][33];     // [column][4-row word], odd pitch
+    // [column][4-row word]; a 36-word pitch keeps each row 16-byte aligned, so a lane's two code words go in as
+    // one 8-byte write and the transposed rows come out as 16-byte reads (measured 3.7 % faster than the odd
+    // 33-word pitch with 4-byte accesses)
+    __shared__ __attribute__((aligned(16))) uint32_t tcodes[128][36];
     const int t = threadIdx.x, lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int l16 = lane & 15, rs = lane >> 4, rb8 = 4 * wave + rs;
@@ -309,8 +314,7 @@ __global__ __launch_bounds__(256) void quant_requant_cols_kernel(const uint8_t* 
         for (int i = 0; i < 8; ++i) f[i] = xv[i][j];
         const GroupScale gs = make_group_scale(__uint_as_float(m));
         const uint2 out = encode8(f, gs);
-        tcodes[8 * l16 + j][2 * rb8] = out.x;
-        tcodes[8 * l16 + j][2 * rb8 + 1] = out.y;
+        *reinterpret_cast<uint2*>(&tcodes[8 * l16 + j][2 * rb8]) = out;
         if (j == rs) col_scale_a = gs.s;
         if (j == rs + 4) col_scale_b = gs.s;
     }
@@ -325,8 +329,8 @@ __global__ __launch_bounds__(256) void quant_requant_cols_kernel(const uint8_t* 
     const int to = oc * (int)R + 64 * hf;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-        const uint32_t* src = &tcodes[oc][16 * hf + 4 * k];
-        const u32x4_q o = {src[0], src[1], src[2], src[3]};
+        const uint4 w4 = *reinterpret_cast<const uint4*>(&tcodes[oc][16 * hf + 4 * k]);
+        const u32x4_q o = {w4.x, w4.y, w4.z, w4.w};
         __builtin_amdgcn_raw_buffer_store_b128(o, rqt, to + 16 * k, 0, 0);
     }
 }
