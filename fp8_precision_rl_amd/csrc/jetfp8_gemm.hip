@@ -60,7 +60,6 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, int bytes) {
 
 // Renumber a 1-D block index so that XCD x (which receives blocks x, x+8, ...) owns a contiguous range of
 // tiles, then walk tiles in bands of `group_m` tile-rows, N fastest inside a band.  Bands of 4 tile-rows
-// measured 1.4 % faster than bands of 8 (fewer L2 misses on the large shapes) and bands of 2 or 16 slower.  Bands of 4 tile-rows
 // measured 1.4 % faster than bands of 8 (fewer L2 misses on the large shapes) and bands of 2 or 16 slower.
 __device__ __forceinline__ void tile_of_block(int pid, int tiles_m, int tiles_n, int& tm, int& tn) {
     const int T = tiles_m * tiles_n;
