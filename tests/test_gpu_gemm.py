@@ -1,22 +1,18 @@
 """GPU parity of the block-scaled FP8 GEMMs (forward, dgrad, wgrad) against the oracle, plus the
 kernel-level unified-flow property: an output row's bits do not depend on how many rows are computed.
 
-Tolerance (stated with the path): relative Frobenius error <= 1e-3 and max |error| <= 1e-2 * rms(out),
-comparing bf16 outputs with the oracle's bf16 outputs, where the oracle's per-group dot product follows the
-matrix instruction (MFMA mode).  Against the oracle's exact group sums (EXACT mode) the relative Frobenius
-error must stay within 1e-3, or within 1.25x the distance between the oracle's two modes on the same inputs:
-on heavy-tailed groups the instruction's own alignment (which the MFMA mode reproduces) alone can move the
-bf16 outputs by slightly more than 1e-3 from the exact sums.
+Tolerance: against the plain definition (the oracle's EXACT mode, each group's dot product the fp32 rounding
+of its exact sum), relative Frobenius error <= 1e-3 and max |error| <= 1e-2 * rms(out) over the outputs that
+are not single-bf16-ulp rounding flips (the raw max-abs, flips included, is printed).  Separately, as a
+hardware-model check, the outputs are bitwise equal to the oracle's matrix-instruction mode (see
+conftest.check_gemm_parity).
 """
 import numpy as np
 import pytest
 
-from conftest import bits_to_dev, compare_bf16, dev_to_bits, f32_to_bits
+from conftest import bits_to_dev, check_gemm_parity, dev_to_bits, f32_to_bits
 
 pytestmark = pytest.mark.gpu
-
-REL_FROB = 1e-3
-MAX_ABS = 1e-2
 
 
 @pytest.fixture(scope="module")
@@ -45,21 +41,6 @@ def _dy(M, N, seed):
     return f32_to_bits((rng.standard_t(3, (M, N)) * 1e-3).astype(np.float32))
 
 
-def _report(name, got, orc_ref_mfma, orc_ref_exact):
-    m = compare_bf16(got, orc_ref_mfma)
-    e = compare_bf16(got, orc_ref_exact)
-    e["model_vs_exact"] = compare_bf16(orc_ref_mfma, orc_ref_exact)["rel_frob"]
-    print(f"{name}: vs matrix-core model {m}; vs exact group sums {e}", flush=True)
-    return m, e
-
-
-def _assert_tol(name, m, e):
-    assert m["rel_frob"] <= REL_FROB and m["max_abs_over_rms"] <= MAX_ABS, (name, m)
-    # against the exact group sums: the bound, or no further than the matrix instruction's own rounding
-    # (as the model reproduces it) puts the oracle's two readings apart
-    assert e["rel_frob"] <= max(REL_FROB, 1.25 * e["model_vs_exact"]), (name, e)
-
-
 @pytest.mark.parametrize("M,N,K", [(64, 256, 512), (300, 384, 640), (1, 128, 128), (129, 256, 1024)])
 def test_forward_parity(jf, orc, M, N, K):
     import torch
@@ -70,9 +51,8 @@ def test_forward_parity(jf, orc, M, N, K):
     oxq, oxs = orc.quantize_rows(xb)
     owq, ows = orc.quantize_blocks(wb)
     got = dev_to_bits(y)
-    m, e = _report(f"fwd {M}x{N}x{K}", got, orc.gemm_fwd(oxq, oxs, owq, ows, mode=orc.MFMA),
+    check_gemm_parity(f"fwd {M}x{N}x{K}", got, orc.gemm_fwd(oxq, oxs, owq, ows, mode=orc.MFMA),
                    orc.gemm_fwd(oxq, oxs, owq, ows, mode=orc.EXACT))
-    _assert_tol("fwd", m, e)
 
 
 @pytest.mark.parametrize("M,N,K", [(64, 256, 512), (300, 384, 256)])
@@ -85,9 +65,8 @@ def test_dgrad_parity(jf, orc, M, N, K):
     torch.cuda.synchronize()
     odq, ods = orc.quantize_rows(dyb)
     owq, ows = orc.quantize_blocks(wb)
-    m, e = _report(f"dgrad {M}x{N}x{K}", dev_to_bits(dx), orc.gemm_dgrad(odq, ods, owq, ows, mode=orc.MFMA),
+    check_gemm_parity(f"dgrad {M}x{N}x{K}", dev_to_bits(dx), orc.gemm_dgrad(odq, ods, owq, ows, mode=orc.MFMA),
                    orc.gemm_dgrad(odq, ods, owq, ows, mode=orc.EXACT))
-    _assert_tol("dgrad", m, e)
 
 
 @pytest.mark.parametrize("M,N,K", [(256, 256, 512), (384, 128, 384)])
@@ -100,9 +79,8 @@ def test_wgrad_parity(jf, orc, M, N, K):
     torch.cuda.synchronize()
     odq, ods = orc.quantize_cols(dyb)
     oxq, oxs = orc.quantize_cols(xb)
-    m, e = _report(f"wgrad {M}x{N}x{K}", dev_to_bits(dw), orc.gemm_wgrad(odq, ods, oxq, oxs, mode=orc.MFMA),
+    check_gemm_parity(f"wgrad {M}x{N}x{K}", dev_to_bits(dw), orc.gemm_wgrad(odq, ods, oxq, oxs, mode=orc.MFMA),
                    orc.gemm_wgrad(odq, ods, oxq, oxs, mode=orc.EXACT))
-    _assert_tol("wgrad", m, e)
 
 
 def test_rows_are_bitwise_independent_of_M(jf):
@@ -172,9 +150,8 @@ def test_decode_ragged_chunks_many_slices(jf, orc, m_small):
     assert np.array_equal(dev_to_bits(dx_small), dev_to_bits(dx_big)[:m_small])
     oxq, oxs = orc.quantize_rows(xb[:m_small])
     owq, ows = orc.quantize_blocks(wb)
-    m, e = _report(f"decode fwd {m_small}x{n_wide}x{k_ragged}", dev_to_bits(y_small),
+    check_gemm_parity(f"decode fwd {m_small}x{n_wide}x{k_ragged}", dev_to_bits(y_small),
                    orc.gemm_fwd(oxq, oxs, owq, ows, mode=orc.MFMA), orc.gemm_fwd(oxq, oxs, owq, ows, mode=orc.EXACT))
-    _assert_tol("decode fwd", m, e)
 
 
 def test_degenerate_groups_fwd_dgrad_wgrad(jf, orc):

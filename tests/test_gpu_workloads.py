@@ -8,20 +8,22 @@ own, from the same seeded bf16 inputs:
   * an output element of a GEMM depends only on its row of A and its row of B, so each GEMM is compared on a
     block of sampled output rows x one 128-wide slab of output columns, the oracle quantizing just the operand
     rows and columns that block needs (128-aligned slabs keep the same groups and blocks).
-The sampled rows always include the first, the last and the row holding the largest |x| (or |dY|).
-Tolerance as in the small parity tests: relative Frobenius <= 1e-3 and max |error| <= 1e-2 * rms against the
-oracle's matrix-instruction model; against exact group sums, relative Frobenius <= 1e-3 or <= 1.25x the
-distance between the oracle's two modes on the same block (heavy-tailed dY groups at the 32B shapes).
+The sampled rows always include the first, the last and the row holding the largest |x| (or |dY|), plus 64
+rows at random.
+Tolerance as in the small parity tests (conftest.check_gemm_parity), against the oracle's exact group sums:
+max |error| <= 1e-2 * rms beyond single-ulp rounding flips for every sampled block (raw max-abs printed), and
+relative Frobenius <= 1e-3 for each GEMM over all of its sampled blocks together.  The relative Frobenius error
+of the full output is a property of the whole matrix; a block of a few rows is a noisy estimate of it, because
+the bf16 rounding flips that carry it (about 1.3 % of outputs, each worth 2^-8 to 2^-7 of its element) are
+few there and one large row can carry most of a small block's norm.  Bitwise equality with the oracle's
+matrix-instruction mode is the separate hardware-model check, per block.
 """
 import numpy as np
 import pytest
 
-from conftest import bits_to_dev, compare_bf16, dev_to_bits
+from conftest import bits_to_dev, check_gemm_parity, dev_to_bits
 
 pytestmark = pytest.mark.gpu
-
-REL_FROB = 1e-3
-MAX_ABS = 1e-2
 
 
 @pytest.fixture(scope="module")
@@ -33,19 +35,33 @@ def jf():
     return m
 
 
-def _check_gemm(name, got, ref_mfma, ref_exact):
-    m = compare_bf16(got, ref_mfma)
-    e = compare_bf16(got, ref_exact)
-    model_vs_exact = compare_bf16(ref_mfma, ref_exact)["rel_frob"]
-    print(f"{name}: vs matrix-core model {m}; vs exact group sums {e}; model vs exact {model_vs_exact:.3g}",
-          flush=True)
-    assert m["rel_frob"] <= REL_FROB and m["max_abs_over_rms"] <= MAX_ABS, (name, m)
-    # against the exact group sums: the bound, or no further than the matrix instruction's own rounding
-    # (as the model reproduces it) puts the oracle's two readings apart
-    assert e["rel_frob"] <= max(REL_FROB, 1.25 * model_vs_exact), (name, e, model_vs_exact)
+class GemmCheck:
+    """Collects the sampled blocks of one GEMM: each block is checked on its own (max-abs beyond single-ulp
+    flips against the exact group sums, bitwise equality with the matrix-instruction mode), and the relative
+    Frobenius error is asserted over all blocks together (finish())."""
+
+    def __init__(self, name):
+        self.name, self.got, self.mfma, self.exact = name, [], [], []
+
+    def add(self, what, got, ref_mfma, ref_exact):
+        from conftest import GEMM_MAX_ABS, compare_bf16
+        e = compare_bf16(got, ref_exact)
+        m = compare_bf16(got, ref_mfma)
+        print(f"{self.name} {what}: vs exact rel_frob={e['rel_frob']:.3e} max_abs/rms raw={e['max_abs_over_rms']:.3e} "
+              f"beyond-1ulp={e['max_abs_over_rms_beyond_1ulp']:.3e} (flips {e['one_ulp_flips']}/{got.size}); "
+              f"hardware model bit_match={m['bit_match']:.6f}", flush=True)
+        assert e["max_abs_over_rms_beyond_1ulp"] <= GEMM_MAX_ABS, (self.name, what, e)
+        assert m["bit_match"] == 1.0, (self.name, what, "hardware model (matrix-instruction group sums)", m)
+        self.got.append(got.ravel())
+        self.mfma.append(ref_mfma.ravel())
+        self.exact.append(ref_exact.ravel())
+
+    def finish(self):
+        check_gemm_parity(f"{self.name} (all sampled blocks)", np.concatenate(self.got), np.concatenate(self.mfma),
+                          np.concatenate(self.exact))
 
 
-def _rows(t, rng, extra=3):
+def _rows(t, rng, extra=64):
     """Sampled row indices of a device tensor: first, last, the row of the largest |value|, a few random."""
     import torch
     R, C = t.shape
@@ -119,11 +135,13 @@ def _forward_checks(jf, orc, d, rng, tag):
     nslabs = _slabs(N, rng)
     _quant_blocks_check(orc, w, wq, ws, wqT, nslabs, f"{tag} W")
     oxq, oxs = orc.quantize_rows(dev_to_bits(_take(x, rows)))
+    chk = GemmCheck(f"{tag} fwd ({rows.size} sampled rows)")
     for b in nslabs:
         owq, ows = orc.quantize_blocks(dev_to_bits(w[b * 128:(b + 1) * 128]))
         got = dev_to_bits(_take(y, rows)[:, b * 128:(b + 1) * 128])
-        _check_gemm(f"{tag} fwd rows {rows.tolist()} cols {b * 128}..", got,
-                    orc.gemm_fwd(oxq, oxs, owq, ows, mode=orc.MFMA), orc.gemm_fwd(oxq, oxs, owq, ows, mode=orc.EXACT))
+        chk.add(f"cols {b * 128}..", got, orc.gemm_fwd(oxq, oxs, owq, ows, mode=orc.MFMA),
+                orc.gemm_fwd(oxq, oxs, owq, ows, mode=orc.EXACT))
+    chk.finish()
     return wq, ws, wqT
 
 
@@ -167,23 +185,25 @@ def _backward_checks(jf, orc, d, wqT, ws, rng, tag):
 
     # DGrad: rows of dX x one 128-column slab of K; W's 128x128 blocks over that slab
     odq, ods = orc.quantize_rows(dev_to_bits(_take(dy, rows)))
+    chk = GemmCheck(f"{tag} dgrad ({rows.size} sampled rows)")
     for b in _slabs(K, rng):
         owq, ows = orc.quantize_blocks(dev_to_bits(w[:, b * 128:(b + 1) * 128].contiguous()))
         got = dev_to_bits(_take(dx, rows)[:, b * 128:(b + 1) * 128])
-        _check_gemm(f"{tag} dgrad rows {rows.tolist()} cols {b * 128}..", got,
-                    orc.gemm_dgrad(odq, ods, owq, ows, mode=orc.MFMA),
-                    orc.gemm_dgrad(odq, ods, owq, ows, mode=orc.EXACT))
+        chk.add(f"cols {b * 128}..", got, orc.gemm_dgrad(odq, ods, owq, ows, mode=orc.MFMA),
+                orc.gemm_dgrad(odq, ods, owq, ows, mode=orc.EXACT))
+    chk.finish()
 
     # WGrad: a 128x128 block of dW = (slab of N) x (slab of K); each needs its dY / X columns over all M
     nb = _slabs(N, rng)
     kb = _slabs(K, rng)
+    chk = GemmCheck(f"{tag} wgrad")
     for bn, bk in zip(nb, kb[::-1]):
         oyq, oys = orc.quantize_cols(dev_to_bits(dy[:, bn * 128:(bn + 1) * 128].contiguous()))
         oxq, oxs = orc.quantize_cols(dev_to_bits(x[:, bk * 128:(bk + 1) * 128].contiguous()))
         got = dev_to_bits(dw[bn * 128:(bn + 1) * 128, bk * 128:(bk + 1) * 128])
-        _check_gemm(f"{tag} wgrad block ({bn * 128}.., {bk * 128}..)", got,
-                    orc.gemm_wgrad(oyq, oys, oxq, oxs, mode=orc.MFMA),
-                    orc.gemm_wgrad(oyq, oys, oxq, oxs, mode=orc.EXACT))
+        chk.add(f"block ({bn * 128}.., {bk * 128}..)", got, orc.gemm_wgrad(oyq, oys, oxq, oxs, mode=orc.MFMA),
+                orc.gemm_wgrad(oyq, oys, oxq, oxs, mode=orc.EXACT))
+    chk.finish()
 
 
 def _release():
@@ -212,7 +232,7 @@ def test_decode_m32_full_rows_and_single_rows(jf, orc, lin):
     oxq, oxs = orc.quantize_rows(h["x"])
     owq, ows = orc.quantize_blocks(h["w"])
     assert np.array_equal(wq.cpu().numpy(), owq) and np.array_equal(ws.cpu().numpy(), ows)
-    _check_gemm(f"decode {h['name']} 32x{h['N']}x{h['K']}", got, orc.gemm_fwd(oxq, oxs, owq, ows, mode=orc.MFMA),
+    check_gemm_parity(f"decode {h['name']} 32x{h['N']}x{h['K']}", got, orc.gemm_fwd(oxq, oxs, owq, ows, mode=orc.MFMA),
                 orc.gemm_fwd(oxq, oxs, owq, ows, mode=orc.EXACT))
 
 
