@@ -95,12 +95,49 @@ def _dt(t, dtype, name):
         raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
 
 
+def _need(t, shape, dtype, name, device=None):
+    """Host-side check of one operand before its pointer reaches the C ABI (which trusts the sizes it is
+    given): a contiguous device tensor of exactly this shape and dtype, on `device` when given."""
+    import torch
+    if t is None:
+        raise ValueError(f"{name}: required")
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name}: expected a device tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(int(d) for d in shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name}: on {t.device}, other operands on {device}")
+
+
+def _bf16_u8_f32():
+    import torch
+    return torch.bfloat16, torch.uint8, torch.float32
+
+
 # ------------------------------------------------------------------------------------------------
 # Raw entry points: same names and argument order as the C ABI; outputs are caller-allocated.
 # ------------------------------------------------------------------------------------------------
 def jetfp8_quantize(src_bf16, rows: int, cols: int, mode: int, dst_codes, dst_scales, dst_codes_t=None,
                     stream=None) -> None:
     L = load_library()
+    bf, u8, f32 = _bf16_u8_f32()
+    R, C = int(rows), int(cols)
+    if R >= 1 and C >= 1 and mode in (ROWS_1x128, COLS_128x1_T, BLOCKS_128x128):
+        _need(src_bf16, (R, C), bf, "src_bf16")
+        dev = src_bf16.device
+        if mode == ROWS_1x128:
+            _need(dst_codes, (R, C), u8, "dst_codes", dev)
+            _need(dst_scales, (C // 128, R), f32, "dst_scales", dev)
+        elif mode == COLS_128x1_T:
+            _need(dst_codes, (C, R), u8, "dst_codes", dev)
+            _need(dst_scales, (R // 128, C), f32, "dst_scales", dev)
+        else:
+            _need(dst_codes, (R, C), u8, "dst_codes", dev)
+            _need(dst_scales, (R // 128, C // 128), f32, "dst_scales", dev)
+            if dst_codes_t is not None:
+                _need(dst_codes_t, (C, R), u8, "dst_codes_t", dev)
     st = L.jetfp8_quantize(_ptr(src_bf16), int(rows), int(cols), int(mode), _ptr(dst_codes), _ptr(dst_scales),
                            _ptr(dst_codes_t), _stream(stream))
     _check("jetfp8_quantize", st)
@@ -109,6 +146,15 @@ def jetfp8_quantize(src_bf16, rows: int, cols: int, mode: int, dst_codes, dst_sc
 def jetfp8_quantize_dual(src_bf16, rows: int, cols: int, dst_codes, dst_scales, dst_codes_t, dst_scales_t,
                          stream=None) -> None:
     L = load_library()
+    bf, u8, f32 = _bf16_u8_f32()
+    R, C = int(rows), int(cols)
+    if R >= 1 and C >= 1:
+        _need(src_bf16, (R, C), bf, "src_bf16")
+        dev = src_bf16.device
+        _need(dst_codes, (R, C), u8, "dst_codes", dev)
+        _need(dst_scales, (C // 128, R), f32, "dst_scales", dev)
+        _need(dst_codes_t, (C, R), u8, "dst_codes_t", dev)
+        _need(dst_scales_t, (R // 128, C), f32, "dst_scales_t", dev)
     st = L.jetfp8_quantize_dual(_ptr(src_bf16), int(rows), int(cols), _ptr(dst_codes), _ptr(dst_scales),
                                 _ptr(dst_codes_t), _ptr(dst_scales_t), _stream(stream))
     _check("jetfp8_quantize_dual", st)
@@ -116,6 +162,14 @@ def jetfp8_quantize_dual(src_bf16, rows: int, cols: int, dst_codes, dst_scales, 
 
 def jetfp8_requantize_cols_t(codes, scales, rows: int, cols: int, dst_codes_t, dst_scales_t, stream=None) -> None:
     L = load_library()
+    bf, u8, f32 = _bf16_u8_f32()
+    R, C = int(rows), int(cols)
+    if R >= 1 and C >= 1:
+        _need(codes, (R, C), u8, "codes")
+        dev = codes.device
+        _need(scales, (C // 128, R), f32, "scales", dev)
+        _need(dst_codes_t, (C, R), u8, "dst_codes_t", dev)
+        _need(dst_scales_t, (R // 128, C), f32, "dst_scales_t", dev)
     st = L.jetfp8_requantize_cols_t(_ptr(codes), _ptr(scales), int(rows), int(cols), _ptr(dst_codes_t),
                                     _ptr(dst_scales_t), _stream(stream))
     _check("jetfp8_requantize_cols_t", st)
@@ -124,6 +178,18 @@ def jetfp8_requantize_cols_t(codes, scales, rows: int, cols: int, dst_codes_t, d
 def jetfp8_rmsnorm_quantize(x_bf16, weight_bf16, rows: int, cols: int, eps: float, dst_codes, dst_scales,
                             dst_rstd=None, dst_y_bf16=None, stream=None) -> None:
     L = load_library()
+    bf, u8, f32 = _bf16_u8_f32()
+    R, C = int(rows), int(cols)
+    if R >= 1 and C >= 1:
+        _need(x_bf16, (R, C), bf, "x_bf16")
+        dev = x_bf16.device
+        _need(weight_bf16, (C,), bf, "weight_bf16", dev)
+        _need(dst_codes, (R, C), u8, "dst_codes", dev)
+        _need(dst_scales, (C // 128, R), f32, "dst_scales", dev)
+        if dst_rstd is not None:
+            _need(dst_rstd, (R,), f32, "dst_rstd", dev)
+        if dst_y_bf16 is not None:
+            _need(dst_y_bf16, (R, C), bf, "dst_y_bf16", dev)
     st = L.jetfp8_rmsnorm_quantize(_ptr(x_bf16), _ptr(weight_bf16), int(rows), int(cols), float(eps),
                                    _ptr(dst_codes), _ptr(dst_scales), _ptr(dst_rstd), _ptr(dst_y_bf16),
                                    _stream(stream))
@@ -133,25 +199,52 @@ def jetfp8_rmsnorm_quantize(x_bf16, weight_bf16, rows: int, cols: int, eps: floa
 def jetfp8_swiglu_quantize(gate_up_bf16, rows: int, cols: int, dst_codes, dst_scales, dst_h_bf16=None,
                            stream=None) -> None:
     L = load_library()
+    bf, u8, f32 = _bf16_u8_f32()
+    R, F = int(rows), int(cols)
+    if R >= 1 and F >= 1:
+        _need(gate_up_bf16, (R, 2 * F), bf, "gate_up_bf16")
+        dev = gate_up_bf16.device
+        _need(dst_codes, (R, F), u8, "dst_codes", dev)
+        _need(dst_scales, (F // 128, R), f32, "dst_scales", dev)
+        if dst_h_bf16 is not None:
+            _need(dst_h_bf16, (R, F), bf, "dst_h_bf16", dev)
     st = L.jetfp8_swiglu_quantize(_ptr(gate_up_bf16), int(rows), int(cols), _ptr(dst_codes), _ptr(dst_scales),
                                   _ptr(dst_h_bf16), _stream(stream))
     _check("jetfp8_swiglu_quantize", st)
 
 
+def _check_gemm_operands(a, sa, b, sb, out, a_shape, sa_shape, b_shape, sb_shape, out_shape):
+    bf, u8, f32 = _bf16_u8_f32()
+    if min(a_shape + b_shape) < 1:
+        return                                  # the C ABI rejects non-positive sizes itself
+    _need(a, a_shape, u8, "A codes")
+    dev = a.device
+    _need(sa, sa_shape, f32, "A scales", dev)
+    _need(b, b_shape, u8, "B codes", dev)
+    _need(sb, sb_shape, f32, "B scales", dev)
+    _need(out, out_shape, bf, "output", dev)
+
+
 def jetfp8_gemm_fwd(xq, xs, wq, ws, y_bf16, M: int, N: int, K: int, stream=None) -> None:
     L = load_library()
+    M, N, K = int(M), int(N), int(K)
+    _check_gemm_operands(xq, xs, wq, ws, y_bf16, (M, K), (K // 128, M), (N, K), (N // 128, K // 128), (M, N))
     _check("jetfp8_gemm_fwd", L.jetfp8_gemm_fwd(_ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws), _ptr(y_bf16),
                                                  int(M), int(N), int(K), _stream(stream)))
 
 
 def jetfp8_gemm_dgrad(dyq, dys, wqT, ws, dx_bf16, M: int, N: int, K: int, stream=None) -> None:
     L = load_library()
+    M, N, K = int(M), int(N), int(K)
+    _check_gemm_operands(dyq, dys, wqT, ws, dx_bf16, (M, N), (N // 128, M), (K, N), (N // 128, K // 128), (M, K))
     _check("jetfp8_gemm_dgrad", L.jetfp8_gemm_dgrad(_ptr(dyq), _ptr(dys), _ptr(wqT), _ptr(ws), _ptr(dx_bf16),
                                                      int(M), int(N), int(K), _stream(stream)))
 
 
 def jetfp8_gemm_wgrad(dyqT, dysT, xqT, xsT, dw_bf16, M: int, N: int, K: int, stream=None) -> None:
     L = load_library()
+    M, N, K = int(M), int(N), int(K)
+    _check_gemm_operands(dyqT, dysT, xqT, xsT, dw_bf16, (N, M), (M // 128, N), (K, M), (M // 128, K), (N, K))
     _check("jetfp8_gemm_wgrad", L.jetfp8_gemm_wgrad(_ptr(dyqT), _ptr(dysT), _ptr(xqT), _ptr(xsT), _ptr(dw_bf16),
                                                      int(M), int(N), int(K), _stream(stream)))
 

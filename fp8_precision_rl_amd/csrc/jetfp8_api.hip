@@ -37,7 +37,7 @@ int check_gemm_extent(int64_t I, int64_t J, int64_t Kc) {
 
 extern "C" {
 
-int jetfp8_version(void) { return 300; }
+int jetfp8_version(void) { return 301; }
 
 const char* jetfp8_status_string(int status) {
     switch (status) {
@@ -64,6 +64,10 @@ int jetfp8_quantize(const void* src_bf16, int64_t rows, int64_t cols, int mode, 
         case JETFP8_COLS_128x1_T: if (rows % 128 || cols % 64) return JETFP8_ERR_SHAPE; break;
         default: if (rows % 128 || cols % 128) return JETFP8_ERR_SHAPE; break;
     }
+    const bool fits = mode == JETFP8_ROWS_1x128 ? jetfp8::quant_rows_fits(rows, cols)
+                      : mode == JETFP8_COLS_128x1_T ? jetfp8::quant_cols_t_fits(rows, cols)
+                                                    : jetfp8::quant_blocks_fits(rows, cols);
+    if (!fits) return JETFP8_ERR_SHAPE;
     if (!aligned16(src_bf16) || !aligned16(dst_codes) || !aligned16(dst_scales) ||
         (dst_codes_t && !aligned16(dst_codes_t)))
         return JETFP8_ERR_ALIGN;
@@ -80,6 +84,7 @@ int jetfp8_quantize_dual(const void* src_bf16, int64_t rows, int64_t cols, uint8
                          uint8_t* dst_codes_t, float* dst_scales_t, void* stream) {
     if (!src_bf16 || !dst_codes || !dst_scales || !dst_codes_t || !dst_scales_t) return JETFP8_ERR_NULL;
     if (!dim_ok(rows) || !dim_ok(cols) || rows % 128 || cols % 128) return JETFP8_ERR_SHAPE;
+    if (!jetfp8::quant_dual_fits(rows, cols)) return JETFP8_ERR_SHAPE;
     if (!aligned16(src_bf16) || !aligned16(dst_codes) || !aligned16(dst_scales) || !aligned16(dst_codes_t) ||
         !aligned16(dst_scales_t))
         return JETFP8_ERR_ALIGN;
@@ -92,6 +97,7 @@ int jetfp8_requantize_cols_t(const uint8_t* codes, const float* scales, int64_t 
                              uint8_t* dst_codes_t, float* dst_scales_t, void* stream) {
     if (!codes || !scales || !dst_codes_t || !dst_scales_t) return JETFP8_ERR_NULL;
     if (!dim_ok(rows) || !dim_ok(cols) || rows % 128 || cols % 128) return JETFP8_ERR_SHAPE;
+    if (!jetfp8::quant_requant_cols_fits(rows, cols)) return JETFP8_ERR_SHAPE;
     if (!aligned16(codes) || !aligned16(scales) || !aligned16(dst_codes_t) || !aligned16(dst_scales_t))
         return JETFP8_ERR_ALIGN;
     return hip_status(jetfp8::launch_quant_requant_cols(codes, scales, rows, cols, dst_codes_t, dst_scales_t,
@@ -116,6 +122,7 @@ int jetfp8_swiglu_quantize(const void* gate_up_bf16, int64_t rows, int64_t cols,
                            float* dst_scales, void* dst_h_bf16, void* stream) {
     if (!gate_up_bf16 || !dst_codes || !dst_scales) return JETFP8_ERR_NULL;
     if (!dim_ok(rows) || !dim_ok(cols) || !dim_ok(2 * cols) || cols % 128) return JETFP8_ERR_SHAPE;
+    if (!jetfp8::swiglu_quant_fits(rows, cols)) return JETFP8_ERR_SHAPE;
     if (!aligned16(gate_up_bf16) || !aligned16(dst_codes) || !aligned16(dst_scales) ||
         (dst_h_bf16 && !aligned16(dst_h_bf16)))
         return JETFP8_ERR_ALIGN;

@@ -19,6 +19,8 @@
 //     the tile); row-scaled B (WGrad): sa * sb per element;
 //   - blocks are renumbered so that each XCD (8 per device, dispatched round robin) works on a compact
 //     band of output tiles that share A rows and B rows in its L2.
+#include <atomic>
+
 #include "jetfp8_common.h"
 #include "jetfp8_launch.h"
 
@@ -31,6 +33,10 @@ typedef __attribute__((address_space(3))) void lds_void;
 // 16x16x128 FP8 (E4M3 x E4M3) matrix product with C = 0: D[i][j] = sum_k a[i][k] * b[j][k].  Lane l supplies
 // row (l % 16) of a and of b, bytes k = 32 * (l / 16) .. +31; result element v of lane l is
 // D[4 * (l / 16) + v][l % 16].
+// The builtin is the scaled form (V_MFMA_SCALE_F32_16X16X128_F8F6F4); its trailing operands are the formats of
+// a and b (0 = E4M3 for both) and the E8M0 block-scale operands with their byte selectors.  With the scale
+// operands constant zero the compiler selects the plain, unscaled V_MFMA_F32_16X16X128_F8F6F4 (the only matrix
+// opcode in this file's gfx950 assembly), so the result is the unscaled E4M3 x E4M3 product.
 __device__ __forceinline__ v4f mfma_group(const v8i& a, const v8i& b) {
     const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, z, 0, 0, 0, 0, 0, 0);
@@ -376,17 +382,18 @@ __global__ __launch_bounds__(L_THREADS, 1) void gemm_large_kernel(
 }
 
 // Compute units of the current device (one persistent block per compute unit: a block's LDS ring
-// takes most of a CU's LDS).
+// takes most of a CU's LDS).  The per-device cache is atomic: concurrent first calls may both query the
+// runtime, and they store the same value.
 static int device_cu_count() {
-    static int cache[64];
+    static std::atomic<int> cache[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cache[dev] == 0) {
-        int n = 0;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-        cache[dev] = n;
+        cache[dev].store(n, std::memory_order_relaxed);
     }
-    return cache[dev];
+    return n;
 }
 
 // ---- small-M kernel (rollout decode batches: I <= 16 * RT rows, RT = 1, 2, 4) --------------------------

@@ -9,6 +9,15 @@ namespace jetfp8 {
 // (groups x rows x 4 bytes) through 32-bit buffer offsets; the C ABI rejects shapes beyond this.
 constexpr int64_t kMaxGemmBand = ((int64_t)1 << 31) - 1;
 
+// Size limits of each kernel's launch grid and of its 32-bit buffer offsets.  The C ABI checks these on the host
+// (JETFP8_ERR_SHAPE) before calling a launcher; the launchers assume them.
+bool quant_rows_fits(int64_t R, int64_t C);
+bool quant_cols_t_fits(int64_t R, int64_t C);
+bool quant_dual_fits(int64_t R, int64_t C);
+bool quant_requant_cols_fits(int64_t R, int64_t C);
+bool quant_blocks_fits(int64_t R, int64_t C);
+bool swiglu_quant_fits(int64_t R, int64_t F);
+
 hipError_t launch_quant_rows(const uint16_t* x, int64_t R, int64_t C, uint8_t* q, float* s, hipStream_t st);
 hipError_t launch_quant_cols_t(const uint16_t* x, int64_t R, int64_t C, uint8_t* qT, float* sT, hipStream_t st);
 hipError_t launch_quant_dual(const uint16_t* x, int64_t R, int64_t C, uint8_t* q, float* s, uint8_t* qT, float* sT,

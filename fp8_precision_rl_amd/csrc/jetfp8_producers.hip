@@ -262,10 +262,14 @@ hipError_t launch_rmsnorm_quant(const uint16_t* x, const uint16_t* w, int64_t R,
     return hipGetLastError();
 }
 
+bool swiglu_quant_fits(int64_t R, int64_t F) {
+    return ((F + SG_COLS - 1) / SG_COLS) * ((R + SG_ROWS - 1) / SG_ROWS) < ((int64_t)1 << 31);
+}
+
 hipError_t launch_swiglu_quant(const uint16_t* gu, int64_t R, int64_t F, uint8_t* q, float* s, uint16_t* h,
                                hipStream_t st) {
     const int64_t col_blocks = (F + SG_COLS - 1) / SG_COLS, row_blocks = (R + SG_ROWS - 1) / SG_ROWS;
-    if (col_blocks * row_blocks >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+    if (!swiglu_quant_fits(R, F)) return hipErrorInvalidValue;
     hipLaunchKernelGGL(swiglu_quant_kernel, dim3((unsigned)(col_blocks * row_blocks)), dim3(SG_WAVES * 64), 0, st,
                        gu, R, F, q, s, h, (uint32_t)col_blocks);
     return hipGetLastError();

@@ -388,9 +388,23 @@ __global__ __launch_bounds__(256) void quant_blocks_kernel(const uint16_t* __res
     }
 }
 
+// One-dimensional grids of at most 2^31 - 1 blocks; the fused and requantizing kernels also address a tile's
+// 32 (or 128) rows through buffer offsets below 2^31 bytes; the block kernel's grid.y (row blocks) is at most 65535.
+bool quant_rows_fits(int64_t R, int64_t C) {
+    return ((C + QR_COLS - 1) / QR_COLS) * ((R + QR_ROWS - 1) / QR_ROWS) <= 0x7FFFFFFF;
+}
+bool quant_cols_t_fits(int64_t R, int64_t C) { return ((C + 127) / 128) * (R / 128) <= 0x7FFFFFFF; }
+bool quant_dual_fits(int64_t R, int64_t C) {
+    return (C / 128) * (R / 128) <= 0x7FFFFFFF && 64 * C + 256 < ((int64_t)1 << 31) && 128 * R + 128 < ((int64_t)1 << 31);
+}
+bool quant_requant_cols_fits(int64_t R, int64_t C) {
+    return (C / 128) * (R / 128) <= 0x7FFFFFFF && 32 * C + 128 < ((int64_t)1 << 31) && 128 * R + 128 < ((int64_t)1 << 31);
+}
+bool quant_blocks_fits(int64_t R, int64_t C) { return R / 128 <= 65535 && C / 128 <= 0x7FFFFFFF; }
+
 hipError_t launch_quant_rows(const uint16_t* x, int64_t R, int64_t C, uint8_t* q, float* s, hipStream_t st) {
     const int64_t col_blocks = (C + QR_COLS - 1) / QR_COLS, row_blocks = (R + QR_ROWS - 1) / QR_ROWS;
-    if (col_blocks * row_blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    if (!quant_rows_fits(R, C)) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(quant_rows_kernel, dim3((unsigned)(col_blocks * row_blocks)), dim3(QR_WAVES * 64), 0, st, x, R,
                        C, q, s, (uint32_t)col_blocks);
     return hipGetLastError();
@@ -399,7 +413,7 @@ hipError_t launch_quant_rows(const uint16_t* x, int64_t R, int64_t C, uint8_t* q
 hipError_t launch_quant_cols_t(const uint16_t* x, int64_t R, int64_t C, uint8_t* qT, float* sT, hipStream_t st) {
     // R is a multiple of 128 (whole groups); C a multiple of 64 (a partial last column tile is masked).
     const int64_t col_blocks = (C + 127) / 128, row_blocks = R / 128;
-    if (col_blocks * row_blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    if (!quant_cols_t_fits(R, C)) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(quant_cols_t_kernel, dim3((unsigned)(col_blocks * row_blocks)), dim3(256), 0, st, x, R, C, qT,
                        sT, (uint32_t)col_blocks);
     return hipGetLastError();
@@ -409,9 +423,8 @@ hipError_t launch_quant_dual(const uint16_t* x, int64_t R, int64_t C, uint8_t* q
                              hipStream_t st) {
     // R and C are multiples of 128 (whole groups both ways)
     const int64_t col_blocks = C / 128, row_blocks = R / 128;
-    if (col_blocks * row_blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
     // buffer spans and offsets in 31 bits: 32 bf16 rows (2 * (31 C + 128) bytes) and 128 transposed rows
-    if (64 * C + 256 >= ((int64_t)1 << 31) || 128 * R + 128 >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+    if (!quant_dual_fits(R, C)) return hipErrorInvalidValue;
     hipLaunchKernelGGL(quant_dual_kernel, dim3((unsigned)(col_blocks * row_blocks)), dim3(256), 0, st, x, R, C, q, s,
                        qT, sT, (uint32_t)col_blocks);
     return hipGetLastError();
@@ -421,8 +434,7 @@ hipError_t launch_quant_requant_cols(const uint8_t* q, const float* s, int64_t R
                                      float* sT, hipStream_t st) {
     // R and C are multiples of 128; buffer spans and offsets in 31 bits (32 code rows, 128 transposed rows)
     const int64_t col_blocks = C / 128, row_blocks = R / 128;
-    if (col_blocks * row_blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-    if (32 * C + 128 >= ((int64_t)1 << 31) || 128 * R + 128 >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+    if (!quant_requant_cols_fits(R, C)) return hipErrorInvalidValue;
     hipLaunchKernelGGL(quant_requant_cols_kernel, dim3((unsigned)(col_blocks * row_blocks)), dim3(256), 0, st, q, s,
                        R, C, qT, sT, (uint32_t)col_blocks);
     return hipGetLastError();
@@ -430,6 +442,7 @@ hipError_t launch_quant_requant_cols(const uint8_t* q, const float* s, int64_t R
 
 hipError_t launch_quant_blocks(const uint16_t* x, int64_t R, int64_t C, uint8_t* q, float* s, uint8_t* qT,
                                hipStream_t st) {
+    if (!quant_blocks_fits(R, C)) return hipErrorInvalidValue;
     dim3 grid((unsigned)(C / 128), (unsigned)(R / 128));
     hipLaunchKernelGGL(quant_blocks_kernel, grid, dim3(256), 0, st, x, R, C, q, s, qT);
     return hipGetLastError();

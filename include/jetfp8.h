@@ -31,9 +31,19 @@
  *     been enqueued).  No exception ever crosses this interface.
  *   - All pointers must be 16-byte aligned (JETFP8_ERR_ALIGN otherwise).  Buffers must not overlap.
  *   - Sizes: every dimension >= 1; every grouped or contraction axis a multiple of 128, plus the
- *     per-mode rules below (JETFP8_ERR_SHAPE otherwise); every dimension < 2^31.  GEMMs additionally
- *     need 256 * (contraction length) < 2^31 and (contraction length / 128) * (rows of either operand)
- *     * 4 < 2^31 bytes of scales (they address operand bands and scale arrays with 32-bit offsets).
+ *     per-mode rules below (JETFP8_ERR_SHAPE otherwise); every dimension < 2^31.  Kernels address their
+ *     tiles with 32-bit offsets and launch one-dimensional grids, so each call also rejects, with
+ *     JETFP8_ERR_SHAPE and before any launch:
+ *       GEMMs ............... 256 * (contraction length) >= 2^31, or (contraction length / 128) * (rows of
+ *                             either operand) * 4 >= 2^31 (bytes of a scale array);
+ *       ROWS_1x128 .......... ceil(cols / 512) * ceil(rows / 32) > 2^31 - 1;
+ *       COLS_128x1_T ........ ceil(cols / 128) * (rows / 128) > 2^31 - 1;
+ *       BLOCKS_128x128 ...... rows / 128 > 65535;
+ *       quantize_dual ....... (cols / 128) * (rows / 128) > 2^31 - 1, 64 * cols + 256 >= 2^31, or
+ *                             128 * rows + 128 >= 2^31;
+ *       requantize_cols_t ... (cols / 128) * (rows / 128) > 2^31 - 1, 32 * cols + 128 >= 2^31, or
+ *                             128 * rows + 128 >= 2^31;
+ *       swiglu_quantize ..... ceil(cols / 512) * ceil(rows / 32) >= 2^31.
  *   - Thread safety: calls are independent; concurrent calls on different streams are allowed.
  */
 #ifndef JETFP8_H
@@ -123,15 +133,17 @@ int jetfp8_rmsnorm_quantize(const void* x_bf16, const void* weight_bf16, int64_t
 int jetfp8_swiglu_quantize(const void* gate_up_bf16, int64_t rows, int64_t cols, uint8_t* dst_codes,
                            float* dst_scales, void* dst_h_bf16, void* stream);
 
-/* Forward FP8 linear (rollout decode, prefill, training forward):
+/* Forward FP8 linear (rollout decode, prefill, training forward).  Jet-RL explainers, "Architecture Centrale":
+ * rollout runs the same FP8 linear layers, with the same quantization, as the training forward pass;
+ * "Schema de Quantification": activations in 1x128 groups, weights in 128x128 blocks, FP8 GEMM.
  *   Y[m][n] = sum_g xs[g][m] * ws[n/128][g] * sum_{k in g} xq[m][k] * wq[n][k]
  * xq [M][K], xs [K/128][M] (JETFP8_ROWS_1x128 of X); wq [N][K], ws [N/128][K/128]
  * (JETFP8_BLOCKS_128x128 of W); y [M][N] bf16.  K % 128 == 0, N % 128 == 0, any M >= 1. */
 int jetfp8_gemm_fwd(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws,
                     void* y_bf16, int64_t M, int64_t N, int64_t K, void* stream);
 
-/* DGrad FP8 GEMM (Jet-RL explainers, "Passage Arriere": DGrad in FP8 with BF16 gradients quantized
- * on entry):
+/* DGrad FP8 GEMM (Jet-RL explainers, "Schema de Quantification", backward-pass items: gradients between
+ * operators stay BF16, and the DGrad GEMM runs in FP8 with the gradient quantized on entry):
  *   dX[m][k] = sum_g dys[g][m] * ws[g][k/128] * sum_{n in g} dyq[m][n] * wqT[k][n]
  * dyq [M][N], dys [N/128][M] (JETFP8_ROWS_1x128 of dY); wqT [K][N] (the transposed block codes of W
  * from JETFP8_BLOCKS_128x128), ws [N/128][K/128] (the forward block scales, unchanged);
@@ -139,8 +151,9 @@ int jetfp8_gemm_fwd(const uint8_t* xq, const float* xs, const uint8_t* wq, const
 int jetfp8_gemm_dgrad(const uint8_t* dyq, const float* dys, const uint8_t* wqT, const float* ws,
                       void* dx_bf16, int64_t M, int64_t N, int64_t K, void* stream);
 
-/* WGrad FP8 GEMM ("1x128 and 128x1" kernel configuration: both operands grouped along the token axis,
- * which is the contraction axis):
+/* WGrad FP8 GEMM.  Jet-RL explainers, "Schema de Quantification" / "Esquema de Quantizacao": the weight
+ * gradient GEMM runs in FP8 with the "1x128 and 128x1" configuration, read as both operands grouped along the
+ * token axis, which is the contraction axis; gradients reach it in BF16 and are quantized on entry:
  *   dW[n][k] = sum_g dysT[g][n] * xsT[g][k] * sum_{m in g} dyqT[n][m] * xqT[k][m]
  * dyqT [N][M], dysT [M/128][N] (JETFP8_COLS_128x1_T of dY); xqT [K][M], xsT [M/128][K]
  * (JETFP8_COLS_128x1_T of X); dw [N][K] bf16, overwritten.  M % 128 == 0, N % 128 == 0,
