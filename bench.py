@@ -38,9 +38,13 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", default="llama3_8b_train_m16384")
+    p.add_argument("--workload", default="qwen25_32b_train_m65536",
+                   help="training-step workload (default: the Qwen2.5-32B-shaped linears at 65536 tokens, the largest "
+                        "single-GPU configuration; llama3_8b_train_m16384 is the 8B step at 16384 tokens)")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-sample-rows", type=int, default=128)
+    p.add_argument("--cpu-sample-rows", type=int, default=None,
+                   help="token rows per linear of the oracle's all-thread sample (default: 64 for the 32B shapes, "
+                        "128 otherwise); the one-thread sample uses 1/16 of them")
     p.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "gemm_traffic.json"),
                    help="per-launch HBM bytes measured by rocprofv3 for this workload (optional)")
     p.add_argument("--x-from-fp8", action="store_true",
@@ -185,33 +189,52 @@ def step_description(args):
     return f"per linear: W block quant(+T), {x}, {dy}{xt}, wgrad"
 
 
+def host_core_counts():
+    """(logical CPUs of the host, CPUs this process may run on)."""
+    n = os.cpu_count() or 1
+    try:
+        aff = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        aff = n
+    return n, aff
+
+
 def cpu_baseline(wl, rows, workloads):
-    """The oracle (unchanged) on a bounded sample of the workload: for every linear, the full weight
-    quantization, then forward and DGrad for `rows` token rows and WGrad for `rows` rows of dW over one
-    128-token group, with all of this host's threads."""
+    """The oracle (unchanged) on a bounded sample of the workload, timed twice on this host: with all the threads
+    it uses by default (its pool is capped at 16, one GPU's share of a shared host) and with one thread.  Per
+    linear: the weight is block-quantized untimed (once per optimizer step), then the timed part quantizes the
+    sampled activation and gradient rows and runs the forward and DGrad GEMMs for `rows` token rows (all output
+    columns) and WGrad for `rows` rows of dW over one 128-token group.  The one-thread run does the same for
+    rows // 16 token rows (at least 1).  value = GEMM flops of the sample / time with all threads."""
     import numpy as np
     import oracle
     threads = oracle.default_threads()
-    flops = 0
-    elapsed = 0.0
+    rows1 = max(1, rows // 16)
+    flops = {threads: 0, 1: 0}
+    elapsed = {threads: 0.0, 1: 0.0}
     for i, (name, K, N) in enumerate(wl.linears):
         h = workloads.host_linear(workloads.Workload(wl.name, 128, wl.linears, wl.outlier_frac, wl.seed, True, ""), i)
-        t0 = time.perf_counter()
         wq, ws = oracle.quantize_blocks(h["w"], threads)
-        xq, xs = oracle.quantize_rows(h["x"], threads)
-        dyq, dys = oracle.quantize_rows(h["dy"], threads)
-        oracle.gemm_fwd(xq, xs, wq, ws, rows=np.arange(rows), mode=oracle.MFMA, threads=threads)
-        oracle.gemm_dgrad(dyq, dys, wq, ws, rows=np.arange(rows), mode=oracle.MFMA, threads=threads)
-        dyqc, dysc = oracle.quantize_cols(h["dy"], threads)
-        xqc, xsc = oracle.quantize_cols(h["x"], threads)
-        oracle.gemm_wgrad(dyqc, dysc, xqc, xsc, rows=np.arange(rows), mode=oracle.MFMA, threads=threads)
-        elapsed += time.perf_counter() - t0
-        flops += 2 * rows * N * K * 2 + 2 * rows * K * 128
-    return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": (f"per linear: full 128x128 weight quantization; forward and dgrad for {rows} token rows; "
-                       f"wgrad for {rows} rows of dW over one 128-token group; total {flops / 1e9:.1f} GFLOP "
-                       f"in {elapsed:.1f} s"),
-            "seconds": elapsed}
+        for nt, r in ((threads, rows), (1, rows1)):
+            t0 = time.perf_counter()
+            xq, xs = oracle.quantize_rows(np.ascontiguousarray(h["x"][:r]), nt)
+            dyq, dys = oracle.quantize_rows(np.ascontiguousarray(h["dy"][:r]), nt)
+            oracle.gemm_fwd(xq, xs, wq, ws, mode=oracle.MFMA, threads=nt)
+            oracle.gemm_dgrad(dyq, dys, wq, ws, mode=oracle.MFMA, threads=nt)
+            dyqc, dysc = oracle.quantize_cols(np.ascontiguousarray(h["dy"][:, :r]), nt)
+            xqc, xsc = oracle.quantize_cols(h["x"], nt)
+            oracle.gemm_wgrad(dyqc, dysc, xqc, xsc, mode=oracle.MFMA, threads=nt)
+            elapsed[nt] += time.perf_counter() - t0
+            flops[nt] += 2 * r * N * K * 2 + 2 * r * K * 128
+    host, aff = host_core_counts()
+    return {"value": flops[threads] / elapsed[threads] / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "host_cores": host, "affinity_cores": aff,
+            "value_1thread": flops[1] / elapsed[1] / 1e12,
+            "sample": (f"per linear (weights block-quantized untimed): the sampled rows' 1x128 / 128x1 quantization, "
+                       f"forward and dgrad for {rows} token rows, wgrad for {rows} rows of dW over one 128-token "
+                       f"group; {flops[threads] / 1e9:.1f} GFLOP in {elapsed[threads]:.1f} s on {threads} threads. "
+                       f"One thread: the same for {rows1} rows, {flops[1] / 1e9:.1f} GFLOP in {elapsed[1]:.1f} s"),
+            "seconds": elapsed[threads] + elapsed[1]}
 
 
 def producer_bytes(R, C, F):
@@ -547,7 +570,8 @@ def main():
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample_rows, workloads)
+        rows = args.cpu_sample_rows or (64 if wl.M > 16384 else 128)
+        out["cpu_baseline"] = cpu_baseline(wl, rows, workloads)
     print(json.dumps(out), flush=True)
 
 

@@ -13,6 +13,9 @@ row with the same call whatever the mode, so any difference between the modes ca
   * Prefill of 96 tokens (M = 96), incremental decode of the same tokens one at a time (M = 1, with a key/value
     cache) and chunked decode (M = 32 per step) give bitwise the same hidden state for every token at every depth:
     no rollout/training mismatch.
+  * The prefill hidden states equal, bit for bit at every depth, the same stack run through the CPU oracle
+    (its RMSNorm->1x128 and SwiGLU->1x128 producers, its 1x128 quantizer, its block quantizer and its forward GEMM
+    in the matrix-instruction mode), with the same attention stand-in and the same fp32 residual adds.
   * Against a bf16 reference of the same stack (fp32 math on the bf16 tensors, same attention stand-in), each FP8
     block adds a quantization error of a few percent that does not grow with depth (teacher forcing).
 Weights are random and seeded; no trained model is involved.
@@ -67,18 +70,38 @@ def _attn_row(q, K, V):
     return out
 
 
-def _attention(qkv_rows, cache, start):
-    """qkv_rows: bf16 [m, 3D] for tokens start .. start+m-1; cache: dict of K, V float64 lists (appended here).
-    Returns the attention output rows as bf16 [m, D]."""
+def _f32(bits):
+    """bf16 bit patterns (numpy uint16) -> float32, exact."""
+    return (np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def _to_bf16_bits(a32):
+    """float32 (numpy) -> bf16 bit patterns, round to nearest even (torch's conversion, on the CPU)."""
     import torch
-    a = qkv_rows.float().cpu().numpy().astype(np.float64)
+    t = torch.from_numpy(np.ascontiguousarray(a32, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def _attention_bits(qkv_bits, cache, start):
+    """qkv_bits: bf16 bits [m, 3D] for tokens start .. start+m-1; cache: dict of K, V float64 lists (appended
+    here).  Returns the attention output rows as bf16 bits [m, D] (fp64 -> fp32 -> bf16, each rounding to
+    nearest even)."""
+    a = _f32(qkv_bits).astype(np.float64)
     outs = []
     for i in range(a.shape[0]):
         cache["K"].append(a[i, D:2 * D])
         cache["V"].append(a[i, 2 * D:])
         t = start + i
         outs.append(_attn_row(a[i, :D], np.array(cache["K"][:t + 1]), np.array(cache["V"][:t + 1])))
-    return torch.from_numpy(np.array(outs, dtype=np.float32)).to("cuda").to(torch.bfloat16)
+    return _to_bf16_bits(np.array(outs, dtype=np.float32))
+
+
+def _attention(qkv_rows, cache, start):
+    """Device wrapper of _attention_bits: bf16 [m, 3D] on the GPU -> bf16 [m, D] on the GPU."""
+    import torch
+    bits = qkv_rows.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    out = _attention_bits(bits, cache, start)
+    return torch.from_numpy(out.view(np.int16)).to("cuda").view(torch.bfloat16)
 
 
 # --------------------------------------------------------------------------------------------- blocks
@@ -140,6 +163,38 @@ def test_decode_and_prefill_hidden_states_are_bitwise_equal(stack):
         for depth in range(LAYERS):
             diff = np.flatnonzero((dec[depth] != prefill[depth]).any(axis=1))
             assert diff.size == 0, f"M = {chunk}: tokens {diff[:8]} differ at depth {depth}"
+
+
+def _oracle_block(orc, prod, Lq, x, cache):
+    """One block on the CPU oracle (prefill of every token at once): bf16 bits in, bf16 bits out."""
+    xq, xs, _, _, _ = prod.rmsnorm_quantize(x, Lq["n1"], EPS)
+    qkv = orc.gemm_fwd(xq, xs, Lq["qkv_q"], Lq["qkv_s"], mode=orc.MFMA)
+    aq, as_ = orc.quantize_rows(_attention_bits(qkv, cache, 0))
+    h = _to_bf16_bits(_f32(x) + _f32(orc.gemm_fwd(aq, as_, Lq["o_q"], Lq["o_s"], mode=orc.MFMA)))
+    hq, hs, _, _, _ = prod.rmsnorm_quantize(h, Lq["n2"], EPS)
+    gu = orc.gemm_fwd(hq, hs, Lq["gu_q"], Lq["gu_s"], mode=orc.MFMA)
+    sq, ss, _ = prod.swiglu_quantize(gu)
+    return _to_bf16_bits(_f32(h) + _f32(orc.gemm_fwd(sq, ss, Lq["dn_q"], Lq["dn_s"], mode=orc.MFMA)))
+
+
+def test_prefill_hidden_states_equal_the_oracle_stack(stack, orc):
+    """The GPU prefill (M = 96) against the same three blocks run through the CPU oracle from the same bf16
+    weights and inputs: every hidden state bitwise equal at every depth."""
+    import torch
+    from oracle import producers as prod
+    jf, layers, x0 = stack
+    bits = lambda t: t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    gpu = _run_fp8(jf, layers, x0, S)
+    x = bits(x0)
+    for depth, L in enumerate(layers):
+        Lq = {"n1": bits(L["n1"]), "n2": bits(L["n2"])}
+        for k in ("qkv", "o", "gu", "dn"):
+            Lq[k + "_q"], Lq[k + "_s"] = orc.quantize_blocks(bits(L["w_" + k]))
+            assert np.array_equal(Lq[k + "_q"], L[k + "_q"].cpu().numpy()), (depth, k, "weight codes")
+        x = _oracle_block(orc, prod, Lq, x, {"K": [], "V": []})
+        diff = np.flatnonzero((x.view(np.int16) != gpu[depth]).any(axis=1))
+        print(f"depth {depth}: GPU prefill vs oracle stack, {diff.size} of {S} token rows differ", flush=True)
+        assert diff.size == 0, f"depth {depth}: tokens {diff[:8]} differ from the oracle"
 
 
 def test_fp8_block_error_against_bf16(stack):
