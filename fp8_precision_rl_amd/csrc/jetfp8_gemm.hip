@@ -43,8 +43,18 @@ __device__ __forceinline__ v4f mfma_group(const v8i& a, const v8i& b) {
 }
 
 constexpr int BK = 128;            // one quantization group along the contraction axis
-constexpr int L_BM = 256, L_BN = 256, L_THREADS = 512;
-constexpr int L_A_BYTES = L_BM * BK, L_B_BYTES = L_BN * BK;
+constexpr int L_THREADS = 512;
+// Block tile of the large-M kernel: 256 x 256 (SPLIT = 1), or 128 x 128 (SPLIT = 2) for the last, partial round
+// of tiles and for 65..128-row calls.  8 waves as 2 (rows) x 4 (columns); a wave owns TM x TN 16x16 tiles.  The
+// operand tiles are staged in parts of 64 rows (one 1 KB region per wave and part).
+template <int SPLIT>
+struct LargeCfg {
+    static constexpr int BM = 256 / SPLIT, BN = 256 / SPLIT;
+    static constexpr int WROWS = BM / 2, WCOLS = BN / 4;          // wave tile
+    static constexpr int TM = WROWS / 16, TN = WCOLS / 16;        // 8 x 4 or 4 x 2 tiles of 16x16
+    static constexpr int PA = BM / 64, PB = BN / 64;              // staging parts of A and B
+    static constexpr int PARTS = PA > PB ? PA : PB;
+};
 // s_waitcnt immediate: lgkmcnt == 0 only (vmcnt and expcnt at their maxima)
 constexpr int kWaitLgkm0 = 0xF | (7 << 4) | (3 << 14);
 
@@ -64,30 +74,47 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, int bytes) {
 #define JETFP8_BUFFER_LOAD_LDS(r, lds, size, voffset, soffset) \
     __builtin_amdgcn_raw_ptr_buffer_load_lds((r), (lds), (size), (voffset), (soffset), 0, 0)
 
-// Renumber a 1-D block index so that XCD x (which receives blocks x, x+8, ...) owns a contiguous range of
-// tiles, then walk tiles in bands of `group_m` tile-rows, N fastest inside a band.  Bands of 4 tile-rows
-// measured 1.4 % faster than bands of 8 (fewer L2 misses on the large shapes) and bands of 2 or 16 slower.
-__device__ __forceinline__ void tile_of_block(int pid, int tiles_m, int tiles_n, int& tm, int& tn) {
-    const int T = tiles_m * tiles_n;
-    const int per = T / 8, rem = T % 8, xcd = pid % 8, idx = pid / 8;
-    const int q = xcd * per + (xcd < rem ? xcd : rem) + idx;
+// Work item -> output tile.  Tiles of the 256 x 256 grid (tiles_m x tiles_n) are ordered in bands of `group_m`
+// tile-rows, N fastest inside a band; a call covers the band-order range [q_begin, q_begin + q_count).
+// SPLIT = 1: the work item is renumbered so that XCD x (which receives blocks x, x+8, ...) owns a contiguous part
+// of the range.  Bands of 4 tile-rows measured 1.4 % faster than bands of 8 (fewer L2 misses on the large shapes)
+// and bands of 2 or 16 slower.  SPLIT = 2: each 256 x 256 tile is `qrows` x 2 work items, its 128 x 128 quarters
+// (qrows = 1: the upper two only), returned in units of the 128 x 128 grid.
+template <int SPLIT>
+__device__ __forceinline__ void tile_of_work(int w, int tiles_m, int tiles_n, int q_begin, int q_count, int qrows,
+                                             int& tm, int& tn) {
+    int q, quad = 0;
+    if (SPLIT == 1) {
+        // (a 256 x 256 call always starts at the first tile: q_begin is 0 and not read, which keeps it out of the
+        // scalar registers the kernel's buffer descriptors need)
+        const int per = q_count / 8, rem = q_count % 8, xcd = w % 8, idx = w / 8;
+        q = xcd * per + (xcd < rem ? xcd : rem) + idx;
+    } else {
+        q = q_begin + w / (2 * qrows);
+        quad = w % (2 * qrows);
+    }
     const int group_m = 4;
     const int band = group_m * tiles_n;
     const int first_m = (q / band) * group_m;
     const int gsz = min(tiles_m - first_m, group_m);
-    const int w = q % band;
-    tm = first_m + w % gsz;
-    tn = w / gsz;
+    const int wb = q % band;
+    tm = first_m + wb % gsz;
+    tn = wb / gsz;
+    if (SPLIT == 2) {
+        tm = 2 * tm + quad / 2;
+        tn = 2 * tn + quad % 2;
+    }
 }
 
 // One ring stage: A tile, B tile and the scales of one group.  Distinct LDS objects (not one array
 // indexed by a run-time stage) let the compiler see that the stage being filled by the direct-to-LDS loads
 // is not the stage being read, so it does not drain the loads before every LDS read.
+template <int SPLIT>
 struct __attribute__((aligned(1024))) LargeStage {
-    uint8_t a[L_A_BYTES];
-    uint8_t b[L_B_BYTES];
-    float sa[L_BM];    // row scales of A
-    float sb[L_BN];    // row scales of B (WGrad)
+    uint8_t a[LargeCfg<SPLIT>::BM * BK];
+    uint8_t b[LargeCfg<SPLIT>::BN * BK];
+    float sa[LargeCfg<SPLIT>::BM];    // row scales of A
+    float sb[LargeCfg<SPLIT>::BN];    // row scales of B (WGrad)
 };
 
 // Per-tile values shared by the block: output tile coordinates and the buffer descriptors of the tile's
@@ -96,43 +123,54 @@ struct __attribute__((aligned(1024))) LargeStage {
 struct TileCtx {
     int tmi, tni;          // tile row / column
     int i0, j0;            // first output row / column
-    rsrc_t ra, rb;         // A rows i0 .. i0+255, B rows j0 .. j0+255 (clipped to I, J)
+    rsrc_t ra, rb;         // A rows i0 .. i0+BM-1, B rows j0 .. j0+BN-1 (clipped to I, J)
     rsrc_t rsa, rsb;       // A-row scales from i0; B-row scales from j0 (row-scaled B only)
 };
 
-template <bool ROW_SCALED_B>
-__global__ __launch_bounds__(L_THREADS, 1) void gemm_large_kernel(
+template <bool ROW_SCALED_B, int SPLIT>
+__global__ __launch_bounds__(L_THREADS, SPLIT) void gemm_large_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ As, const uint8_t* __restrict__ B,
     const float* __restrict__ Bs, uint16_t* __restrict__ Cout, int64_t I, int64_t J, int64_t Kc, int64_t sbj,
-    int64_t sbg, int tiles_m, int tiles_n) {
+    int64_t sbg, int tiles_m, int tiles_n, int q_begin, int q_count, int qrows) {
+    using Cfg = LargeCfg<SPLIT>;
+    constexpr int BM = Cfg::BM, BN = Cfg::BN, WROWS = Cfg::WROWS, WCOLS = Cfg::WCOLS, TM = Cfg::TM, TN = Cfg::TN;
+    typedef LargeStage<SPLIT> Stage;
     // 2-deep ring: while group g is multiplied, the next group is in flight.
-    __shared__ LargeStage stage0, stage1;
+    __shared__ Stage stage0, stage1;
 
     const int t = threadIdx.x, lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);     // wave-uniform, kept in scalar registers
-    const int wm = wave >> 2, wn = wave & 3;                      // wave tile: rows wm*128.., cols wn*64..
+    const int wm = wave >> 2, wn = wave & 3;                      // wave tile: rows wm*WROWS.., cols wn*WCOLS..
     const int G = (int)(Kc / BK);
-    const int T = tiles_m * tiles_n;
+    const int T = SPLIT == 1 ? q_count : q_count * 2 * qrows;      // work items (tiles) of this call
     // Persistent blocks: block b computes tiles b, b + gridDim.x, ... one after the other; the ring and its
     // prefetch run on across tile boundaries, and a tile's output is stored while the next tile's first
-    // group is multiplied (row of tiles tm just before that row's first promotion).  Every block has at least one tile (grid <= number of tiles).
+    // group is multiplied (row of tiles tm just before that row's first promotion).  Every block has at least
+    // one tile (grid <= number of tiles).
     const int nsteps = ((T - 1 - (int)blockIdx.x) / (int)gridDim.x + 1) * G;
 
     auto tile_ctx = [&](int pid) __attribute__((always_inline)) -> TileCtx {
         TileCtx c;
         int tm_, tn_;
-        tile_of_block(pid, tiles_m, tiles_n, tm_, tn_);
+        tile_of_work<SPLIT>(pid, tiles_m, tiles_n, q_begin, q_count, qrows, tm_, tn_);
         // the tile index is block-uniform; the integer divisions above run on the vector unit, so say so
         c.tmi = __builtin_amdgcn_readfirstlane(tm_);
         c.tni = __builtin_amdgcn_readfirstlane(tn_);
-        c.i0 = c.tmi * L_BM;
-        c.j0 = c.tni * L_BN;
-        // 32-bit scalar arithmetic: all dims are < 2^31 and operand bands < 2^31 bytes
-        const int rows_a = min((int)I - c.i0, L_BM), rows_b = min((int)J - c.j0, L_BN);
+        c.i0 = c.tmi * BM;
+        c.j0 = c.tni * BN;
+        // 32-bit scalar arithmetic: all dims are < 2^31 and operand bands < 2^31 bytes.  A 128 x 128 quarter of a
+        // 256 x 256 tile can lie wholly past I or J: its descriptors are then empty (loads read zero) and none of
+        // its outputs is stored.  The clamps compile to a vector median instruction; readfirstlane returns the
+        // (uniform) results to scalar registers, so the descriptors stay scalar (in vector registers every buffer
+        // load would be wrapped in a loop over the distinct descriptors of the wave).
+        const int rows_a = __builtin_amdgcn_readfirstlane(max(0, min((int)I - c.i0, BM)));
+        const int rows_b = __builtin_amdgcn_readfirstlane(max(0, min((int)J - c.j0, BN)));
+        const int sa_bytes = __builtin_amdgcn_readfirstlane(max(0, G * (int)I - c.i0) * 4);
+        const int sb_bytes = ROW_SCALED_B ? __builtin_amdgcn_readfirstlane(max(0, G * (int)J - c.j0) * 4) : 0;
         c.ra = make_rsrc(A + (int64_t)c.i0 * Kc, rows_a * (int)Kc);
         c.rb = make_rsrc(B + (int64_t)c.j0 * Kc, rows_b * (int)Kc);
-        c.rsa = make_rsrc(As + c.i0, (G * (int)I - c.i0) * 4);
-        c.rsb = make_rsrc(Bs + (ROW_SCALED_B ? c.j0 : 0), ROW_SCALED_B ? (G * (int)J - c.j0) * 4 : 0);
+        c.rsa = make_rsrc(As + c.i0, sa_bytes);
+        c.rsb = make_rsrc(Bs + (ROW_SCALED_B ? c.j0 : 0), sb_bytes);
         return c;
     };
 
@@ -149,40 +187,40 @@ __global__ __launch_bounds__(L_THREADS, 1) void gemm_large_kernel(
     const int ooff = (int)(r0 * (uint32_t)Kc + (((lane & 7) ^ swz(r0)) << 4));
     const int cstep = 64 * (int)Kc;
     const int os = ((wave & 3) * 64 + lane) * 4;
-    auto issue_part = [&](int c, const TileCtx& tc, int g, LargeStage& S) __attribute__((always_inline)) {
+    auto issue_part = [&](int c, const TileCtx& tc, int g, Stage& S) __attribute__((always_inline)) {
         if (c == 0) {
-            if (wave < 4) JETFP8_BUFFER_LOAD_LDS(tc.rsa, (lds_void*)&S.sa[wave * 64], 4, os, g * (int)I * 4);
-            else if (ROW_SCALED_B)
+            if (wave < Cfg::PA) JETFP8_BUFFER_LOAD_LDS(tc.rsa, (lds_void*)&S.sa[wave * 64], 4, os, g * (int)I * 4);
+            else if (ROW_SCALED_B && wave >= 4 && wave - 4 < Cfg::PB)
                 JETFP8_BUFFER_LOAD_LDS(tc.rsb, (lds_void*)&S.sb[(wave - 4) * 64], 4, os, g * (int)J * 4);
         }
         const int go = g * BK + c * cstep;
-        JETFP8_BUFFER_LOAD_LDS(tc.ra, (lds_void*)(&S.a[(c * 8 + wave) * 1024]), 16, ooff, go);
-        JETFP8_BUFFER_LOAD_LDS(tc.rb, (lds_void*)(&S.b[(c * 8 + wave) * 1024]), 16, ooff, go);
+        if (c < Cfg::PA) JETFP8_BUFFER_LOAD_LDS(tc.ra, (lds_void*)(&S.a[(c * 8 + wave) * 1024]), 16, ooff, go);
+        if (c < Cfg::PB) JETFP8_BUFFER_LOAD_LDS(tc.rb, (lds_void*)(&S.b[(c * 8 + wave) * 1024]), 16, ooff, go);
     };
 
-    v4f acc[8][4];
+    v4f acc[TM][TN];
 #pragma unroll
-    for (int a = 0; a < 8; ++a)
+    for (int a = 0; a < TM; ++a)
 #pragma unroll
-        for (int b = 0; b < 4; ++b) acc[a][b] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
+        for (int b = 0; b < TN; ++b) acc[a][b] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
 
     const int qc4 = 4 * (lane >> 4);       // first of the 4 output columns of this lane inside a 16x16 tile
     // Fragment bytes of this lane: row (lane & 15) of each 16-row tile, logical chunks cp and cp + 1.  The
     // tile's first row is a multiple of 16, so the swizzle depends on (lane & 15) only and consecutive
     // tiles are 2048 bytes apart: one base offset per chunk, tiles by immediate offsets.
     const uint32_t rl = lane & 15, cp = 2 * (lane >> 4), sw = swz(rl);
-    const uint32_t fa0 = (wm * 128 + rl) * BK + ((cp ^ sw) << 4), fa1 = (wm * 128 + rl) * BK + (((cp + 1) ^ sw) << 4);
-    const uint32_t fb0 = (wn * 64 + rl) * BK + ((cp ^ sw) << 4), fb1 = (wn * 64 + rl) * BK + (((cp + 1) ^ sw) << 4);
+    const uint32_t fa0 = (wm * WROWS + rl) * BK + ((cp ^ sw) << 4), fa1 = (wm * WROWS + rl) * BK + (((cp + 1) ^ sw) << 4);
+    const uint32_t fb0 = (wn * WCOLS + rl) * BK + ((cp ^ sw) << 4), fb1 = (wn * WCOLS + rl) * BK + (((cp + 1) ^ sw) << 4);
 
     // Output of one row of 16x16 tiles: bf16, round to nearest even; each lane writes 4 consecutive columns
     // (8 bytes) per tile.  J is a multiple of 128, so a lane's 4 columns are either all inside J or all
     // outside.  The accumulators of the row are cleared for the next tile.
     auto store_row = [&](int tm, int i0, int j0) __attribute__((always_inline)) {
-        const int64_t r = i0 + wm * 128 + tm * 16 + rl;
+        const int64_t r = i0 + wm * WROWS + tm * 16 + rl;
         if (r < I) {
 #pragma unroll
-            for (int tn = 0; tn < 4; ++tn) {
-                const int64_t c = j0 + wn * 64 + tn * 16 + qc4;
+            for (int tn = 0; tn < TN; ++tn) {
+                const int64_t c = j0 + wn * WCOLS + tn * 16 + qc4;
                 if (c < J) {
                     uint2 w;
                     w.x = f32_to_bf16_rne(acc[tm][tn][0]) | (f32_to_bf16_rne(acc[tm][tn][1]) << 16);
@@ -192,7 +230,7 @@ __global__ __launch_bounds__(L_THREADS, 1) void gemm_large_kernel(
             }
         }
 #pragma unroll
-        for (int tn = 0; tn < 4; ++tn) acc[tm][tn] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
+        for (int tn = 0; tn < TN; ++tn) acc[tm][tn] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
     };
 
     // compute cursor (tile, group) and issue cursor (one step ahead)
@@ -214,7 +252,7 @@ __global__ __launch_bounds__(L_THREADS, 1) void gemm_large_kernel(
     // a scalar load in flight).
     const rsrc_t rbs = make_rsrc(Bs, ROW_SCALED_B ? 0 : (int)(J / 128) * G * 4);
     auto load_sb = [&](int j0, int g) __attribute__((always_inline)) -> float {
-        const int bblk = min((j0 + wn * 64) / 128, (int)(J / 128) - 1);
+        const int bblk = min((j0 + wn * WCOLS) / 128, (int)(J / 128) - 1);
         return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rbs, (bblk * (int)sbj + g * (int)sbg) * 4, 0, 0));
     };
     float sbv_cur = 0.0f, sbv_nxt = 0.0f;
@@ -222,7 +260,7 @@ __global__ __launch_bounds__(L_THREADS, 1) void gemm_large_kernel(
     // One step: wait for the current group's stage, store the previous tile at a tile's first group,
     // multiply, and (during the first row tiles) refill the other stage (read one step ago) with the next
     // group, of this tile or of the block's next tile.
-    auto step = [&](int s, LargeStage& S, LargeStage& refill) __attribute__((always_inline)) {
+    auto step = [&](int s, Stage& S, Stage& refill) __attribute__((always_inline)) {
         __builtin_amdgcn_sched_barrier(0);   // keep each group's code in place (bounded register pressure)
         // this wave's loads of this group landed, its LDS reads of the previous one returned and its
         // stores of the previous tile completed; then every wave of the block is past that point
@@ -238,7 +276,7 @@ __global__ __launch_bounds__(L_THREADS, 1) void gemm_large_kernel(
         const bool flush = !ROW_SCALED_B && first_of_tile;
         if (ROW_SCALED_B && first_of_tile) {
 #pragma unroll
-            for (int tm = 0; tm < 8; ++tm) store_row(tm, prev_i0, prev_j0);
+            for (int tm = 0; tm < TM; ++tm) store_row(tm, prev_i0, prev_j0);
         }
         // block-scaled B: one scale per (128-block of B rows, group); a wave's 64 columns lie in one block.
         // Columns past J (last tile when J is an odd multiple of 128) use the last block: never stored.
@@ -246,21 +284,21 @@ __global__ __launch_bounds__(L_THREADS, 1) void gemm_large_kernel(
 
         // The matrix op takes the B fragment as its first operand, so lane l holds output row (l & 15) of
         // each 16-row tile and the 4 consecutive columns 4 * (l >> 4) .. +3: one A-row scale per tile.
-        float s1[8];
-        const float* sar = S.sa + (wm * 128 + (int)rl);     // tiles by immediate offsets
+        float s1[TM];
+        const float* sar = S.sa + (wm * WROWS + (int)rl);   // tiles by immediate offsets
 #pragma unroll
-        for (int tm = 0; tm < 8; ++tm) {
+        for (int tm = 0; tm < TM; ++tm) {
             s1[tm] = sar[tm * 16];
             if (!ROW_SCALED_B) s1[tm] = s1[tm] * sbv;            // s = fl32(sa * sb)
         }
-        v4f sb4[4];
+        v4f sb4[TN];
         if (ROW_SCALED_B) {
 #pragma unroll
-            for (int tn = 0; tn < 4; ++tn) sb4[tn] = *reinterpret_cast<const v4f*>(S.sb + (wn * 64 + qc4) + tn * 16);
+            for (int tn = 0; tn < TN; ++tn) sb4[tn] = *reinterpret_cast<const v4f*>(S.sb + (wn * WCOLS + qc4) + tn * 16);
         }
-        v8i bfr[4];
+        v8i bfr[TN];
 #pragma unroll
-        for (int tn = 0; tn < 4; ++tn) {
+        for (int tn = 0; tn < TN; ++tn) {
             const uint4 lo = *reinterpret_cast<const uint4*>(&S.b[fb0 + tn * 2048]);
             const uint4 hi = *reinterpret_cast<const uint4*>(&S.b[fb1 + tn * 2048]);
             bfr[tn] = (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
@@ -277,7 +315,7 @@ __global__ __launch_bounds__(L_THREADS, 1) void gemm_large_kernel(
             float srow = s1[tm];
             if (ROW_SCALED_B) asm volatile("" : "+v"(srow));
 #pragma unroll
-            for (int tn = 0; tn < 4; ++tn)
+            for (int tn = 0; tn < TN; ++tn)
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
                     const float sc = ROW_SCALED_B ? srow * sb4[tn][v] : srow;
@@ -286,32 +324,32 @@ __global__ __launch_bounds__(L_THREADS, 1) void gemm_large_kernel(
             // pin the promotion here: without this the compiler sinks it below later matrix ops and keeps
             // every group product alive at once
 #pragma unroll
-            for (int tn = 0; tn < 4; ++tn) asm volatile("" : "+v"(acc[tm][tn]));
+            for (int tn = 0; tn < TN; ++tn) asm volatile("" : "+v"(acc[tm][tn]));
         };
         // software pipeline over the 8 row tiles: the matrix ops of tile tm+1 run while tile tm is promoted.
         // Block-scaled B: one product buffer -- tile (tm-1, tn) is promoted right before (tm, tn) is issued
         // into the same registers (the other wave of the SIMD keeps the matrix unit busy meanwhile).
         // Row-scaled B: two buffers, a whole row of tiles issued before the previous row is promoted.
         if (!ROW_SCALED_B) {
-            v4f pp[4];
+            v4f pp[TN];
             v8i af = a_frag(0);
 #pragma unroll
-            for (int tn = 0; tn < 4; ++tn) pp[tn] = mfma_group(bfr[tn], af);
+            for (int tn = 0; tn < TN; ++tn) pp[tn] = mfma_group(bfr[tn], af);
 #pragma unroll
-            for (int tm = 1; tm < 8; ++tm) {
+            for (int tm = 1; tm < TM; ++tm) {
                 af = a_frag(tm);
-                if (tm <= 4 && refill_next) issue_part(tm - 1, iss, ig, refill);
+                if (tm <= Cfg::PARTS && refill_next) issue_part(tm - 1, iss, ig, refill);
                 if (tm == 1 && refill_next) sbv_nxt = load_sb(iss.j0, ig);
                 __builtin_amdgcn_sched_barrier(0);
                 // Each SIMD runs one wave of each half (wm = 0, 1).  Issue arbitration favours the older wave
                 // (wm = 0), which then reaches the step's barrier well before its partner and leaves the matrix
                 // unit to a single wave; raising the younger wave's priority for the first half of the step
                 // evens out their progress.
-                if (wm == 1 && tm < 4) __builtin_amdgcn_s_setprio(1);
+                if (wm == 1 && tm < TM / 2) __builtin_amdgcn_s_setprio(1);
                 else __builtin_amdgcn_s_setprio(0);
                 if (flush) store_row(tm - 1, prev_i0, prev_j0);
 #pragma unroll
-                for (int tn = 0; tn < 4; ++tn) {
+                for (int tn = 0; tn < TN; ++tn) {
 #pragma unroll
                     for (int v = 0; v < 4; ++v) acc[tm - 1][tn][v] = fmaf(pp[tn][v], s1[tm - 1], acc[tm - 1][tn][v]);
                     asm volatile("" : "+v"(acc[tm - 1][tn]));
@@ -319,38 +357,38 @@ __global__ __launch_bounds__(L_THREADS, 1) void gemm_large_kernel(
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
-            if (flush) store_row(7, prev_i0, prev_j0);
+            if (flush) store_row(TM - 1, prev_i0, prev_j0);
 #pragma unroll
-            for (int tn = 0; tn < 4; ++tn) {
+            for (int tn = 0; tn < TN; ++tn) {
 #pragma unroll
-                for (int v = 0; v < 4; ++v) acc[7][tn][v] = fmaf(pp[tn][v], s1[7], acc[7][tn][v]);
-                asm volatile("" : "+v"(acc[7][tn]));
+                for (int v = 0; v < 4; ++v) acc[TM - 1][tn][v] = fmaf(pp[tn][v], s1[TM - 1], acc[TM - 1][tn][v]);
+                asm volatile("" : "+v"(acc[TM - 1][tn]));
             }
             __builtin_amdgcn_sched_barrier(0);
         } else {
-            v4f pa[4], pb[4];
+            v4f pa[TN], pb[TN];
             v8i af = a_frag(0);
 #pragma unroll
-            for (int tn = 0; tn < 4; ++tn) pa[tn] = mfma_group(bfr[tn], af);
+            for (int tn = 0; tn < TN; ++tn) pa[tn] = mfma_group(bfr[tn], af);
 #pragma unroll
-            for (int tm = 1; tm < 8; ++tm) {
+            for (int tm = 1; tm < TM; ++tm) {
                 af = a_frag(tm);
-                if (tm <= 4 && refill_next) issue_part(tm - 1, iss, ig, refill);
+                if (tm <= Cfg::PARTS && refill_next) issue_part(tm - 1, iss, ig, refill);
                 __builtin_amdgcn_sched_barrier(0);
-                if (wm == 1 && tm < 4) __builtin_amdgcn_s_setprio(1);
+                if (wm == 1 && tm < TM / 2) __builtin_amdgcn_s_setprio(1);
                 else __builtin_amdgcn_s_setprio(0);
                 if (tm & 1) {
 #pragma unroll
-                    for (int tn = 0; tn < 4; ++tn) pb[tn] = mfma_group(bfr[tn], af);
+                    for (int tn = 0; tn < TN; ++tn) pb[tn] = mfma_group(bfr[tn], af);
                     promote(tm - 1, pa);
                 } else {
 #pragma unroll
-                    for (int tn = 0; tn < 4; ++tn) pa[tn] = mfma_group(bfr[tn], af);
+                    for (int tn = 0; tn < TN; ++tn) pa[tn] = mfma_group(bfr[tn], af);
                     promote(tm - 1, pb);
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
-            promote(7, pb);
+            promote(TM - 1, pb);
             __builtin_amdgcn_sched_barrier(0);
         }
         if (refill_next) {
@@ -368,7 +406,7 @@ __global__ __launch_bounds__(L_THREADS, 1) void gemm_large_kernel(
     };
 
 #pragma unroll
-    for (int c = 0; c < 4; ++c) issue_part(c, iss, ig, stage0);
+    for (int c = 0; c < Cfg::PARTS; ++c) issue_part(c, iss, ig, stage0);
     if (!ROW_SCALED_B) sbv_cur = load_sb(iss.j0, ig);
     advance_issue();
     int s = 0;
@@ -378,7 +416,7 @@ __global__ __launch_bounds__(L_THREADS, 1) void gemm_large_kernel(
     }
     if (s < nsteps) step(s, stage0, stage1);
 #pragma unroll
-    for (int tm = 0; tm < 8; ++tm) store_row(tm, prev_i0, prev_j0);
+    for (int tm = 0; tm < TM; ++tm) store_row(tm, prev_i0, prev_j0);
 }
 
 // Compute units of the current device (one persistent block per compute unit: a block's LDS ring
@@ -590,15 +628,40 @@ static hipError_t launch_decode(const uint8_t* A, const float* As, const uint8_t
     return hipGetLastError();
 }
 
+template <bool ROW_SCALED_B, int SPLIT>
+static hipError_t launch_large_part(const uint8_t* A, const float* As, const uint8_t* B, const float* Bs, uint16_t* C,
+                                    int64_t I, int64_t J, int64_t Kc, int64_t sbj, int64_t sbg, int tiles_m,
+                                    int tiles_n, int q_begin, int q_count, int qrows, int max_blocks, hipStream_t st) {
+    const int items = q_count * (SPLIT == 1 ? 1 : 2 * qrows);
+    const int grid = min(items, max_blocks);
+    hipLaunchKernelGGL((gemm_large_kernel<ROW_SCALED_B, SPLIT>), dim3(grid), dim3(L_THREADS), 0, st, A, As, B, Bs, C,
+                       I, J, Kc, sbj, sbg, tiles_m, tiles_n, q_begin, q_count, qrows);
+    return hipGetLastError();
+}
+
+// Large-M schedule.  T tiles of 256 x 256 run on one persistent block per CU (ceil(T / CUs) rounds).  When T is
+// at most half the CU count, the whole call runs on 128 x 128 quarter tiles instead (two blocks per CU; for at
+// most 128 rows only the upper quarters), so that more CUs share the work.  When the last round is at most half
+// full, that round's R tiles run as 4R quarter tiles after the full rounds, at up to two blocks per CU.  Every
+// output element goes through the same operation sequence in every variant, so the bits do not change.
 template <bool ROW_SCALED_B>
 static hipError_t launch_large(const uint8_t* A, const float* As, const uint8_t* B, const float* Bs, uint16_t* C,
                                int64_t I, int64_t J, int64_t Kc, int64_t sbj, int64_t sbg, hipStream_t st) {
-    const int tiles_m = (int)((I + L_BM - 1) / L_BM), tiles_n = (int)((J + L_BN - 1) / L_BN);
-    const int tiles = tiles_m * tiles_n;
-    const int grid = min(tiles, device_cu_count());
-    hipLaunchKernelGGL(gemm_large_kernel<ROW_SCALED_B>, dim3(grid), dim3(L_THREADS), 0, st, A, As, B, Bs, C, I,
-                       J, Kc, sbj, sbg, tiles_m, tiles_n);
-    return hipGetLastError();
+    const int tiles_m = (int)((I + 255) / 256), tiles_n = (int)((J + 255) / 256);
+    const int T = tiles_m * tiles_n;
+    const int cus = device_cu_count();
+    if (2 * T <= cus)
+        return launch_large_part<ROW_SCALED_B, 2>(A, As, B, Bs, C, I, J, Kc, sbj, sbg, tiles_m, tiles_n, 0, T,
+                                                  I <= 128 ? 1 : 2, 2 * cus, st);
+    const int R = T % cus;
+    if (T > cus && R > 0 && 2 * R <= cus) {
+        hipError_t e = launch_large_part<ROW_SCALED_B, 1>(A, As, B, Bs, C, I, J, Kc, sbj, sbg, tiles_m, tiles_n, 0,
+                                                          T - R, 1, cus, st);
+        if (e != hipSuccess) return e;
+        return launch_large_part<ROW_SCALED_B, 2>(A, As, B, Bs, C, I, J, Kc, sbj, sbg, tiles_m, tiles_n, T - R, R, 2,
+                                                  2 * cus, st);
+    }
+    return launch_large_part<ROW_SCALED_B, 1>(A, As, B, Bs, C, I, J, Kc, sbj, sbg, tiles_m, tiles_n, 0, T, 1, cus, st);
 }
 
 hipError_t launch_gemm_block_scaled_b(const uint8_t* A, const float* As, const uint8_t* B, const float* Bs,

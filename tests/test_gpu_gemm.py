@@ -84,15 +84,16 @@ def test_wgrad_parity(jf, orc, M, N, K):
 
 
 def test_rows_are_bitwise_independent_of_M(jf):
-    """Decode (M=1), decode batches (M=20, 32, 48, 64: the small-M kernel with 1, 2 and 4 row tiles) and a
-    training batch (the large-tile kernel) produce bitwise identical rows."""
+    """Decode (M=1), decode batches (M=20, 32, 48, 64: the small-M kernel with 1, 2 and 4 row tiles; M=96, 128: the
+    upper 128 x 128 quarter tiles) and a training batch (M=300: 128 x 128 quarter tiles) produce bitwise identical
+    rows."""
     import torch
     M, N, K = 300, 256, 512
     xb, wb = _x(M, K, 41), _w(N, K, 42)
     wq, ws, _ = jf.quantize_blocks(bits_to_dev(wb))
     x = bits_to_dev(xb)
     y_all, _ = jf.linear_forward(x, wq, ws)
-    batches = {m: jf.linear_forward(x[100:100 + m].contiguous(), wq, ws)[0] for m in (20, 32, 48, 64)}
+    batches = {m: jf.linear_forward(x[100:100 + m].contiguous(), wq, ws)[0] for m in (20, 32, 48, 64, 96, 128)}
     ones = [jf.linear_forward(x[r:r + 1].contiguous(), wq, ws)[0] for r in (0, 131, 299)]
     torch.cuda.synchronize()
     full = dev_to_bits(y_all)
@@ -192,3 +193,57 @@ def test_degenerate_groups_fwd_dgrad_wgrad(jf, orc):
     got = dev_to_bits(dw)
     assert np.array_equal(got, orc.gemm_wgrad(odc, odsc, oxc, oxsc, mode=orc.MFMA))
     assert not got[:128].any()                   # dW rows of the all-zero dY columns
+
+
+def _tiles_and_rounds(M, N):
+    T = ((M + 255) // 256) * ((N + 255) // 256)
+    return T, T % 256
+
+
+def test_large_tiles_and_tail_round_equal_quarter_tiles(jf, orc):
+    """Schedules of the large-M kernel against each other, bit for bit (each output element goes through the same
+    operation sequence in all of them):
+      * M = 8192, N = 2048: 256 tiles of 256 x 256, one full round (no quarter tiles);
+      * M = 4352, N = 4096: 272 tiles, one full round and a last round of 16 tiles run as 64 quarter tiles;
+    both against the same rows computed 128 at a time (quarter tiles only) and, on sampled rows, the oracle."""
+    import torch
+    K = 512
+    for M, N, seed in ((8192, 2048, 91), (4352, 4096, 93)):
+        T, R = _tiles_and_rounds(M, N)
+        print(f"M={M} N={N}: {T} tiles of 256 x 256, last round {R}", flush=True)
+        xb, wb = _x(M, K, seed), _w(N, K, seed + 1)
+        wq, ws, _ = jf.quantize_blocks(bits_to_dev(wb))
+        x = bits_to_dev(xb)
+        y, (xq, xs) = jf.linear_forward(x, wq, ws)
+        parts = [jf.gemm_fwd(xq[r:r + 128].contiguous(), xs[:, r:r + 128].contiguous(), wq, ws) for r in range(0, M, 128)]
+        torch.cuda.synchronize()
+        full = dev_to_bits(y)
+        assert np.array_equal(full, np.concatenate([dev_to_bits(p) for p in parts])), (M, N)
+        rows = np.array([0, 1, 2047, M - 129, M - 1])
+        oxq, oxs = orc.quantize_rows(xb[rows])
+        owq, ows = orc.quantize_blocks(wb)
+        check_gemm_parity(f"large-M fwd {M}x{N}x{K} sampled rows", full[rows],
+                          orc.gemm_fwd(oxq, oxs, owq, ows, mode=orc.MFMA), orc.gemm_fwd(oxq, oxs, owq, ows, mode=orc.EXACT))
+        del y, parts, x
+
+
+def test_wgrad_tail_round_equal_row_slabs(jf, orc):
+    """WGrad with N = 4352, K = 4096 (272 tiles: a full round and 16 tiles as quarter tiles) against the same dW
+    rows computed 128 at a time (quarter tiles only), bit for bit, and sampled dW rows against the oracle."""
+    import torch
+    M, N, K = 256, 4352, 4096
+    dyb, xb = _dy(M, N, 95), _x(M, K, 96)
+    dyqT, dysT = jf.quantize_cols_t(bits_to_dev(dyb))
+    xqT, xsT = jf.quantize_cols_t(bits_to_dev(xb))
+    dw = jf.gemm_wgrad(dyqT, dysT, xqT, xsT)
+    slabs = [jf.gemm_wgrad(dyqT[n:n + 128].contiguous(), dysT[:, n:n + 128].contiguous(), xqT, xsT)
+             for n in range(0, N, 128)]
+    torch.cuda.synchronize()
+    full = dev_to_bits(dw)
+    assert np.array_equal(full, np.concatenate([dev_to_bits(p) for p in slabs]))
+    rows = np.array([0, 129, N - 1])
+    odq, ods = orc.quantize_cols(dyb)
+    oxq, oxs = orc.quantize_cols(xb)
+    check_gemm_parity(f"wgrad {M}x{N}x{K} sampled dW rows", full[rows],
+                      orc.gemm_wgrad(odq, ods, oxq, oxs, rows=rows, mode=orc.MFMA),
+                      orc.gemm_wgrad(odq, ods, oxq, oxs, rows=rows, mode=orc.EXACT))
