@@ -147,7 +147,9 @@ __global__ __launch_bounds__(L_THREADS, SPLIT) void gemm_large_kernel(
     // prefetch run on across tile boundaries, and a tile's output is stored while the next tile's first
     // group is multiplied (row of tiles tm just before that row's first promotion).  Every block has at least
     // one tile (grid <= number of tiles).
-    const int nsteps = ((T - 1 - (int)blockIdx.x) / (int)gridDim.x + 1) * G;
+    // (the division runs on the vector unit; readfirstlane marks the uniform result as scalar, so every condition
+    // derived from it stays a scalar branch)
+    const int nsteps = __builtin_amdgcn_readfirstlane(((T - 1 - (int)blockIdx.x) / (int)gridDim.x + 1) * G);
 
     auto tile_ctx = [&](int pid) __attribute__((always_inline)) -> TileCtx {
         TileCtx c;
@@ -267,7 +269,10 @@ __global__ __launch_bounds__(L_THREADS, SPLIT) void gemm_large_kernel(
         __builtin_amdgcn_s_setprio(0);
         __builtin_amdgcn_s_waitcnt(0);
         __builtin_amdgcn_s_barrier();
-        const bool refill_next = s + 1 < nsteps;   // the next step's group goes into the other stage
+        // The refill of the other stage is issued in every step, the last one included: there the issue cursor
+        // still points at a valid group (of the block's last tile) and nothing reads that stage any more.  A guard
+        // on it cost a vector select and compare per row tile (the compiler negates a uniform branch condition as
+        // a lane mask).  Flags below are scalar integers (readfirstlane) for the same reason.
         // first group of a tile after the first: the previous tile's rows are stored one row of tiles at a
         // time, each just before its first promotion, so the stores spread over the group.  Row-scaled B
         // (long contraction, few tiles per block, no register room in the hot loop) stores the whole tile
@@ -338,8 +343,8 @@ __global__ __launch_bounds__(L_THREADS, SPLIT) void gemm_large_kernel(
 #pragma unroll
             for (int tm = 1; tm < TM; ++tm) {
                 af = a_frag(tm);
-                if (tm <= Cfg::PARTS && refill_next) issue_part(tm - 1, iss, ig, refill);
-                if (tm == 1 && refill_next) sbv_nxt = load_sb(iss.j0, ig);
+                if (tm <= Cfg::PARTS) issue_part(tm - 1, iss, ig, refill);
+                if (tm == 1) sbv_nxt = load_sb(iss.j0, ig);
                 __builtin_amdgcn_sched_barrier(0);
                 // Each SIMD runs one wave of each half (wm = 0, 1).  Issue arbitration favours the older wave
                 // (wm = 0), which then reaches the step's barrier well before its partner and leaves the matrix
@@ -373,7 +378,7 @@ __global__ __launch_bounds__(L_THREADS, SPLIT) void gemm_large_kernel(
 #pragma unroll
             for (int tm = 1; tm < TM; ++tm) {
                 af = a_frag(tm);
-                if (tm <= Cfg::PARTS && refill_next) issue_part(tm - 1, iss, ig, refill);
+                if (tm <= Cfg::PARTS) issue_part(tm - 1, iss, ig, refill);
                 __builtin_amdgcn_sched_barrier(0);
                 if (wm == 1 && tm < TM / 2) __builtin_amdgcn_s_setprio(1);
                 else __builtin_amdgcn_s_setprio(0);
@@ -391,10 +396,8 @@ __global__ __launch_bounds__(L_THREADS, SPLIT) void gemm_large_kernel(
             promote(TM - 1, pb);
             __builtin_amdgcn_sched_barrier(0);
         }
-        if (refill_next) {
-            advance_issue();
-            if (!ROW_SCALED_B) sbv_cur = sbv_nxt;
-        }
+        advance_issue();
+        if (!ROW_SCALED_B) sbv_cur = sbv_nxt;
         // advance the compute cursor
         if (++cg == G) {
             cg = 0;
@@ -415,6 +418,8 @@ __global__ __launch_bounds__(L_THREADS, SPLIT) void gemm_large_kernel(
         step(s + 1, stage1, stage0);
     }
     if (s < nsteps) step(s, stage0, stage1);
+    // the last step's refill loads are still in flight: they must land before the block's LDS is released
+    __builtin_amdgcn_s_waitcnt(0);
 #pragma unroll
     for (int tm = 0; tm < TM; ++tm) store_row(tm, prev_i0, prev_j0);
 }
@@ -458,11 +463,13 @@ constexpr int D_SA_MAX = 8192;     // A-row scales kept in LDS: (contraction / 1
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
+// A and As address rows 0 .. I-1 of the call (row m of group g has its scale at As[g * sa_ld + m]), so a call can
+// cover a range of a larger batch's rows.
 template <int RT>
 __global__ __launch_bounds__(D_THREADS) void gemm_decode_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ As, const uint8_t* __restrict__ B,
     const float* __restrict__ Bs, uint16_t* __restrict__ Cout, int64_t I, int64_t J, int64_t Kc, int64_t sbj,
-    int64_t sbg) {
+    int64_t sbg, int64_t sa_ld) {
     // chunks in flight: RT = 2 keeps 2 (82 VGPRs, so two blocks share a CU: measured 4 % faster at 32 rows);
     // RT = 4 keeps 2 to fit its registers; deeper prefetch measured no faster
     constexpr int AHEAD = RT >= 2 ? 2 : D_AHEAD;
@@ -546,7 +553,10 @@ __global__ __launch_bounds__(D_THREADS) void gemm_decode_kernel(
 
     // the A-row scales of every group (the same for all slices) in LDS: sa_tab[g * I + m]; filled before the
     // first operand loads are issued, so waiting for it does not wait for them
-    for (int i = t; i < G * Ii; i += D_THREADS) sa_tab[i] = As[i];
+    for (int i = t; i < G * Ii; i += D_THREADS) {
+        const int g = i / Ii, m = i - g * Ii;
+        sa_tab[i] = As[(int64_t)g * sa_ld + m];
+    }
 #pragma unroll
     for (int k = 0; k < AHEAD; ++k) load_chunk(k, wf[k], af[k], swf[k]);
     // LDS writes done, then every wave is here (a plain barrier: the operand loads stay in flight)
@@ -619,13 +629,26 @@ __global__ __launch_bounds__(D_THREADS) void gemm_decode_kernel(
 
 template <int RT>
 static hipError_t launch_decode(const uint8_t* A, const float* As, const uint8_t* B, const float* Bs, uint16_t* C,
-                                int64_t I, int64_t J, int64_t Kc, int64_t sbj, int64_t sbg, hipStream_t st) {
+                                int64_t I, int64_t J, int64_t Kc, int64_t sbj, int64_t sbg, int64_t sa_ld,
+                                hipStream_t st) {
     const int slices = (int)(J / 16);
     // persistent blocks: one per CU, two for RT = 2 (registers and LDS allow it, and it measured faster)
     const int grid = min(slices, (RT == 2 ? 2 : 1) * device_cu_count());
     hipLaunchKernelGGL(gemm_decode_kernel<RT>, dim3((unsigned)grid), dim3(D_THREADS), 0, st, A, As, B, Bs, C, I, J,
-                       Kc, sbj, sbg);
+                       Kc, sbj, sbg, sa_ld);
     return hipGetLastError();
+}
+
+// Rows r0 .. r0 + rows - 1 of a call with I rows on the small-M kernel (rows <= 64).
+static hipError_t launch_decode_rows(const uint8_t* A, const float* As, const uint8_t* B, const float* Bs,
+                                     uint16_t* C, int64_t I, int64_t r0, int64_t rows, int64_t J, int64_t Kc,
+                                     int64_t sbj, int64_t sbg, hipStream_t st) {
+    const uint8_t* a = A + r0 * Kc;
+    const float* as = As + r0;
+    uint16_t* c = C + r0 * J;
+    if (rows <= 16) return launch_decode<1>(a, as, B, Bs, c, rows, J, Kc, sbj, sbg, I, st);
+    if (rows <= 32) return launch_decode<2>(a, as, B, Bs, c, rows, J, Kc, sbj, sbg, I, st);
+    return launch_decode<4>(a, as, B, Bs, c, rows, J, Kc, sbj, sbg, I, st);
 }
 
 template <bool ROW_SCALED_B, int SPLIT>
@@ -668,10 +691,16 @@ hipError_t launch_gemm_block_scaled_b(const uint8_t* A, const float* As, const u
                                       uint16_t* C, int64_t I, int64_t J, int64_t Kc, int64_t sbj, int64_t sbg,
                                       hipStream_t st) {
     // decode sizes: the small-M schedule (same per-element sequence, so the same bits)
-    if (I <= 64 && (Kc / BK) * I <= D_SA_MAX) {
-        if (I <= 16) return launch_decode<1>(A, As, B, Bs, C, I, J, Kc, sbj, sbg, st);
-        if (I <= 32) return launch_decode<2>(A, As, B, Bs, C, I, J, Kc, sbj, sbg, st);
-        return launch_decode<4>(A, As, B, Bs, C, I, J, Kc, sbj, sbg, st);
+    if (I <= 64 && (Kc / BK) * I <= D_SA_MAX) return launch_decode_rows(A, As, B, Bs, C, I, 0, I, J, Kc, sbj, sbg, st);
+    // 65..128 rows with fewer output columns than contraction: the small-M kernel on the first 64 rows, then on
+    // the rest (the weights are read twice, but the 16-column slices keep every CU busy where the quarter tiles of
+    // the large kernel would number J / 128 only; measured down projection 14336 -> 4096 at 128 rows: 98 us
+    // against 125 us on quarter tiles).  Wider outputs use the quarter tiles (gate_up 4096 -> 28672: 46 us
+    // against 168 us).
+    if (I <= 128 && J < Kc && (Kc / BK) * 64 <= D_SA_MAX) {
+        const hipError_t e = launch_decode_rows(A, As, B, Bs, C, I, 0, 64, J, Kc, sbj, sbg, st);
+        if (e != hipSuccess) return e;
+        return launch_decode_rows(A, As, B, Bs, C, I, 64, I - 64, J, Kc, sbj, sbg, st);
     }
     return launch_large<false>(A, As, B, Bs, C, I, J, Kc, sbj, sbg, st);
 }

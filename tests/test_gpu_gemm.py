@@ -85,8 +85,8 @@ def test_wgrad_parity(jf, orc, M, N, K):
 
 def test_rows_are_bitwise_independent_of_M(jf):
     """Decode (M=1), decode batches (M=20, 32, 48, 64: the small-M kernel with 1, 2 and 4 row tiles; M=96, 128: the
-    upper 128 x 128 quarter tiles) and a training batch (M=300: 128 x 128 quarter tiles) produce bitwise identical
-    rows."""
+    small-M kernel on rows 0-63 and then on the rest, fewer output columns than contraction) and a training batch
+    (M=300: 128 x 128 quarter tiles) produce bitwise identical rows."""
     import torch
     M, N, K = 300, 256, 512
     xb, wb = _x(M, K, 41), _w(N, K, 42)
@@ -126,12 +126,13 @@ def test_repeat_runs_are_bitwise_identical(jf):
     assert all(np.array_equal(outs[0], o) for o in outs[1:])
 
 
-@pytest.mark.parametrize("m_small", [1, 17, 33])
+@pytest.mark.parametrize("m_small", [1, 17, 33, 100, 128])
 def test_decode_ragged_chunks_many_slices(jf, orc, m_small):
     """Small-M kernel (1, 2 and 4 row tiles) on a contraction of 11 groups (a full chunk of 8 and a partial
     one of 3) and 520 column slices (more than the persistent blocks, so the operand stream crosses slice
-    boundaries): forward and DGrad rows are bitwise equal to the same rows from the large-tile kernel, and the
-    forward matches the oracle within the stated tolerance."""
+    boundaries); 100 and 128 rows run on the upper 128 x 128 quarter tiles (more output columns than
+    contraction).  Forward and DGrad rows are bitwise equal to the same rows of a 300-row call, and the forward
+    matches the oracle within the stated tolerance."""
     import torch
     big, n_wide, k_ragged = 300, 8320, 1408
     xb, wb = _x(big, k_ragged, 71), _w(n_wide, k_ragged, 72)
