@@ -60,6 +60,9 @@ def parse():
                         "weights quantized beforehand) and print its own JSON line")
     p.add_argument("--decode-rows", type=int, default=None,
                    help="token rows of a decode step (default: the workload's 32)")
+    p.add_argument("--decode-rowmajor", action="store_true",
+                   help="decode over row-major FP8 weights (jetfp8_gemm_fwd) instead of the fragment order "
+                        "(JETFP8_BLOCKS_128x128_FRAG + jetfp8_gemm_fwd_frag, used up to 64 rows)")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="first run a 1 GiB device-to-device copy (known bytes) to scale rocprofv3 byte counters")
     return p.parse_args()
@@ -394,6 +397,7 @@ def decode_traffic(path=os.path.join(ROOT, "profiles", "decode_traffic.json")):
 def run_decode(args, torch, jf, workloads):
     wl = workloads.WORKLOADS["llama3_8b_decode_m32"]
     M = args.decode_rows or wl.M
+    frag = not args.decode_rowmajor and M <= 64
     u8, f32, bf = torch.uint8, torch.float32, torch.bfloat16
     lin = []
     for i, (name, K, N) in enumerate(wl.linears):
@@ -403,7 +407,7 @@ def run_decode(args, torch, jf, workloads):
         for _ in range(DECODE_COPIES):
             wq = torch.empty((N, K), dtype=u8, device=dev)
             ws = torch.empty((N // 128, K // 128), dtype=f32, device=dev)
-            jf.jetfp8_quantize(d["w"], N, K, jf.BLOCKS_128x128, wq, ws, None)
+            jf.jetfp8_quantize(d["w"], N, K, jf.BLOCKS_128x128_FRAG if frag else jf.BLOCKS_128x128, wq, ws, None)
             copies.append((wq, ws))
         del d["w"]
         lin.append(dict(name=name, K=K, N=N, x=d["x"], copies=copies,
@@ -421,7 +425,7 @@ def run_decode(args, torch, jf, workloads):
             if ev is not None:
                 a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 a.record(st)
-            jf.jetfp8_gemm_fwd(L["xq"], L["xs"], wq, ws, L["y"], M, N, K, st)
+            (jf.jetfp8_gemm_fwd_frag if frag else jf.jetfp8_gemm_fwd)(L["xq"], L["xs"], wq, ws, L["y"], M, N, K, st)
             if ev is not None:
                 b.record(st)
                 ev.append((L["name"], decode_gemm_bytes(M, N, K), a, b))
@@ -455,7 +459,8 @@ def run_decode(args, torch, jf, workloads):
                 f"W~N(0,0.02^2)); {DECODE_COPIES} weight copies cycled past the 256 MB MALL",
         "config": {"workload": wl.name if M == wl.M else f"llama3_8b_decode_m{M}", "tokens": M,
                    "linears": [{"name": n, "K": K, "N": N} for n, K, N in wl.linears],
-                   "step": "per linear: X rows quant (1x128), fwd GEMM against FP8 weights quantized beforehand"},
+                   "step": "per linear: X rows quant (1x128), fwd GEMM against FP8 weights quantized beforehand",
+                   "weights": "fragment order (jetfp8_gemm_fwd_frag)" if frag else "row-major (jetfp8_gemm_fwd)"},
         "roofline": {"bound": "hbm", "kernel": f"gemm_decode_kernel<{rt}>",
                      "achieved": round(gemm_bytes / (gemm_ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gemm_bytes / (gemm_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),

@@ -19,10 +19,10 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "lib", "libjetfp8.so")
 
 OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_MODE, ERR_HIP, ERR_VALUE = 0, -1, -2, -3, -4, -5, -6
-ROWS_1x128, COLS_128x1_T, BLOCKS_128x128 = 0, 1, 2
+ROWS_1x128, COLS_128x1_T, BLOCKS_128x128, BLOCKS_128x128_FRAG = 0, 1, 2, 3
 EXPORTED = ("jetfp8_quantize", "jetfp8_quantize_dual", "jetfp8_requantize_cols_t", "jetfp8_rmsnorm_quantize",
-            "jetfp8_swiglu_quantize", "jetfp8_gemm_fwd", "jetfp8_gemm_dgrad", "jetfp8_gemm_wgrad",
-            "jetfp8_status_string", "jetfp8_version")
+            "jetfp8_swiglu_quantize", "jetfp8_gemm_fwd", "jetfp8_gemm_fwd_frag", "jetfp8_gemm_dgrad",
+            "jetfp8_gemm_wgrad", "jetfp8_status_string", "jetfp8_version")
 
 _lib = None
 
@@ -52,7 +52,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.jetfp8_rmsnorm_quantize.argtypes = [vp, vp, i64, i64, ctypes.c_float, vp, vp, vp, vp, vp]
     L.jetfp8_swiglu_quantize.restype = c_int
     L.jetfp8_swiglu_quantize.argtypes = [vp, i64, i64, vp, vp, vp, vp]
-    for name in ("jetfp8_gemm_fwd", "jetfp8_gemm_dgrad", "jetfp8_gemm_wgrad"):
+    for name in ("jetfp8_gemm_fwd", "jetfp8_gemm_fwd_frag", "jetfp8_gemm_dgrad", "jetfp8_gemm_wgrad"):
         f = getattr(L, name)
         f.restype = c_int
         f.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp]
@@ -124,7 +124,7 @@ def jetfp8_quantize(src_bf16, rows: int, cols: int, mode: int, dst_codes, dst_sc
     L = load_library()
     bf, u8, f32 = _bf16_u8_f32()
     R, C = int(rows), int(cols)
-    if R >= 1 and C >= 1 and mode in (ROWS_1x128, COLS_128x1_T, BLOCKS_128x128):
+    if R >= 1 and C >= 1 and mode in (ROWS_1x128, COLS_128x1_T, BLOCKS_128x128, BLOCKS_128x128_FRAG):
         _need(src_bf16, (R, C), bf, "src_bf16")
         dev = src_bf16.device
         if mode == ROWS_1x128:
@@ -233,6 +233,14 @@ def jetfp8_gemm_fwd(xq, xs, wq, ws, y_bf16, M: int, N: int, K: int, stream=None)
                                                  int(M), int(N), int(K), _stream(stream)))
 
 
+def jetfp8_gemm_fwd_frag(xq, xs, wq_frag, ws, y_bf16, M: int, N: int, K: int, stream=None) -> None:
+    L = load_library()
+    M, N, K = int(M), int(N), int(K)
+    _check_gemm_operands(xq, xs, wq_frag, ws, y_bf16, (M, K), (K // 128, M), (N, K), (N // 128, K // 128), (M, N))
+    _check("jetfp8_gemm_fwd_frag", L.jetfp8_gemm_fwd_frag(_ptr(xq), _ptr(xs), _ptr(wq_frag), _ptr(ws), _ptr(y_bf16),
+                                                           int(M), int(N), int(K), _stream(stream)))
+
+
 def jetfp8_gemm_dgrad(dyq, dys, wqT, ws, dx_bf16, M: int, N: int, K: int, stream=None) -> None:
     L = load_library()
     M, N, K = int(M), int(N), int(K)
@@ -338,6 +346,27 @@ def quantize_blocks(w, transposed: bool = True, stream=None):
     qT = torch.empty((K, N), dtype=torch.uint8, device=w.device) if transposed else None
     jetfp8_quantize(w, N, K, BLOCKS_128x128, q, s, qT, stream)
     return (q, s, qT) if transposed else (q, s)
+
+
+def quantize_blocks_frag(w, stream=None):
+    """128x128 blocks with the codes in the fragment order of the decode GEMM: w bf16 [N, K] -> codes uint8 [N, K]
+    (the same bytes as quantize_blocks, permuted: see JETFP8_BLOCKS_128x128_FRAG), scales [N/128, K/128]."""
+    import torch
+    _dt(w, torch.bfloat16, "w")
+    N, K = w.shape
+    q = torch.empty((N, K), dtype=torch.uint8, device=w.device)
+    s = torch.empty((N // 128, K // 128), dtype=torch.float32, device=w.device)
+    jetfp8_quantize(w, N, K, BLOCKS_128x128_FRAG, q, s, None, stream)
+    return q, s
+
+
+def gemm_fwd_frag(xq, xs, wq_frag, ws, stream=None):
+    import torch
+    M, K = xq.shape
+    N = wq_frag.shape[0]
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=xq.device)
+    jetfp8_gemm_fwd_frag(xq, xs, wq_frag, ws, y, M, N, K, stream)
+    return y
 
 
 def gemm_fwd(xq, xs, wq, ws, stream=None):

@@ -37,7 +37,7 @@ int check_gemm_extent(int64_t I, int64_t J, int64_t Kc) {
 
 extern "C" {
 
-int jetfp8_version(void) { return 301; }
+int jetfp8_version(void) { return 302; }
 
 const char* jetfp8_status_string(int status) {
     switch (status) {
@@ -54,9 +54,10 @@ const char* jetfp8_status_string(int status) {
 
 int jetfp8_quantize(const void* src_bf16, int64_t rows, int64_t cols, int mode, uint8_t* dst_codes,
                     float* dst_scales, uint8_t* dst_codes_t, void* stream) {
-    if (mode != JETFP8_ROWS_1x128 && mode != JETFP8_COLS_128x1_T && mode != JETFP8_BLOCKS_128x128)
+    if (mode != JETFP8_ROWS_1x128 && mode != JETFP8_COLS_128x1_T && mode != JETFP8_BLOCKS_128x128 &&
+        mode != JETFP8_BLOCKS_128x128_FRAG)
         return JETFP8_ERR_MODE;
-    if (dst_codes_t && mode != JETFP8_BLOCKS_128x128) return JETFP8_ERR_MODE;
+    if (dst_codes_t && mode != JETFP8_BLOCKS_128x128 && mode != JETFP8_BLOCKS_128x128_FRAG) return JETFP8_ERR_MODE;
     if (!src_bf16 || !dst_codes || !dst_scales) return JETFP8_ERR_NULL;
     if (!dim_ok(rows) || !dim_ok(cols)) return JETFP8_ERR_SHAPE;
     switch (mode) {
@@ -76,7 +77,8 @@ int jetfp8_quantize(const void* src_bf16, int64_t rows, int64_t cols, int mode, 
     switch (mode) {
         case JETFP8_ROWS_1x128: return hip_status(jetfp8::launch_quant_rows(x, rows, cols, dst_codes, dst_scales, st));
         case JETFP8_COLS_128x1_T: return hip_status(jetfp8::launch_quant_cols_t(x, rows, cols, dst_codes, dst_scales, st));
-        default: return hip_status(jetfp8::launch_quant_blocks(x, rows, cols, dst_codes, dst_scales, dst_codes_t, st));
+        default: return hip_status(jetfp8::launch_quant_blocks(x, rows, cols, dst_codes, dst_scales, dst_codes_t,
+                                                               mode == JETFP8_BLOCKS_128x128_FRAG, st));
     }
 }
 
@@ -138,6 +140,16 @@ int jetfp8_gemm_fwd(const uint8_t* xq, const float* xs, const uint8_t* wq, const
     if (rc != JETFP8_OK) return rc;
     return hip_status(jetfp8::launch_gemm_block_scaled_b(xq, xs, wq, ws, static_cast<uint16_t*>(y_bf16), M, N, K,
                                                          K / 128, 1, static_cast<hipStream_t>(stream)));
+}
+
+int jetfp8_gemm_fwd_frag(const uint8_t* xq, const float* xs, const uint8_t* wq_frag, const float* ws, void* y_bf16,
+                         int64_t M, int64_t N, int64_t K, void* stream) {
+    int rc = check_gemm(xq, xs, wq_frag, ws, y_bf16, M, N, K, false);
+    if (rc == JETFP8_OK) rc = check_gemm_extent(M, N, K);
+    if (rc != JETFP8_OK) return rc;
+    if (!jetfp8::gemm_fwd_frag_fits(M, K)) return JETFP8_ERR_SHAPE;
+    return hip_status(jetfp8::launch_gemm_fwd_frag(xq, xs, wq_frag, ws, static_cast<uint16_t*>(y_bf16), M, N, K,
+                                                   static_cast<hipStream_t>(stream)));
 }
 
 int jetfp8_gemm_dgrad(const uint8_t* dyq, const float* dys, const uint8_t* wqT, const float* ws, void* dx_bf16,

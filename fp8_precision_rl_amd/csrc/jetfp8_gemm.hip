@@ -465,7 +465,11 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 // A and As address rows 0 .. I-1 of the call (row m of group g has its scale at As[g * sa_ld + m]), so a call can
 // cover a range of a larger batch's rows.
-template <int RT>
+// B layout: FRAG = false, row-major [J][Kc]; FRAG = true, the fragment order written by the block quantizer's
+// JETFP8_BLOCKS_128x128_FRAG mode: for each 16-row slice s and group g a 2 KB block at (s * G + g) * 2048 holding
+// the 16 B (lo) and then the 16 B (hi) fragment pieces of lanes 0..63, so each of the two loads of a wave's
+// fragment reads 1 KB of whole 128-byte lines (row-major, each load touches 16 half-used lines).
+template <int RT, bool FRAG>
 __global__ __launch_bounds__(D_THREADS) void gemm_decode_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ As, const uint8_t* __restrict__ B,
     const float* __restrict__ Bs, uint16_t* __restrict__ Cout, int64_t I, int64_t J, int64_t Kc, int64_t sbj,
@@ -490,7 +494,8 @@ __global__ __launch_bounds__(D_THREADS) void gemm_decode_kernel(
     // lane l holds row (l & 15) of a 16-row tile, contraction bytes 32 (l >> 4) .. +31 of the group
     const rsrc_t ra = make_rsrc(A, Ii * (int)Kc);
     const int kofs = 32 * (lane >> 4);
-    const int vb = (lane & 15) * (int)Kc + kofs;
+    const int vb = FRAG ? 16 * lane : (lane & 15) * (int)Kc + kofs;
+    const int vb_hi = FRAG ? vb + 1024 : vb + 16;
     int va[RT];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
@@ -530,8 +535,9 @@ __global__ __launch_bounds__(D_THREADS) void gemm_decode_kernel(
         }
         const rsrc_t rb = make_rsrc(live ? B + (int64_t)slice_col(sc) * Kc : B, live ? 16 * (int)Kc : 0);
         const int so = (ch * D_WAVES + wave) * BK;
-        w[0] = __builtin_amdgcn_raw_buffer_load_b128(rb, vb, so, 0);
-        w[1] = __builtin_amdgcn_raw_buffer_load_b128(rb, vb + 16, so, 0);
+        const int sow = FRAG ? (ch * D_WAVES + wave) * 2048 : so;
+        w[0] = __builtin_amdgcn_raw_buffer_load_b128(rb, vb, sow, 0);
+        w[1] = __builtin_amdgcn_raw_buffer_load_b128(rb, vb_hi, sow, 0);
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
             a[rt][0] = __builtin_amdgcn_raw_buffer_load_b128(ra, va[rt], so, 0);
@@ -627,28 +633,37 @@ __global__ __launch_bounds__(D_THREADS) void gemm_decode_kernel(
         if (c + k < nstream) chunk(c + k, wf[k], af[k], swf[k]);
 }
 
-template <int RT>
+template <int RT, bool FRAG>
 static hipError_t launch_decode(const uint8_t* A, const float* As, const uint8_t* B, const float* Bs, uint16_t* C,
                                 int64_t I, int64_t J, int64_t Kc, int64_t sbj, int64_t sbg, int64_t sa_ld,
                                 hipStream_t st) {
     const int slices = (int)(J / 16);
     // persistent blocks: one per CU, two for RT = 2 (registers and LDS allow it, and it measured faster)
     const int grid = min(slices, (RT == 2 ? 2 : 1) * device_cu_count());
-    hipLaunchKernelGGL(gemm_decode_kernel<RT>, dim3((unsigned)grid), dim3(D_THREADS), 0, st, A, As, B, Bs, C, I, J,
-                       Kc, sbj, sbg, sa_ld);
+    hipLaunchKernelGGL((gemm_decode_kernel<RT, FRAG>), dim3((unsigned)grid), dim3(D_THREADS), 0, st, A, As, B, Bs, C,
+                       I, J, Kc, sbj, sbg, sa_ld);
     return hipGetLastError();
 }
 
 // Rows r0 .. r0 + rows - 1 of a call with I rows on the small-M kernel (rows <= 64).
+template <bool FRAG = false>
 static hipError_t launch_decode_rows(const uint8_t* A, const float* As, const uint8_t* B, const float* Bs,
                                      uint16_t* C, int64_t I, int64_t r0, int64_t rows, int64_t J, int64_t Kc,
                                      int64_t sbj, int64_t sbg, hipStream_t st) {
     const uint8_t* a = A + r0 * Kc;
     const float* as = As + r0;
     uint16_t* c = C + r0 * J;
-    if (rows <= 16) return launch_decode<1>(a, as, B, Bs, c, rows, J, Kc, sbj, sbg, I, st);
-    if (rows <= 32) return launch_decode<2>(a, as, B, Bs, c, rows, J, Kc, sbj, sbg, I, st);
-    return launch_decode<4>(a, as, B, Bs, c, rows, J, Kc, sbj, sbg, I, st);
+    if (rows <= 16) return launch_decode<1, FRAG>(a, as, B, Bs, c, rows, J, Kc, sbj, sbg, I, st);
+    if (rows <= 32) return launch_decode<2, FRAG>(a, as, B, Bs, c, rows, J, Kc, sbj, sbg, I, st);
+    return launch_decode<4, FRAG>(a, as, B, Bs, c, rows, J, Kc, sbj, sbg, I, st);
+}
+
+bool gemm_fwd_frag_fits(int64_t M, int64_t K) { return M <= 64 && (K / BK) * M <= D_SA_MAX; }
+
+// Forward GEMM over fragment-ordered weights (the small-M kernel only; the caller checks gemm_fwd_frag_fits).
+hipError_t launch_gemm_fwd_frag(const uint8_t* xq, const float* xs, const uint8_t* wqf, const float* ws, uint16_t* y,
+                                int64_t M, int64_t N, int64_t K, hipStream_t st) {
+    return launch_decode_rows<true>(xq, xs, wqf, ws, y, M, 0, M, N, K, K / BK, 1, st);
 }
 
 template <bool ROW_SCALED_B, int SPLIT>

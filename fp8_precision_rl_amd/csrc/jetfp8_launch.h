@@ -31,7 +31,8 @@ hipError_t launch_rmsnorm_quant(const uint16_t* x, const uint16_t* w, int64_t R,
                                 float* s, float* rstd, uint16_t* y, hipStream_t st);
 hipError_t launch_swiglu_quant(const uint16_t* gu, int64_t R, int64_t F, uint8_t* q, float* s, uint16_t* h,
                                hipStream_t st);
-hipError_t launch_quant_blocks(const uint16_t* x, int64_t R, int64_t C, uint8_t* q, float* s, uint8_t* qT,
+// frag = true: q in the fragment order of JETFP8_BLOCKS_128x128_FRAG instead of row-major.
+hipError_t launch_quant_blocks(const uint16_t* x, int64_t R, int64_t C, uint8_t* q, float* s, uint8_t* qT, bool frag,
                                hipStream_t st);
 
 // C[i][j] = sum_g As[g][i] * sb(j, g) * sum_{k in g} A[i][k] * B[j][k], A [I][Kc], B [J][Kc].
@@ -39,6 +40,11 @@ hipError_t launch_quant_blocks(const uint16_t* x, int64_t R, int64_t C, uint8_t*
 hipError_t launch_gemm_block_scaled_b(const uint8_t* A, const float* As, const uint8_t* B, const float* Bs,
                                       uint16_t* C, int64_t I, int64_t J, int64_t Kc, int64_t sbj, int64_t sbg,
                                       hipStream_t st);
+// Forward GEMM with the weight codes in the fragment order of JETFP8_BLOCKS_128x128_FRAG (small-M kernel only:
+// M <= 64 and (K / 128) * M <= 8192, checked by gemm_fwd_frag_fits).
+bool gemm_fwd_frag_fits(int64_t M, int64_t K);
+hipError_t launch_gemm_fwd_frag(const uint8_t* xq, const float* xs, const uint8_t* wqf, const float* ws, uint16_t* y,
+                                int64_t M, int64_t N, int64_t K, hipStream_t st);
 hipError_t launch_gemm_row_scaled_b(const uint8_t* A, const float* As, const uint8_t* B, const float* Bs,
                                     uint16_t* C, int64_t I, int64_t J, int64_t Kc, hipStream_t st);
 

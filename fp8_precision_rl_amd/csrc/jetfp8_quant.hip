@@ -337,6 +337,10 @@ __global__ __launch_bounds__(256) void quant_requant_cols_kernel(const uint8_t* 
 
 // One block owns one 128x128 block: 8 rows x 8 columns per thread, a block-wide amax, codes written in
 // place and, through an LDS transpose, to the transposed copy.
+// FRAG: the codes go out in the fragment order the small-M GEMM kernel loads (JETFP8_BLOCKS_128x128_FRAG): for each
+// 16-row slice s and 128-column group g a 2 KB block at (s * C/128 + g) * 2048, in which lane l of a wave (row l % 16 of
+// the slice, columns 32 (l / 16) .. +31 of the group) has columns +0..15 at 16 l and +16..31 at 1024 + 16 l.
+template <bool FRAG>
 __global__ __launch_bounds__(256) void quant_blocks_kernel(const uint16_t* __restrict__ x, int64_t R, int64_t C,
                                                            uint8_t* __restrict__ q, float* __restrict__ s,
                                                            uint8_t* __restrict__ qT) {
@@ -364,7 +368,14 @@ __global__ __launch_bounds__(256) void quant_blocks_kernel(const uint16_t* __res
     for (int i = 0; i < 8; ++i) {
         const int row = (t >> 4) + 16 * i;
         const uint2 out = encode8(f[i], gs);
-        *reinterpret_cast<uint2*>(q + (r0 + row) * C + c0 + ch * 8) = out;
+        if (FRAG) {
+            // columns 8 ch .. +7 of the group: lane (row % 16) + 16 (ch / 4), half (ch % 4) / 2, byte 8 (ch % 2)
+            const int64_t blk = ((r0 + row) / 16) * (C / 128) + c0 / 128;
+            const int off = ((ch & 3) >> 1) * 1024 + 16 * ((row & 15) + 16 * (ch >> 2)) + 8 * (ch & 1);
+            *reinterpret_cast<uint2*>(q + blk * 2048 + off) = out;
+        } else {
+            *reinterpret_cast<uint2*>(q + (r0 + row) * C + c0 + ch * 8) = out;
+        }
         if (qT) {
             uint32_t* crow = reinterpret_cast<uint32_t*>(&codes[row][ch * 8]);
             crow[0] = out.x; crow[1] = out.y;
@@ -440,11 +451,12 @@ hipError_t launch_quant_requant_cols(const uint8_t* q, const float* s, int64_t R
     return hipGetLastError();
 }
 
-hipError_t launch_quant_blocks(const uint16_t* x, int64_t R, int64_t C, uint8_t* q, float* s, uint8_t* qT,
+hipError_t launch_quant_blocks(const uint16_t* x, int64_t R, int64_t C, uint8_t* q, float* s, uint8_t* qT, bool frag,
                                hipStream_t st) {
     if (!quant_blocks_fits(R, C)) return hipErrorInvalidValue;
     dim3 grid((unsigned)(C / 128), (unsigned)(R / 128));
-    hipLaunchKernelGGL(quant_blocks_kernel, grid, dim3(256), 0, st, x, R, C, q, s, qT);
+    if (frag) hipLaunchKernelGGL(quant_blocks_kernel<true>, grid, dim3(256), 0, st, x, R, C, q, s, qT);
+    else hipLaunchKernelGGL(quant_blocks_kernel<false>, grid, dim3(256), 0, st, x, R, C, q, s, qT);
     return hipGetLastError();
 }
 

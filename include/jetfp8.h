@@ -76,7 +76,13 @@ typedef enum {
     /* 128x128 blocks (weights).  src [rows][cols] -> dst_codes [rows][cols],
      * dst_scales [rows/128][cols/128], and when dst_codes_t != NULL the same codes transposed,
      * dst_codes_t [cols][rows] (the B operand of DGrad).  rows % 128 == 0 and cols % 128 == 0. */
-    JETFP8_BLOCKS_128x128 = 2
+    JETFP8_BLOCKS_128x128 = 2,
+    /* As JETFP8_BLOCKS_128x128 (same codes, scales and optional row-major transposed copy), with dst_codes written
+     * in the fragment order that jetfp8_gemm_fwd_frag reads: the byte of row n, column k goes to
+     *   ((n / 16) * (cols / 128) + k / 128) * 2048 + ((k % 32) / 16) * 1024 + 16 * (n % 16 + 16 * ((k % 128) / 32))
+     *   + k % 16.
+     * A pure permutation of the row-major codes (same size); rows % 128 == 0 and cols % 128 == 0. */
+    JETFP8_BLOCKS_128x128_FRAG = 3
 } jetfp8_grouping;
 
 /* Group quantization of a bf16 matrix to E4M3 codes plus fp32 scales (Jet-RL explainers,
@@ -141,6 +147,15 @@ int jetfp8_swiglu_quantize(const void* gate_up_bf16, int64_t rows, int64_t cols,
  * (JETFP8_BLOCKS_128x128 of W); y [M][N] bf16.  K % 128 == 0, N % 128 == 0, any M >= 1. */
 int jetfp8_gemm_fwd(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws,
                     void* y_bf16, int64_t M, int64_t N, int64_t K, void* stream);
+
+/* Forward FP8 linear for rollout decode over weights in the fragment order of JETFP8_BLOCKS_128x128_FRAG: the
+ * same operation, and bitwise the same result, as jetfp8_gemm_fwd on the row-major codes.  Jet-RL explainers,
+ * "Enonce du Probleme": rollout takes over 70 % of RL training time; at decode token counts the GEMM streams the
+ * FP8 weights once per step, and this layout lets every weight load read whole 128-byte lines.
+ * xq [M][K], xs [K/128][M]; wq_frag (N * K bytes, fragment order), ws [N/128][K/128]; y [M][N] bf16.
+ * K % 128 == 0, N % 128 == 0, 1 <= M <= 64 and (K / 128) * M <= 8192 (JETFP8_ERR_SHAPE otherwise). */
+int jetfp8_gemm_fwd_frag(const uint8_t* xq, const float* xs, const uint8_t* wq_frag, const float* ws,
+                         void* y_bf16, int64_t M, int64_t N, int64_t K, void* stream);
 
 /* DGrad FP8 GEMM (Jet-RL explainers, "Schema de Quantification", backward-pass items: gradients between
  * operators stay BF16, and the DGrad GEMM runs in FP8 with the gradient quantized on entry):

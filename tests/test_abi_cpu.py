@@ -134,8 +134,11 @@ def test_quantize_validation(lib):
     assert q(lib, src=None) == -1
     assert q(lib, codes=None) == -1
     assert q(lib, scales=None) == -1
-    assert q(lib, mode=3) == -4
+    assert q(lib, mode=4) == -4
     assert q(lib, mode=-1) == -4
+    assert q(lib, mode=3, rows=128, cols=200) == -2     # fragment-ordered blocks: both dims multiples of 128
+    assert q(lib, mode=3, rows=100, cols=128) == -2
+    assert q(lib, mode=3, codes_t=BAD) == -3
     assert q(lib, mode=0, codes_t=P) == -4          # transposed copy only exists for blocks
     assert q(lib, mode=1, codes_t=P) == -4
     assert q(lib, cols=200) == -2                   # rows mode: cols % 128
@@ -151,7 +154,26 @@ def test_quantize_validation(lib):
     assert q(lib, mode=2, codes_t=BAD) == -3
 
 
-@pytest.mark.parametrize("fn", ["jetfp8_gemm_fwd", "jetfp8_gemm_dgrad", "jetfp8_gemm_wgrad"])
+def test_gemm_fwd_frag_validation(lib):
+    """The fragment-order forward runs on the small-M kernel only: M <= 64 and (K / 128) * M <= 8192."""
+    f = lib.jetfp8_gemm_fwd_frag
+    good = dict(a=P, sa=P, b=P, sb=P, out=P, M=32, N=256, K=4096)
+
+    def call(**kw):
+        d = dict(good, **kw)
+        return f(d["a"], d["sa"], d["b"], d["sb"], d["out"], d["M"], d["N"], d["K"], None)
+
+    for k in ("a", "sa", "b", "sb", "out"):
+        assert call(**{k: None}) == -1
+        assert call(**{k: BAD}) == -3
+    assert call(M=65) == -2
+    assert call(M=0) == -2
+    assert call(M=64, K=128 * 129) == -2                 # 129 groups x 64 rows of scales > 8192
+    assert call(N=200) == -2
+    assert call(K=200) == -2
+
+
+@pytest.mark.parametrize("fn", ["jetfp8_gemm_fwd", "jetfp8_gemm_fwd_frag", "jetfp8_gemm_dgrad", "jetfp8_gemm_wgrad"])
 def test_gemm_validation(lib, fn):
     f = getattr(lib, fn)
     good = dict(a=P, sa=P, b=P, sb=P, out=P, M=256, N=256, K=256)

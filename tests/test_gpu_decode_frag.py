@@ -1,0 +1,107 @@
+"""Rollout decode over fragment-ordered weights (JETFP8_BLOCKS_128x128_FRAG + jetfp8_gemm_fwd_frag).
+
+The fragment order is a pure permutation of the 128x128 block codes (Jet-RL explainers, "Schema de Quantification":
+weights in 128x128 blocks), chosen so the small-M GEMM kernel reads whole 128-byte lines.  Checked here:
+  * the quantizer's fragment-ordered codes equal the oracle's row-major block codes moved by the permutation the
+    header states (computed independently with numpy index arithmetic), and its scales and transposed codes equal
+    the row-major mode's;
+  * jetfp8_gemm_fwd_frag is bitwise equal to jetfp8_gemm_fwd on the row-major codes for every small-M row-tile
+    count (1, 16, 17, 32, 33, 64 rows), on a ragged contraction (11 groups) with more column slices than blocks and
+    on a Llama-3-8B-shaped linear, and matches the oracle;
+  * more than 64 rows is a shape error.
+"""
+import numpy as np
+import pytest
+
+from conftest import bits_to_dev, check_gemm_parity, dev_to_bits, f32_to_bits
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def jf():
+    import torch
+    import fp8_precision_rl_amd as m
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    m.load_library()
+    return m
+
+
+def _frag_index(N, K):
+    """Destination byte of each row-major code (n, k) in the fragment order."""
+    n = np.arange(N, dtype=np.int64)[:, None]
+    k = np.arange(K, dtype=np.int64)[None, :]
+    return (((n // 16) * (K // 128) + k // 128) * 2048 + ((k % 32) // 16) * 1024 + 16 * (n % 16 + 16 * ((k % 128) // 32))
+            + k % 16)
+
+
+def _w(N, K, seed):
+    rng = np.random.default_rng(seed)
+    return f32_to_bits((rng.standard_normal((N, K)) * 0.02).astype(np.float32))
+
+
+def _x(M, K, seed):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    x[:, rng.integers(K)] *= 50
+    return f32_to_bits(x)
+
+
+def test_frag_index_is_a_permutation():
+    for N, K in ((128, 128), (256, 1408), (384, 512)):
+        idx = _frag_index(N, K).ravel()
+        assert np.array_equal(np.sort(idx), np.arange(N * K))
+
+
+@pytest.mark.parametrize("N,K", [(256, 1408), (384, 512)])
+def test_frag_codes_are_the_permuted_block_codes(jf, orc, N, K):
+    import torch
+    wb = _w(N, K, N + K)
+    w = bits_to_dev(wb)
+    qf, sf = jf.quantize_blocks_frag(w)
+    q, s, qT = jf.quantize_blocks(w)
+    qTf = torch.empty_like(qT)
+    jf.jetfp8_quantize(w, N, K, jf.BLOCKS_128x128_FRAG, torch.empty_like(q), torch.empty_like(s), qTf)
+    torch.cuda.synchronize()
+    oq, os_ = orc.quantize_blocks(wb)
+    want = np.empty(N * K, np.uint8)
+    want[_frag_index(N, K).ravel()] = oq.ravel()
+    assert np.array_equal(qf.cpu().numpy().ravel(), want)
+    assert np.array_equal(sf.cpu().numpy(), os_) and torch.equal(sf, s)
+    assert torch.equal(qTf, qT)
+
+
+@pytest.mark.parametrize("N,K", [(8320, 1408), (6144, 4096)])
+def test_frag_gemm_equals_row_major_gemm(jf, orc, N, K):
+    import torch
+    wb = _w(N, K, 7 + N)
+    w = bits_to_dev(wb)
+    wq, ws = jf.quantize_blocks(w, transposed=False)
+    wqf, wsf = jf.quantize_blocks_frag(w)
+    xb = _x(64, K, 8 + K)
+    x = bits_to_dev(xb)
+    for M in (1, 16, 17, 32, 33, 64):
+        xq, xs = jf.quantize_rows(x[:M].contiguous())
+        y = jf.gemm_fwd(xq, xs, wq, ws)
+        yf = jf.gemm_fwd_frag(xq, xs, wqf, wsf)
+        torch.cuda.synchronize()
+        assert np.array_equal(dev_to_bits(yf), dev_to_bits(y)), (N, K, M)
+    oxq, oxs = orc.quantize_rows(xb[:33])
+    owq, ows = orc.quantize_blocks(wb)
+    xq, xs = jf.quantize_rows(x[:33].contiguous())
+    yf = jf.gemm_fwd_frag(xq, xs, wqf, wsf)
+    torch.cuda.synchronize()
+    check_gemm_parity(f"fwd_frag 33x{N}x{K}", dev_to_bits(yf), orc.gemm_fwd(oxq, oxs, owq, ows, mode=orc.MFMA),
+                      orc.gemm_fwd(oxq, oxs, owq, ows, mode=orc.EXACT))
+
+
+def test_frag_gemm_rejects_more_than_64_rows(jf):
+    import torch
+    N, K, M = 256, 512, 65
+    wqf = torch.zeros((N, K), dtype=torch.uint8, device="cuda")
+    ws = torch.ones((N // 128, K // 128), dtype=torch.float32, device="cuda")
+    xq = torch.zeros((M, K), dtype=torch.uint8, device="cuda")
+    xs = torch.ones((K // 128, M), dtype=torch.float32, device="cuda")
+    with pytest.raises(jf.JetFP8Error) as e:
+        jf.gemm_fwd_frag(xq, xs, wqf, ws)
+    assert e.value.status == jf.ERR_SHAPE
