@@ -133,6 +133,11 @@ __device__ __forceinline__ rsrc_q_t span_rsrc(const void* base, int64_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
+// Word index in row c of the transposed-code staging buffer for logical word w (0..31): its 16-byte chunk w / 4 is
+// XORed with the row's 8-column group (c / 8) % 8, so a staging write instruction (16 columns 8 apart x 4 words)
+// covers all eight chunks.
+__device__ __forceinline__ int tcode_word(int c, int w) { return (((w >> 2) ^ ((c >> 3) & 7)) << 2) | (w & 3); }
+
 // At most 96 VGPRs, so 5 waves per SIMD fit instead of 4 (97 unconstrained): more loads in flight per CU
 // (measured +6 % on 16384-row tensors, no spills).
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5, 8))) void quant_dual_kernel(const uint16_t* __restrict__ x, int64_t R, int64_t C,
@@ -140,10 +145,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5, 8))) voi
                                                          uint8_t* __restrict__ qT, float* __restrict__ sT,
                                                          uint32_t col_blocks) {
     __shared__ uint32_t red[4][16][4];
-    // [column][4-row word]; a 36-word pitch keeps each row 16-byte aligned, so a lane's two code words go in as
-    // one 8-byte write and the transposed rows come out as 16-byte reads (measured 3.7 % faster than the odd
-    // 33-word pitch with 4-byte accesses)
-    __shared__ __attribute__((aligned(16))) uint32_t tcodes[128][36];
+    // [column][4-row word] with the 16-byte chunks of a row XOR-swizzled by the column's 8-column group
+    // (tcode_word): rows stay 16-byte aligned, so a lane's two code words go in as one 8-byte write and the
+    // transposed rows come out as 16-byte reads.  The swizzle spreads a write instruction over every chunk: with
+    // the plain 36-word pitch (8 x 36 = 0 mod 32 banks) the 16 lanes of a write fell on one or two banks.
+    __shared__ __attribute__((aligned(16))) uint32_t tcodes[128][32];
     const int t = threadIdx.x, lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int l16 = lane & 15, rs = lane >> 4, rb8 = 4 * wave + rs;
@@ -218,7 +224,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5, 8))) voi
         const uint32_t half = (j & 1) ? (cm[j >> 1] >> 16) : (cm[j >> 1] & 0xFFFFu);
         const GroupScale gs = make_group_scale(bf16_to_f32(half));
         const uint2 out = encode8(f, gs);
-        *reinterpret_cast<uint2*>(&tcodes[8 * l16 + j][2 * rb8]) = out;
+        *reinterpret_cast<uint2*>(&tcodes[8 * l16 + j][tcode_word(8 * l16 + j, 2 * rb8)]) = out;
         if (j == rs) col_scale_a = gs.s;
         if (j == rs + 4) col_scale_b = gs.s;
     }
@@ -235,7 +241,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5, 8))) voi
     const int to = oc * (int)R + 64 * hf;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-        const uint4 w4 = *reinterpret_cast<const uint4*>(&tcodes[oc][16 * hf + 4 * k]);
+        const uint4 w4 = *reinterpret_cast<const uint4*>(&tcodes[oc][tcode_word(oc, 16 * hf + 4 * k)]);
         const u32x4_q o = {w4.x, w4.y, w4.z, w4.w};
         __builtin_amdgcn_raw_buffer_store_b128(o, rqt, to + 16 * k, 0, 0);
     }
@@ -253,10 +259,11 @@ __global__ __launch_bounds__(256) void quant_requant_cols_kernel(const uint8_t* 
                                                                  int64_t C, uint8_t* __restrict__ qT,
                                                                  float* __restrict__ sT, uint32_t col_blocks) {
     __shared__ uint32_t red[4][16][8];
-    // [column][4-row word]; a 36-word pitch keeps each row 16-byte aligned, so a lane's two code words go in as
-    // one 8-byte write and the transposed rows come out as 16-byte reads (measured 3.7 % faster than the odd
-    // 33-word pitch with 4-byte accesses)
-    __shared__ __attribute__((aligned(16))) uint32_t tcodes[128][36];
+    // [column][4-row word] with the 16-byte chunks of a row XOR-swizzled by the column's 8-column group
+    // (tcode_word): rows stay 16-byte aligned, so a lane's two code words go in as one 8-byte write and the
+    // transposed rows come out as 16-byte reads.  The swizzle spreads a write instruction over every chunk: with
+    // the plain 36-word pitch (8 x 36 = 0 mod 32 banks) the 16 lanes of a write fell on one or two banks.
+    __shared__ __attribute__((aligned(16))) uint32_t tcodes[128][32];
     const int t = threadIdx.x, lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int l16 = lane & 15, rs = lane >> 4, rb8 = 4 * wave + rs;
@@ -314,7 +321,7 @@ __global__ __launch_bounds__(256) void quant_requant_cols_kernel(const uint8_t* 
         for (int i = 0; i < 8; ++i) f[i] = xv[i][j];
         const GroupScale gs = make_group_scale(__uint_as_float(m));
         const uint2 out = encode8(f, gs);
-        *reinterpret_cast<uint2*>(&tcodes[8 * l16 + j][2 * rb8]) = out;
+        *reinterpret_cast<uint2*>(&tcodes[8 * l16 + j][tcode_word(8 * l16 + j, 2 * rb8)]) = out;
         if (j == rs) col_scale_a = gs.s;
         if (j == rs + 4) col_scale_b = gs.s;
     }
@@ -329,7 +336,7 @@ __global__ __launch_bounds__(256) void quant_requant_cols_kernel(const uint8_t* 
     const int to = oc * (int)R + 64 * hf;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-        const uint4 w4 = *reinterpret_cast<const uint4*>(&tcodes[oc][16 * hf + 4 * k]);
+        const uint4 w4 = *reinterpret_cast<const uint4*>(&tcodes[oc][tcode_word(oc, 16 * hf + 4 * k)]);
         const u32x4_q o = {w4.x, w4.y, w4.z, w4.w};
         __builtin_amdgcn_raw_buffer_store_b128(o, rqt, to + 16 * k, 0, 0);
     }
