@@ -68,12 +68,15 @@ def parse():
     return p.parse_args()
 
 
-GEMM_SOURCE = os.path.join(ROOT, "fp8_precision_rl_amd", "csrc", "jetfp8_gemm.hip")
+CSRC = os.path.join(ROOT, "fp8_precision_rl_amd", "csrc")
+GEMM_SOURCES = [os.path.join(CSRC, f) for f in ("jetfp8_gemm.hip", "jetfp8_mfma.h")]
+DECODE_SOURCES = [os.path.join(CSRC, f) for f in ("jetfp8_decode.hip", "jetfp8_mfma.h")]
 
 
-def source_digest(path=GEMM_SOURCE) -> str:
+def source_digest(paths=GEMM_SOURCES) -> str:
+    """sha256 over the kernel's source files: a traffic record applies only to the kernel it was taken on."""
     import hashlib
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()
+    return hashlib.sha256(b"".join(open(p, "rb").read() for p in paths)).hexdigest()
 
 
 def recorded_traffic(path, workload):
@@ -389,7 +392,7 @@ def decode_traffic(path=os.path.join(ROOT, "profiles", "decode_traffic.json")):
         tj = json.load(open(path))
     except (OSError, ValueError):
         return None
-    if tj.get("kernel_source_sha256") != source_digest():
+    if tj.get("kernel_source_sha256") != source_digest(DECODE_SOURCES):
         return None
     return tj.get("decode_bytes_per_launch")
 

@@ -13,7 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 SRC_DIR = os.path.join(HERE, "csrc")
 LIB_DIR = os.path.join(HERE, "lib")
 LIB = os.path.join(LIB_DIR, "libjetfp8.so")
-SOURCES = ["jetfp8_api.hip", "jetfp8_quant.hip", "jetfp8_gemm.hip", "jetfp8_producers.hip"]
+SOURCES = ["jetfp8_api.hip", "jetfp8_quant.hip", "jetfp8_gemm.hip", "jetfp8_decode.hip", "jetfp8_producers.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

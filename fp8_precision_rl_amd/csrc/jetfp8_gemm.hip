@@ -19,30 +19,12 @@
 //     the tile); row-scaled B (WGrad): sa * sb per element;
 //   - blocks are renumbered so that each XCD (8 per device, dispatched round robin) works on a compact
 //     band of output tiles that share A rows and B rows in its L2.
-#include <atomic>
-
 #include "jetfp8_common.h"
 #include "jetfp8_launch.h"
+#include "jetfp8_mfma.h"
 
 namespace jetfp8 {
 
-typedef int v8i __attribute__((ext_vector_type(8)));
-typedef float v4f __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void;
-
-// 16x16x128 FP8 (E4M3 x E4M3) matrix product with C = 0: D[i][j] = sum_k a[i][k] * b[j][k].  Lane l supplies
-// row (l % 16) of a and of b, bytes k = 32 * (l / 16) .. +31; result element v of lane l is
-// D[4 * (l / 16) + v][l % 16].
-// The builtin is the scaled form (V_MFMA_SCALE_F32_16X16X128_F8F6F4); its trailing operands are the formats of
-// a and b (0 = E4M3 for both) and the E8M0 block-scale operands with their byte selectors.  With the scale
-// operands constant zero the compiler selects the plain, unscaled V_MFMA_F32_16X16X128_F8F6F4 (the only matrix
-// opcode in this file's gfx950 assembly), so the result is the unscaled E4M3 x E4M3 product.
-__device__ __forceinline__ v4f mfma_group(const v8i& a, const v8i& b) {
-    const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
-    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, z, 0, 0, 0, 0, 0, 0);
-}
-
-constexpr int BK = 128;            // one quantization group along the contraction axis
 constexpr int L_THREADS = 512;
 // Block tile of the large-M kernel: 256 x 256 (SPLIT = 1), or 128 x 128 (SPLIT = 2) for the last, partial round
 // of tiles and for 65..128-row calls.  8 waves as 2 (rows) x 4 (columns); a wave owns TM x TN 16x16 tiles.  The
@@ -55,22 +37,12 @@ struct LargeCfg {
     static constexpr int PA = BM / 64, PB = BN / 64;              // staging parts of A and B
     static constexpr int PARTS = PA > PB ? PA : PB;
 };
-// s_waitcnt immediate: lgkmcnt == 0 only (vmcnt and expcnt at their maxima)
-constexpr int kWaitLgkm0 = 0xF | (7 << 4) | (3 << 14);
 
 // LDS row layout: 128-byte rows, the 16-byte chunk c of row r stored at chunk c ^ swz(r).  The XOR
 // pattern was chosen by measurement on gfx950 (fragment reads at ~170 B/clk/CU against ~113 for the
 // plain c ^ (r & 7)); it depends on r & 15 only, so 16-row tiles share one pattern.
 __device__ __forceinline__ uint32_t swz(uint32_t r) { return (((r & 7) * 5) & 7) ^ ((r >> 3) & 1); }
 
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-
-// Raw buffer descriptor over [base, base + bytes) (stride 0, range-checked: loads past the end return
-// zero).  base and bytes must be block-uniform values (scalar registers); then so is the descriptor.
-// bytes < 2^31 is guaranteed by the host-side shape limits (kMaxGemmBand).
-__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
-}
 #define JETFP8_BUFFER_LOAD_LDS(r, lds, size, voffset, soffset) \
     __builtin_amdgcn_raw_ptr_buffer_load_lds((r), (lds), (size), (voffset), (soffset), 0, 0)
 
@@ -424,248 +396,6 @@ __global__ __launch_bounds__(L_THREADS, SPLIT) void gemm_large_kernel(
     for (int tm = 0; tm < TM; ++tm) store_row(tm, prev_i0, prev_j0);
 }
 
-// Compute units of the current device (one persistent block per compute unit: a block's LDS ring
-// takes most of a CU's LDS).  The per-device cache is atomic: concurrent first calls may both query the
-// runtime, and they store the same value.
-static int device_cu_count() {
-    static std::atomic<int> cache[64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    int n = cache[dev].load(std::memory_order_relaxed);
-    if (n == 0) {
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-        cache[dev].store(n, std::memory_order_relaxed);
-    }
-    return n;
-}
-
-// ---- small-M kernel (rollout decode batches: I <= 16 * RT rows, RT = 1, 2, 4) --------------------------
-// The large tiles would leave most of the machine idle and stream each weight row through LDS for a handful
-// of output rows, so the decode shape gets its own schedule with the same per-element operation sequence:
-//   - the output is cut into slices of 16 columns (16 rows of B) by all I rows; persistent 512-thread blocks
-//     take slices b, b + gridDim.x, ... and the operand loads run on across slice boundaries, so the weight
-//     stream never drains between slices;
-//   - the groups of the contraction are dealt out in chunks of 8, one group per wave: the wave forms the
-//     group products of its group with one V_MFMA_F32_16X16X128_F8F6F4 per 16-row tile (B fragment first,
-//     C = 0, exactly as the large kernel), and parks them in LDS;
-//   - after a barrier every wave runs the promotion acc = fma(p, fl32(sa * sb), acc) for its share of the
-//     outputs over the chunk's groups in ascending order -- the same chain the large kernel runs, so every
-//     output row is bitwise the same whichever kernel computed it;
-//   - operand fragments go straight from global memory into registers, D_AHEAD chunks ahead (2 for RT >= 2;
-//     range-checked buffer loads: rows past I and groups past the contraction read as zero and are never
-//     promoted); the A-row scales of all groups sit in LDS for the block's lifetime;
-//   - the block scales of a chunk's 8 groups come with its operands, one vector load (lane l: group l & 7),
-//     and are broadcast with readlane.  Read with scalar loads they held up every chunk: the chunk's barrier
-//     waits for LDS traffic with lgkmcnt(0), which also waits for scalar loads in flight (measured: M = 1
-//     78 -> 63 us over the four Llama-3-8B linears).
-constexpr int D_WAVES = 8, D_THREADS = 64 * D_WAVES, D_AHEAD = 3;
-constexpr int D_SA_MAX = 8192;     // A-row scales kept in LDS: (contraction / 128) * rows <= 8192
-
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-
-// A and As address rows 0 .. I-1 of the call (row m of group g has its scale at As[g * sa_ld + m]), so a call can
-// cover a range of a larger batch's rows.
-// B layout: FRAG = false, row-major [J][Kc]; FRAG = true, the fragment order written by the block quantizer's
-// JETFP8_BLOCKS_128x128_FRAG mode: for each 16-row slice s and group g a 2 KB block at (s * G + g) * 2048 holding
-// the 16 B (lo) and then the 16 B (hi) fragment pieces of lanes 0..63, so each of the two loads of a wave's
-// fragment reads 1 KB of whole 128-byte lines (row-major, each load touches 16 half-used lines).
-template <int RT, bool FRAG>
-__global__ __launch_bounds__(D_THREADS) void gemm_decode_kernel(
-    const uint8_t* __restrict__ A, const float* __restrict__ As, const uint8_t* __restrict__ B,
-    const float* __restrict__ Bs, uint16_t* __restrict__ Cout, int64_t I, int64_t J, int64_t Kc, int64_t sbj,
-    int64_t sbg, int64_t sa_ld) {
-    // chunks in flight: RT = 2 keeps 2 (82 VGPRs, so two blocks share a CU: measured 4 % faster at 32 rows);
-    // RT = 4 keeps 2 to fit its registers; deeper prefetch measured no faster
-    constexpr int AHEAD = RT >= 2 ? 2 : D_AHEAD;
-    constexpr int PAIRS = RT * 4;                             // (row tile, lane component) pairs of outputs
-    constexpr int EPW = (PAIRS + D_WAVES - 1) / D_WAVES;      // pairs per wave in the promotion chain
-    constexpr bool ROWC = RT >= 2;                            // row-contiguous A loads (see below)
-    __shared__ v4f pbuf[2][D_WAVES][RT][64];
-    __shared__ float sa_tab[D_SA_MAX];
-    const int t = threadIdx.x, lane = t & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-    const int G = (int)(Kc / BK), nchunks = (G + D_WAVES - 1) / D_WAVES;
-    const int Ii = (int)I;
-    const int slices = (int)(J / 16);
-    // chunk stream of this block: slices blockIdx.x, + gridDim.x, ...; nchunks chunks each
-    const int nstream = ((slices - 1 - (int)blockIdx.x) / (int)gridDim.x + 1) * nchunks;
-    auto slice_col = [&](int sc) -> int { return ((int)blockIdx.x + sc * (int)gridDim.x) * 16; };
-
-    // lane l holds row (l & 15) of a 16-row tile, contraction bytes 32 (l >> 4) .. +31 of the group
-    const rsrc_t ra = make_rsrc(A, Ii * (int)Kc);
-    const int kofs = 32 * (lane >> 4);
-    const int vb = FRAG ? 16 * lane : (lane & 15) * (int)Kc + kofs;
-    const int vb_hi = FRAG ? vb + 1024 : vb + 16;
-    int va[RT];
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-        va[rt] = ROWC ? (rt * 16 + (lane >> 3)) * (int)Kc + (lane & 7) * 16 : (rt * 16 + (lane & 15)) * (int)Kc + kofs;
-    // RT >= 2 (ROWC): the A operand is loaded row-contiguous, each load covering 8 rows x 128 bytes (lane l: row
-    // l / 8, 16-byte piece l % 8; the second load rows 8..15), i.e. 8 whole cache lines per instruction instead of
-    // 16 half lines, and moved into the matrix instruction's layout (lane t: row t % 16, pieces 2 (t / 16) and
-    // 2 (t / 16) + 1) through this wave's own product slot in LDS, one half (8 rows) at a time, the pieces of a row
-    // XOR-permuted by the row so the reads spread over the banks.  Measured 10 % faster at 32 rows and 2-4 % at
-    // 48-64; at 1-16 rows the direct layout is faster.
-    const int wpos = (lane >> 3) * 128 + (((lane & 7) ^ (lane >> 3)) << 4);
-    const int r8 = lane & 7, q2 = 2 * (lane >> 4);
-    const int rpos0 = r8 * 128 + ((q2 ^ r8) << 4), rpos1 = r8 * 128 + (((q2 + 1) ^ r8) << 4);
-    const bool hi_rows = (lane & 15) >= 8;
-
-    // promotion-chain ownership: pair q = wave + 8 e -> row tile q >> 2, lane component q & 3
-    float acc[EPW];
-#pragma unroll
-    for (int e = 0; e < EPW; ++e) acc[e] = 0.0f;
-
-    u32x4 wf[AHEAD][2], af[AHEAD][RT][2];
-    // block scales of a chunk's 8 groups: lane l holds that of group (l & 7), loaded with the chunk's operands
-    // (a vector load, so the per-chunk barrier's LDS wait does not wait for it); range-checked over Bs
-    const rsrc_t rbs = make_rsrc(Bs, (int)(J / 128) * G * 4);
-    float swf[AHEAD];
-    // stream position c -> slice c / nchunks (B rows of that slice only: 16 x Kc bytes), group chunk
-    // c % nchunks.  Positions past the block's stream load unconditionally (a conditional load would make
-    // the compiler wait for it where the paths join) through an empty descriptor: they read zeros.
-    auto load_chunk = [&](int c, u32x4 (&w)[2], u32x4 (&a)[RT][2], float& sw) __attribute__((always_inline)) {
-        const int sc = __builtin_amdgcn_readfirstlane(c / nchunks), ch = c - sc * nchunks;
-        const bool live = c < nstream;
-        {
-            const int scc = live ? sc : 0;
-            const int gi = min(ch * D_WAVES + (lane & 7), G - 1);
-            sw = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-                rbs, ((slice_col(scc) / 128) * (int)sbj + gi * (int)sbg) * 4, 0, 0));
-        }
-        const rsrc_t rb = make_rsrc(live ? B + (int64_t)slice_col(sc) * Kc : B, live ? 16 * (int)Kc : 0);
-        const int so = (ch * D_WAVES + wave) * BK;
-        const int sow = FRAG ? (ch * D_WAVES + wave) * 2048 : so;
-        w[0] = __builtin_amdgcn_raw_buffer_load_b128(rb, vb, sow, 0);
-        w[1] = __builtin_amdgcn_raw_buffer_load_b128(rb, vb_hi, sow, 0);
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-            a[rt][0] = __builtin_amdgcn_raw_buffer_load_b128(ra, va[rt], so, 0);
-            a[rt][1] = __builtin_amdgcn_raw_buffer_load_b128(ra, va[rt] + (ROWC ? 8 * (int)Kc : 16), so, 0);
-        }
-    };
-    auto store_slice = [&](int sc) __attribute__((always_inline)) {
-        const int j0 = slice_col(sc);
-        // pair q of lane l is row (q >> 2) * 16 + (l & 15), column j0 + 4 (l >> 4) + (q & 3)
-#pragma unroll
-        for (int e = 0; e < EPW; ++e) {
-            const int q = wave + D_WAVES * e;
-            const int m = (q >> 2) * 16 + (lane & 15);
-            if (q < PAIRS && m < Ii)
-                Cout[(int64_t)m * J + j0 + 4 * (lane >> 4) + (q & 3)] = (uint16_t)f32_to_bf16_rne(acc[e]);
-            acc[e] = 0.0f;
-        }
-    };
-
-    // the A-row scales of every group (the same for all slices) in LDS: sa_tab[g * I + m]; filled before the
-    // first operand loads are issued, so waiting for it does not wait for them
-    for (int i = t; i < G * Ii; i += D_THREADS) {
-        const int g = i / Ii, m = i - g * Ii;
-        sa_tab[i] = As[(int64_t)g * sa_ld + m];
-    }
-#pragma unroll
-    for (int k = 0; k < AHEAD; ++k) load_chunk(k, wf[k], af[k], swf[k]);
-    // LDS writes done, then every wave is here (a plain barrier: the operand loads stay in flight)
-    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-    __builtin_amdgcn_s_barrier();
-
-    auto chunk = [&](int c, u32x4 (&w)[2], u32x4 (&a)[RT][2], float& sw) __attribute__((always_inline)) {
-        float sb_cur[D_WAVES];
-#pragma unroll
-        for (int gi = 0; gi < D_WAVES; ++gi) sb_cur[gi] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sw), gi));
-        const v8i bfrag = (v8i){(int)w[0][0], (int)w[0][1], (int)w[0][2], (int)w[0][3],
-                                (int)w[1][0], (int)w[1][1], (int)w[1][2], (int)w[1][3]};
-        v4f p[RT];
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-            u32x4 f0 = a[rt][0], f1 = a[rt][1];
-            if (ROWC) {
-                // this wave's product slot of two chunks ago: every wave finished reading it before the previous
-                // chunk's barrier, and only this wave writes it (1 KB: 64 lanes x 16 bytes)
-                uint8_t* slot = reinterpret_cast<uint8_t*>(&pbuf[c & 1][wave][rt][0]);
-                u32x4 lo[2], hi[2];
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    *reinterpret_cast<u32x4*>(slot + wpos) = a[rt][h];
-                    lo[h] = *reinterpret_cast<const u32x4*>(slot + rpos0);
-                    hi[h] = *reinterpret_cast<const u32x4*>(slot + rpos1);
-                }
-                f0 = hi_rows ? lo[1] : lo[0];
-                f1 = hi_rows ? hi[1] : hi[0];
-            }
-            const v8i afrag = (v8i){(int)f0[0], (int)f0[1], (int)f0[2], (int)f0[3],
-                                    (int)f1[0], (int)f1[1], (int)f1[2], (int)f1[3]};
-            p[rt] = mfma_group(bfrag, afrag);
-        }
-        load_chunk(c + AHEAD, w, a, sw);
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) pbuf[c & 1][wave][rt][lane] = p[rt];
-        // this wave's products (and its chain reads of two chunks ago) are in LDS, then every wave is here;
-        // a plain barrier, so the operand loads of the next chunks stay in flight
-        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-        __builtin_amdgcn_s_barrier();
-        const int ch = c % nchunks;
-        // promotion chain over the chunk's groups, ascending
-#pragma unroll
-        for (int gi = 0; gi < D_WAVES; ++gi) {
-            if (ch * D_WAVES + gi < G) {
-#pragma unroll
-                for (int e = 0; e < EPW; ++e) {
-                    const int q = wave + D_WAVES * e;
-                    const int m = (q >> 2) * 16 + (lane & 15);
-                    if (q < PAIRS) {
-                        const float pv = pbuf[c & 1][gi][q >> 2][lane][q & 3];
-                        const float sa = m < Ii ? sa_tab[(ch * D_WAVES + gi) * Ii + m] : 0.0f;
-                        acc[e] = fmaf(pv, sa * sb_cur[gi], acc[e]);          // s = fl32(sa * sb)
-                    }
-                }
-            }
-        }
-        if (ch == nchunks - 1) store_slice(c / nchunks);
-    };
-    int c = 0;
-    for (; c + AHEAD <= nstream; c += AHEAD) {
-#pragma unroll
-        for (int k = 0; k < AHEAD; ++k) chunk(c + k, wf[k], af[k], swf[k]);
-    }
-#pragma unroll
-    for (int k = 0; k < AHEAD; ++k)
-        if (c + k < nstream) chunk(c + k, wf[k], af[k], swf[k]);
-}
-
-template <int RT, bool FRAG>
-static hipError_t launch_decode(const uint8_t* A, const float* As, const uint8_t* B, const float* Bs, uint16_t* C,
-                                int64_t I, int64_t J, int64_t Kc, int64_t sbj, int64_t sbg, int64_t sa_ld,
-                                hipStream_t st) {
-    const int slices = (int)(J / 16);
-    // persistent blocks: one per CU, two for RT = 2 (registers and LDS allow it, and it measured faster)
-    const int grid = min(slices, (RT == 2 ? 2 : 1) * device_cu_count());
-    hipLaunchKernelGGL((gemm_decode_kernel<RT, FRAG>), dim3((unsigned)grid), dim3(D_THREADS), 0, st, A, As, B, Bs, C,
-                       I, J, Kc, sbj, sbg, sa_ld);
-    return hipGetLastError();
-}
-
-// Rows r0 .. r0 + rows - 1 of a call with I rows on the small-M kernel (rows <= 64).
-template <bool FRAG = false>
-static hipError_t launch_decode_rows(const uint8_t* A, const float* As, const uint8_t* B, const float* Bs,
-                                     uint16_t* C, int64_t I, int64_t r0, int64_t rows, int64_t J, int64_t Kc,
-                                     int64_t sbj, int64_t sbg, hipStream_t st) {
-    const uint8_t* a = A + r0 * Kc;
-    const float* as = As + r0;
-    uint16_t* c = C + r0 * J;
-    if (rows <= 16) return launch_decode<1, FRAG>(a, as, B, Bs, c, rows, J, Kc, sbj, sbg, I, st);
-    if (rows <= 32) return launch_decode<2, FRAG>(a, as, B, Bs, c, rows, J, Kc, sbj, sbg, I, st);
-    return launch_decode<4, FRAG>(a, as, B, Bs, c, rows, J, Kc, sbj, sbg, I, st);
-}
-
-bool gemm_fwd_frag_fits(int64_t M, int64_t K) { return M <= 64 && (K / BK) * M <= D_SA_MAX; }
-
-// Forward GEMM over fragment-ordered weights (the small-M kernel only; the caller checks gemm_fwd_frag_fits).
-hipError_t launch_gemm_fwd_frag(const uint8_t* xq, const float* xs, const uint8_t* wqf, const float* ws, uint16_t* y,
-                                int64_t M, int64_t N, int64_t K, hipStream_t st) {
-    return launch_decode_rows<true>(xq, xs, wqf, ws, y, M, 0, M, N, K, K / BK, 1, st);
-}
-
 template <bool ROW_SCALED_B, int SPLIT>
 static hipError_t launch_large_part(const uint8_t* A, const float* As, const uint8_t* B, const float* Bs, uint16_t* C,
                                     int64_t I, int64_t J, int64_t Kc, int64_t sbj, int64_t sbg, int tiles_m,
@@ -706,13 +436,13 @@ hipError_t launch_gemm_block_scaled_b(const uint8_t* A, const float* As, const u
                                       uint16_t* C, int64_t I, int64_t J, int64_t Kc, int64_t sbj, int64_t sbg,
                                       hipStream_t st) {
     // decode sizes: the small-M schedule (same per-element sequence, so the same bits)
-    if (I <= 64 && (Kc / BK) * I <= D_SA_MAX) return launch_decode_rows(A, As, B, Bs, C, I, 0, I, J, Kc, sbj, sbg, st);
+    if (decode_rows_fit(I, Kc)) return launch_decode_rows(A, As, B, Bs, C, I, 0, I, J, Kc, sbj, sbg, st);
     // 65..128 rows with fewer output columns than contraction: the small-M kernel on the first 64 rows, then on
     // the rest (the weights are read twice, but the 16-column slices keep every CU busy where the quarter tiles of
     // the large kernel would number J / 128 only; measured down projection 14336 -> 4096 at 128 rows: 98 us
     // against 125 us on quarter tiles).  Wider outputs use the quarter tiles (gate_up 4096 -> 28672: 46 us
     // against 168 us).
-    if (I <= 128 && J < Kc && (Kc / BK) * 64 <= D_SA_MAX) {
+    if (I <= 128 && J < Kc && decode_rows_fit(64, Kc)) {
         const hipError_t e = launch_decode_rows(A, As, B, Bs, C, I, 0, 64, J, Kc, sbj, sbg, st);
         if (e != hipSuccess) return e;
         return launch_decode_rows(A, As, B, Bs, C, I, 64, I - 64, J, Kc, sbj, sbg, st);

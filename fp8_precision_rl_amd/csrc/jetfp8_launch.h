@@ -40,6 +40,11 @@ hipError_t launch_quant_blocks(const uint16_t* x, int64_t R, int64_t C, uint8_t*
 hipError_t launch_gemm_block_scaled_b(const uint8_t* A, const float* As, const uint8_t* B, const float* Bs,
                                       uint16_t* C, int64_t I, int64_t J, int64_t Kc, int64_t sbj, int64_t sbg,
                                       hipStream_t st);
+// Rows r0 .. r0 + rows - 1 of a block-scaled-B GEMM with I rows on the small-M kernel (decode_rows_fit(rows, Kc)).
+bool decode_rows_fit(int64_t rows, int64_t Kc);
+hipError_t launch_decode_rows(const uint8_t* A, const float* As, const uint8_t* B, const float* Bs, uint16_t* C,
+                              int64_t I, int64_t r0, int64_t rows, int64_t J, int64_t Kc, int64_t sbj, int64_t sbg,
+                              hipStream_t st);
 // Forward GEMM with the weight codes in the fragment order of JETFP8_BLOCKS_128x128_FRAG (small-M kernel only:
 // M <= 64 and (K / 128) * M <= 8192, checked by gemm_fwd_frag_fits).
 bool gemm_fwd_frag_fits(int64_t M, int64_t K);
