@@ -563,7 +563,7 @@ def main():
         "pct_of_fp8_peak": round(100 * value / FP8_PEAK_TFLOPS, 2),
         "gemm_only_tflops": round(achieved, 2),
         "wall_s": round(wall, 4),
-        "roofline": {"bound": "mfma", "kernel": "gemm_large_kernel (fwd, dgrad, wgrad)", "achieved": round(achieved, 2),
+        "roofline": {"bound": "mfma", "kernel": "gemm_pp_kernel (fwd, dgrad), gemm_large_kernel (wgrad, quarter-tile tails)", "achieved": round(achieved, 2),
                      "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / FP8_PEAK_TFLOPS, 4),
                      "traffic": traffic, "launches": n_gemm,
                      "mean_launch_us": round(1e3 * gemm_ms / max(n_gemm, 1), 2),

@@ -396,12 +396,282 @@ __global__ __launch_bounds__(L_THREADS, SPLIT) void gemm_large_kernel(
     for (int tm = 0; tm < TM; ++tm) store_row(tm, prev_i0, prev_j0);
 }
 
+// ---- forward / DGrad on 256 x 256 tiles: the two waves of each SIMD in alternating phases --------------------
+// The same tiles, staging ring, LDS layout and per-element operation sequence as gemm_large_kernel (so the same
+// bits), scheduled so that the matrix unit of a SIMD is fed by one wave at a time while its partner reads LDS:
+//   - a group is two halves (row tiles 0-3, 4-7 of the wave tile); each half is a memory phase (the half's A
+//     fragments, at the first half also the B fragments and the refill loads of the next group) and a compute
+//     phase (16 matrix ops, each followed in issue order by the promotion of the previous row tile's product of
+//     the same column tile, so the VALU works under the matrix unit);
+//   - waves 0-3 (wm = 0, one per SIMD) run one phase ahead of waves 4-7 (wm = 1): between two block barriers
+//     one wave of each SIMD computes while the other loads.  Register-only measurement on gfx950: one wave issuing
+//     matrix op + 4 promotion FMAs in this order keeps the matrix unit 90 % as busy as matrix ops alone; 16 FMAs
+//     followed by 4 matrix ops (the order the compiler picks for the interleaved-waves kernel) only 61 %;
+//   - the promotion lags one row tile, across phases too: row tile 7 of a group is promoted at the start of the
+//     next group's first compute phase.  Rows 0-2 of a tile are final after the first compute phase of its last
+//     group and are stored in the next memory phase; rows 3-6 and row 7 in the memory phases of the next tile's
+//     first group;
+//   - the refill of the ring is spread over all four memory phases of a group (see the staging comment below).
+__global__ __launch_bounds__(L_THREADS, 1) void gemm_pp_kernel(
+    const uint8_t* __restrict__ A, const float* __restrict__ As, const uint8_t* __restrict__ B,
+    const float* __restrict__ Bs, uint16_t* __restrict__ Cout, int64_t I, int64_t J, int64_t Kc, int64_t sbj,
+    int64_t sbg, int tiles_m, int tiles_n, int q_count) {
+    using Cfg = LargeCfg<1>;
+    constexpr int BM = Cfg::BM, BN = Cfg::BN, WROWS = Cfg::WROWS, WCOLS = Cfg::WCOLS, TN = Cfg::TN;
+    typedef LargeStage<1> Stage;
+    __shared__ Stage stage0, stage1;
+
+    const int t = threadIdx.x, lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int wm = wave >> 2, wn = wave & 3;
+    const int G = (int)(Kc / BK);
+    const int T = q_count;
+    const int nsteps = __builtin_amdgcn_readfirstlane(((T - 1 - (int)blockIdx.x) / (int)gridDim.x + 1) * G);
+
+    auto tile_ctx = [&](int pid) __attribute__((always_inline)) -> TileCtx {
+        TileCtx c;
+        int tm_, tn_;
+        tile_of_work<1>(pid, tiles_m, tiles_n, 0, q_count, 1, tm_, tn_);
+        c.tmi = __builtin_amdgcn_readfirstlane(tm_);
+        c.tni = __builtin_amdgcn_readfirstlane(tn_);
+        c.i0 = c.tmi * BM;
+        c.j0 = c.tni * BN;
+        const int rows_a = __builtin_amdgcn_readfirstlane(min((int)I - c.i0, BM));
+        const int rows_b = __builtin_amdgcn_readfirstlane(min((int)J - c.j0, BN));
+        const int sa_bytes = __builtin_amdgcn_readfirstlane((G * (int)I - c.i0) * 4);
+        c.ra = make_rsrc(A + (int64_t)c.i0 * Kc, rows_a * (int)Kc);
+        c.rb = make_rsrc(B + (int64_t)c.j0 * Kc, rows_b * (int)Kc);
+        c.rsa = make_rsrc(As + c.i0, sa_bytes);
+        c.rsb = c.rsa;
+        return c;
+    };
+
+    // staging: the LDS layout of gemm_large_kernel (1 KB region q of an operand tile holds rows 8 q .. 8 q + 7; lane
+    // l lands at row + l / 8, physical chunk l % 8).  Part c = rows 64 c .. 64 c + 63 of A or B: one wave issues two
+    // regions of it, 8 c + (w & 3) and 8 c + (w & 3) + 4, so the 4 waves of one phase cover a part.
+    //   - A parts of the next group: waves 0-3 parts 0 and 2 in their first memory phase, waves 4-7 parts 1 and 3
+    //     in theirs (one phase later); with them the A-row scales of those parts (waves 0, 1, 4, 5);
+    //   - B parts of the group after next (the B tile of the current stage is read by then): waves 0-3 parts 0
+    //     and 1, waves 4-7 parts 2 and 3, in their second memory phases.
+    // Each wave then issues 4 staging loads per memory phase; all of them in one phase made that phase the
+    // critical path (the issue of direct-to-LDS loads stalls the wave).  A wave waits for its loads at the end of
+    // its next second memory phase; the first read of each part comes at least one phase later.
+    const uint32_t rq = (wave & 3) * 8 + (lane >> 3);
+    const int qoff = (int)(rq * (uint32_t)Kc + (((lane & 7) ^ swz(rq)) << 4));   // rows +32: same swizzle
+    const int cstep = 64 * (int)Kc;
+    auto issue_rows = [&](rsrc_t r, uint8_t* base, int c, int g) __attribute__((always_inline)) {
+        const int go = g * BK + c * cstep;
+        JETFP8_BUFFER_LOAD_LDS(r, (lds_void*)(base + (c * 8 + (wave & 3)) * 1024), 16, qoff, go);
+        JETFP8_BUFFER_LOAD_LDS(r, (lds_void*)(base + (c * 8 + (wave & 3) + 4) * 1024), 16, qoff, go + 32 * (int)Kc);
+    };
+    auto issue_a = [&](const TileCtx& tc, int g, Stage& S) __attribute__((always_inline)) {
+        issue_rows(tc.ra, S.a, wm, g);
+        issue_rows(tc.ra, S.a, wm + 2, g);
+        if ((wave & 3) < 2) {
+            const int c = wm + 2 * (wave & 1);
+            JETFP8_BUFFER_LOAD_LDS(tc.rsa, (lds_void*)&S.sa[c * 64], 4, (c * 64 + lane) * 4, g * (int)I * 4);
+        }
+    };
+    auto issue_b = [&](rsrc_t rb, int g, Stage& S) __attribute__((always_inline)) {
+        issue_rows(rb, S.b, 2 * wm, g);
+        issue_rows(rb, S.b, 2 * wm + 1, g);
+    };
+
+    v4f acc[8][TN];
+#pragma unroll
+    for (int a = 0; a < 8; ++a)
+#pragma unroll
+        for (int b = 0; b < TN; ++b) acc[a][b] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
+
+    const int qc4 = 4 * (lane >> 4);
+    const uint32_t rl = lane & 15, cp = 2 * (lane >> 4), sw = swz(rl);
+    const uint32_t fa0 = (wm * WROWS + rl) * BK + ((cp ^ sw) << 4), fa1 = (wm * WROWS + rl) * BK + (((cp + 1) ^ sw) << 4);
+    const uint32_t fb0 = (wn * WCOLS + rl) * BK + ((cp ^ sw) << 4), fb1 = (wn * WCOLS + rl) * BK + (((cp + 1) ^ sw) << 4);
+
+    auto store_row = [&](int tm, int i0, int j0) __attribute__((always_inline)) {
+        const int64_t r = i0 + wm * WROWS + tm * 16 + rl;
+        if (r < I) {
+#pragma unroll
+            for (int tn = 0; tn < TN; ++tn) {
+                const int64_t c = j0 + wn * WCOLS + tn * 16 + qc4;
+                if (c < J) {
+                    uint2 w;
+                    w.x = f32_to_bf16_rne(acc[tm][tn][0]) | (f32_to_bf16_rne(acc[tm][tn][1]) << 16);
+                    w.y = f32_to_bf16_rne(acc[tm][tn][2]) | (f32_to_bf16_rne(acc[tm][tn][3]) << 16);
+                    *reinterpret_cast<uint2*>(&Cout[r * J + c]) = w;
+                }
+            }
+        }
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn) acc[tm][tn] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
+    };
+
+    int cpid = blockIdx.x, cg = 0;
+    TileCtx cur = tile_ctx(cpid);
+    // issue cursors: A (and the block scale) one group ahead of the compute cursor, B two groups ahead.  Past the
+    // block's last group a cursor stays on a valid group of the last tile (loaded, never read).
+    int ipid = cpid, ig = 0;
+    TileCtx iss = cur;
+    int bpid = cpid, bg = 0;
+    rsrc_t rbb = cur.rb;
+    int prev_i0 = 0, prev_j0 = 0;
+    auto advance_issue = [&]() __attribute__((always_inline)) {
+        if (++ig == G) {
+            ig = 0;
+            ipid += gridDim.x;
+            if (ipid < T) iss = tile_ctx(ipid);
+        }
+    };
+    auto advance_b = [&]() __attribute__((always_inline)) {
+        if (++bg == G) {
+            bg = 0;
+            bpid += gridDim.x;
+            if (bpid < T) rbb = tile_ctx(bpid).rb;
+        }
+    };
+    const rsrc_t rbs = make_rsrc(Bs, (int)(J / 128) * G * 4);
+    auto load_sb = [&](int j0, int g) __attribute__((always_inline)) -> float {
+        const int bblk = min((j0 + wn * WCOLS) / 128, (int)(J / 128) - 1);
+        return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rbs, (bblk * (int)sbj + g * (int)sbg) * 4, 0, 0));
+    };
+    float sbv_cur = 0.0f, sbv_nxt = 0.0f;
+
+    // block barrier between phases; the empty asm with a memory clobber keeps every LDS access on its side
+    auto sync = [&]() __attribute__((always_inline)) {
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    v8i bfr[TN], afr[4];
+    v4f pp[TN];
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn) pp[tn] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
+    float s1[4];
+    float s_prev = 0.0f;   // scale of the row tile whose products are in pp (the first promotion adds +0 to +0)
+
+    // memory phase: the half's A fragments (and at the first half the B fragments) and row scales
+    auto read_half = [&](const Stage& S, int hf) __attribute__((always_inline)) {
+        if (hf == 0) {
+#pragma unroll
+            for (int tn = 0; tn < TN; ++tn) {
+                const uint4 lo = *reinterpret_cast<const uint4*>(&S.b[fb0 + tn * 2048]);
+                const uint4 hi = *reinterpret_cast<const uint4*>(&S.b[fb1 + tn * 2048]);
+                bfr[tn] = (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int tm = 4 * hf + i;
+            const uint4 lo = *reinterpret_cast<const uint4*>(&S.a[fa0 + tm * 2048]);
+            const uint4 hi = *reinterpret_cast<const uint4*>(&S.a[fa1 + tm * 2048]);
+            afr[i] = (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        }
+        const float* sar = S.sa + (wm * WROWS + (int)rl);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s1[i] = sar[(4 * hf + i) * 16] * sbv_cur;     // s = fl32(sa * sb)
+    };
+
+    // compute phase: row tiles 4 hf .. 4 hf + 3.  Before the matrix op (r, tn) the product of (r - 1, tn) (row 7 of
+    // the previous group for r = 0) is promoted out of the same registers; the empty asm statements fix this order.
+    auto compute_half = [&](int hf) __attribute__((always_inline)) {
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int prev = i > 0 ? 4 * hf + i - 1 : (hf == 0 ? 7 : 3);
+#pragma unroll
+            for (int tn = 0; tn < TN; ++tn) {
+#pragma unroll
+                for (int v = 0; v < 4; ++v) acc[prev][tn][v] = fmaf(pp[tn][v], s_prev, acc[prev][tn][v]);
+                asm volatile("" : "+v"(acc[prev][tn]));
+                asm volatile("" : "+v"(bfr[tn]));
+                pp[tn] = mfma_group(bfr[tn], afr[i]);
+                asm volatile("" : "+v"(pp[tn]));
+            }
+            s_prev = s1[i];
+        }
+        __builtin_amdgcn_s_setprio(0);
+    };
+
+    auto group = [&](int s, Stage& S, Stage& R) __attribute__((always_inline)) {
+        const bool first_of_tile = cg == 0 && s > 0;
+        // ---- memory phase, first half
+        if (first_of_tile) {
+#pragma unroll
+            for (int tm = 3; tm < 7; ++tm) store_row(tm, prev_i0, prev_j0);
+        }
+        issue_a(iss, ig, R);
+        sbv_nxt = load_sb(iss.j0, ig);
+        read_half(S, 0);
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+        sync();
+        compute_half(0);
+        sync();
+        // ---- memory phase, second half
+        if (first_of_tile) store_row(7, prev_i0, prev_j0);
+        if (cg == G - 1) {
+#pragma unroll
+            for (int tm = 0; tm < 3; ++tm) store_row(tm, cur.i0, cur.j0);
+        }
+        read_half(S, 1);
+        // this wave's staging loads of the previous memory phases have landed, and its fragment reads have returned
+        __builtin_amdgcn_s_waitcnt(0);
+        issue_b(rbb, bg, S);
+        sync();
+        compute_half(1);
+        sync();
+        advance_issue();
+        advance_b();
+        sbv_cur = sbv_nxt;
+        if (++cg == G) {
+            cg = 0;
+            prev_i0 = cur.i0;
+            prev_j0 = cur.j0;
+            cpid += gridDim.x;
+            if (cpid < T) cur = tile_ctx(cpid);
+        }
+    };
+
+    // prologue: the first group whole, and the B tile of the second
+    issue_a(iss, ig, stage0);
+    issue_b(rbb, bg, stage0);
+    sbv_cur = load_sb(iss.j0, ig);
+    advance_issue();
+    advance_b();
+    issue_b(rbb, bg, stage1);
+    advance_b();
+    __builtin_amdgcn_s_waitcnt(0);
+    sync();
+    if (wm == 1) sync();     // waves 4-7 run one phase behind waves 0-3
+    int s = 0;
+    for (; s + 2 <= nsteps; s += 2) {
+        group(s, stage0, stage1);
+        group(s + 1, stage1, stage0);
+    }
+    if (s < nsteps) group(s, stage0, stage1);
+    if (wm == 0) sync();     // matching barrier count
+    // last promotion (row tile 7 of the block's last group), then rows 3-7 of the last tile
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[7][tn][v] = fmaf(pp[tn][v], s_prev, acc[7][tn][v]);
+    __builtin_amdgcn_s_waitcnt(0);
+#pragma unroll
+    for (int tm = 3; tm < 8; ++tm) store_row(tm, prev_i0, prev_j0);
+}
+
 template <bool ROW_SCALED_B, int SPLIT>
 static hipError_t launch_large_part(const uint8_t* A, const float* As, const uint8_t* B, const float* Bs, uint16_t* C,
                                     int64_t I, int64_t J, int64_t Kc, int64_t sbj, int64_t sbg, int tiles_m,
                                     int tiles_n, int q_begin, int q_count, int qrows, int max_blocks, hipStream_t st) {
     const int items = q_count * (SPLIT == 1 ? 1 : 2 * qrows);
     const int grid = min(items, max_blocks);
+    if (!ROW_SCALED_B && SPLIT == 1) {
+        hipLaunchKernelGGL(gemm_pp_kernel, dim3(grid), dim3(L_THREADS), 0, st, A, As, B, Bs, C, I, J, Kc, sbj, sbg,
+                           tiles_m, tiles_n, q_count);
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL((gemm_large_kernel<ROW_SCALED_B, SPLIT>), dim3(grid), dim3(L_THREADS), 0, st, A, As, B, Bs, C,
                        I, J, Kc, sbj, sbg, tiles_m, tiles_n, q_begin, q_count, qrows);
     return hipGetLastError();
