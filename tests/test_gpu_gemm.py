@@ -248,3 +248,42 @@ def test_wgrad_tail_round_equal_row_slabs(jf, orc):
     check_gemm_parity(f"wgrad {M}x{N}x{K} sampled dW rows", full[rows],
                       orc.gemm_wgrad(odq, ods, oxq, oxs, rows=rows, mode=orc.MFMA),
                       orc.gemm_wgrad(odq, ods, oxq, oxs, rows=rows, mode=orc.EXACT))
+
+
+@pytest.mark.parametrize("K", [128, 1152])
+def test_alternating_phase_kernel_edges(jf, orc, K):
+    """Forward and DGrad on 256 x 256 tiles (the alternating-phase schedule) at M = 20000 rows (79 row tiles, the
+    last 32 rows deep) and 1152 output columns (5 column tiles, the last 128 wide): 395 tiles, so blocks take one or
+    two tiles.  Forward contracts over K: one group (K = 128: a tile's first and last group coincide, so its rows
+    are stored across the next tile's phases) or nine.  DGrad contracts over the 1152 columns (nine groups) into K
+    outputs: at K = 1152 the same 395 tiles; at K = 128, 79 tiles on the quarter-tile schedule.  Bit for bit
+    against the same rows computed 128 at a time (the quarter-tile schedule) and, on sampled rows, against the
+    oracle."""
+    import torch
+    M, N = 20000, 1152
+    T, R = _tiles_and_rounds(M, N)
+    print(f"M={M} N={N} K={K}: {T} tiles of 256 x 256, last round {R} (no quarter-tile tail)", flush=True)
+    assert T > 256 and 2 * R > 256
+    xb, wb, dyb = _x(M, K, 201 + K), _w(N, K, 202 + K), _dy(M, N, 203 + K)
+    wq, ws, wqT = jf.quantize_blocks(bits_to_dev(wb))
+    xq, xs = jf.quantize_rows(bits_to_dev(xb))
+    y = jf.gemm_fwd(xq, xs, wq, ws)
+    y_parts = [jf.gemm_fwd(xq[r:r + 128].contiguous(), xs[:, r:r + 128].contiguous(), wq, ws) for r in range(0, M, 128)]
+    # DGrad: dY [M, N] against W [N, K]; its 1x128 groups run along N
+    dyq, dys = jf.quantize_rows(bits_to_dev(dyb))
+    dx = jf.gemm_dgrad(dyq, dys, wqT, ws)
+    dx_parts = [jf.gemm_dgrad(dyq[r:r + 128].contiguous(), dys[:, r:r + 128].contiguous(), wqT, ws)
+                for r in range(0, M, 128)]
+    torch.cuda.synchronize()
+    yb, dxb = dev_to_bits(y), dev_to_bits(dx)
+    assert np.array_equal(yb, np.concatenate([dev_to_bits(p) for p in y_parts])), ("fwd", K)
+    assert np.array_equal(dxb, np.concatenate([dev_to_bits(p) for p in dx_parts])), ("dgrad", K)
+    rows = np.array([0, 255, 256, 9999, M - 33, M - 32, M - 1])
+    owq, ows = orc.quantize_blocks(wb)
+    oxq, oxs = orc.quantize_rows(xb[rows])
+    check_gemm_parity(f"alternating-phase fwd {M}x{N}x{K} sampled rows", yb[rows],
+                      orc.gemm_fwd(oxq, oxs, owq, ows, mode=orc.MFMA), orc.gemm_fwd(oxq, oxs, owq, ows, mode=orc.EXACT))
+    odq, ods = orc.quantize_rows(dyb[rows])
+    check_gemm_parity(f"alternating-phase dgrad {M}x{N}x{K} sampled rows", dxb[rows],
+                      orc.gemm_dgrad(odq, ods, owq, ows, mode=orc.MFMA),
+                      orc.gemm_dgrad(odq, ods, owq, ows, mode=orc.EXACT))
