@@ -74,9 +74,14 @@ DECODE_SOURCES = [os.path.join(CSRC, f) for f in ("jetfp8_decode.hip", "jetfp8_m
 
 
 def source_digest(paths=GEMM_SOURCES) -> str:
-    """sha256 over the kernel's source files: a traffic record applies only to the kernel it was taken on."""
+    """sha256 over the kernel's source files with comments and blank lines removed: a traffic record applies only
+    to the code it was taken on, and an edit of comments alone does not void it."""
     import hashlib
-    return hashlib.sha256(b"".join(open(p, "rb").read() for p in paths)).hexdigest()
+    import re
+    text = "\n".join(open(p).read() for p in paths)
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    lines = (re.sub(r"//.*", "", line).rstrip() for line in text.splitlines())
+    return hashlib.sha256("\n".join(line for line in lines if line).encode()).hexdigest()
 
 
 def recorded_traffic(path, workload):
@@ -276,13 +281,11 @@ PRODUCER_SOURCES = [os.path.join(ROOT, "fp8_precision_rl_amd", "csrc", f) for f 
 def producer_traffic(path=os.path.join(ROOT, "profiles", "producers_traffic.json")):
     """Per-launch HBM bytes of the producer kernels from rocprofv3 FETCH_SIZE / WRITE_SIZE (scaled by a 1 GiB
     copy), or None when the record is missing or was taken on other kernel sources."""
-    import hashlib
     try:
         rec = json.load(open(path))
     except (OSError, ValueError):
         return None
-    digest = hashlib.sha256(b"".join(open(f, "rb").read() for f in PRODUCER_SOURCES)).hexdigest()
-    if rec.get("source_sha256") != digest:
+    if rec.get("source_sha256") != source_digest(PRODUCER_SOURCES):
         return None
     return {k: v["bytes"] for k, v in rec["kernels"].items()}
 

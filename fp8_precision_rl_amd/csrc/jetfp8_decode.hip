@@ -1,5 +1,5 @@
 // Small-M schedule of the block-scaled FP8 forward GEMM (rollout decode batches) for gfx950: the same
-// per-element operation sequence as the large-M kernel (jetfp8_gemm.hip), so an output row's bits do not depend
+// per-element operation sequence as the large-M kernels (jetfp8_gemm.hip), so an output row's bits do not depend
 // on which schedule computed it (Jet-RL explainers, "Architecture Centrale": the rollout graph is a subgraph of
 // the training forward graph with the same quantization).
 #include "jetfp8_common.h"
@@ -16,9 +16,9 @@ namespace jetfp8 {
 //     stream never drains between slices;
 //   - the groups of the contraction are dealt out in chunks of 8, one group per wave: the wave forms the
 //     group products of its group with one V_MFMA_F32_16X16X128_F8F6F4 per 16-row tile (B fragment first,
-//     C = 0, exactly as the large kernel), and parks them in LDS;
+//     C = 0, exactly as the large-M kernels), and parks them in LDS;
 //   - after a barrier every wave runs the promotion acc = fma(p, fl32(sa * sb), acc) for its share of the
-//     outputs over the chunk's groups in ascending order -- the same chain the large kernel runs, so every
+//     outputs over the chunk's groups in ascending order -- the same chain the large-M kernels run, so every
 //     output row is bitwise the same whichever kernel computed it;
 //   - operand fragments go straight from global memory into registers, D_AHEAD chunks ahead (2 for RT >= 2;
 //     range-checked buffer loads: rows past I and groups past the contraction read as zero and are never

@@ -9,11 +9,14 @@
 // acc = fma(p, fl32(sa * sb), acc), groups in ascending order.  The per-element operation sequence does
 // not depend on the tile an element lands in, so a row's bits do not depend on M.
 //
-// Layout of the work (large-M kernel):
+// Layout of the work (large-M kernels):
 //   - 512 threads = 8 waves (2 per SIMD), block tile 256 x 256, wave tile 128 x 64 (8 x 4 MFMA tiles), so
 //     each fragment byte read from LDS feeds 2.7 matrix ops on average (LDS bandwidth is the tight resource);
 //   - A and B group tiles and their scales stream global -> LDS with buffer_load ... lds into a 2-stage
-//     ring (one group in flight while one is multiplied, one barrier per group);
+//     ring (one group in flight while one is multiplied);
+//   - two schedules: gemm_large_kernel interleaves the two waves of each SIMD (one barrier per group; WGrad, and
+//     128 x 128 quarter tiles for every GEMM), gemm_pp_kernel runs them in alternating memory and compute phases
+//     (four barriers per group; forward and DGrad on 256 x 256 tiles);
 //   - LDS rows are 128 bytes with the 16-byte chunks of a row XOR-permuted (see swz) for the fragment reads;
 //   - block-scaled B (forward, DGrad): s = fl32(sa * sb) per row and group (the block scale is uniform over
 //     the tile); row-scaled B (WGrad): sa * sb per element;

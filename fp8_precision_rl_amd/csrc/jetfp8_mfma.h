@@ -1,4 +1,4 @@
-// Pieces shared by the two FP8 GEMM schedules (the large-M kernel in jetfp8_gemm.hip, the small-M kernel in
+// Pieces shared by the FP8 GEMM schedules (the large-M kernels in jetfp8_gemm.hip, the small-M kernel in
 // jetfp8_decode.hip): the group product instruction, buffer descriptors, the group width and the device's
 // compute-unit count.
 #pragma once

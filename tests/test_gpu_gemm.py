@@ -202,7 +202,7 @@ def _tiles_and_rounds(M, N):
 
 
 def test_large_tiles_and_tail_round_equal_quarter_tiles(jf, orc):
-    """Schedules of the large-M kernel against each other, bit for bit (each output element goes through the same
+    """Schedules of the large-M kernels against each other, bit for bit (each output element goes through the same
     operation sequence in all of them):
       * M = 8192, N = 2048: 256 tiles of 256 x 256, one full round (no quarter tiles);
       * M = 4352, N = 4096: 272 tiles, one full round and a last round of 16 tiles run as 64 quarter tiles;
