@@ -50,3 +50,12 @@ def test_recorded_traffic_needs_matching_source_and_workload(tmp_path):
     p.write_text(json.dumps(dict(good, kernel_source_sha256="0" * 64)))
     assert bench.recorded_traffic(str(p), "llama3_8b_train_m16384") is None
     assert bench.recorded_traffic(str(tmp_path / "missing.json"), "llama3_8b_train_m16384") is None
+
+
+def test_source_digest_ignores_comments_only(tmp_path):
+    a, b, c = tmp_path / "a.hip", tmp_path / "b.hip", tmp_path / "c.hip"
+    a.write_text("// header\nint f(int x) {\n    return x + 1;  // one more\n}\n")
+    b.write_text("/* another\n   header */\n\nint f(int x) {\n    return x + 1;\n}\n// trailer\n")
+    c.write_text("int f(int x) {\n    return x + 2;\n}\n")
+    assert bench.source_digest([str(a)]) == bench.source_digest([str(b)])
+    assert bench.source_digest([str(a)]) != bench.source_digest([str(c)])
