@@ -403,9 +403,9 @@ __global__ __launch_bounds__(L_THREADS, SPLIT) void gemm_large_kernel(
 // The same tiles, staging ring, LDS layout and per-element operation sequence as gemm_large_kernel (so the same
 // bits), scheduled so that the matrix unit of a SIMD is fed by one wave at a time while its partner reads LDS:
 //   - a group is two halves (row tiles 0-3, 4-7 of the wave tile); each half is a memory phase (the half's A
-//     fragments, at the first half also the B fragments and the refill loads of the next group) and a compute
-//     phase (16 matrix ops, each followed in issue order by the promotion of the previous row tile's product of
-//     the same column tile, so the VALU works under the matrix unit);
+//     fragments and row scales, at the first half also the B fragments, then staging loads for the ring) and a
+//     compute phase (16 matrix ops, each preceded in issue order by the promotion of the previous row tile's
+//     product of the same column tile, so the VALU works under the matrix unit);
 //   - waves 0-3 (wm = 0, one per SIMD) run one phase ahead of waves 4-7 (wm = 1): between two block barriers
 //     one wave of each SIMD computes while the other loads.  Register-only measurement on gfx950: one wave issuing
 //     matrix op + 4 promotion FMAs in this order keeps the matrix unit 90 % as busy as matrix ops alone; 16 FMAs
@@ -414,7 +414,9 @@ __global__ __launch_bounds__(L_THREADS, SPLIT) void gemm_large_kernel(
 //     next group's first compute phase.  Rows 0-2 of a tile are final after the first compute phase of its last
 //     group and are stored in the next memory phase; rows 3-6 and row 7 in the memory phases of the next tile's
 //     first group;
-//   - the refill of the ring is spread over all four memory phases of a group (see the staging comment below).
+//   - the refill of the ring is spread over all four memory phases of a group (see the staging comment below);
+//   - a wave raises its issue priority in its memory phases, so its reads and loads are not held up behind the
+//     partner's matrix ops.
 __global__ __launch_bounds__(L_THREADS, 1) void gemm_pp_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ As, const uint8_t* __restrict__ B,
     const float* __restrict__ Bs, uint16_t* __restrict__ Cout, int64_t I, int64_t J, int64_t Kc, int64_t sbj,
@@ -445,7 +447,7 @@ __global__ __launch_bounds__(L_THREADS, 1) void gemm_pp_kernel(
         c.ra = make_rsrc(A + (int64_t)c.i0 * Kc, rows_a * (int)Kc);
         c.rb = make_rsrc(B + (int64_t)c.j0 * Kc, rows_b * (int)Kc);
         c.rsa = make_rsrc(As + c.i0, sa_bytes);
-        c.rsb = c.rsa;
+        c.rsb = c.rsa;                                           // unused here: B is block-scaled
         return c;
     };
 
