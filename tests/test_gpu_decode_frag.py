@@ -105,3 +105,28 @@ def test_frag_gemm_rejects_more_than_64_rows(jf):
     with pytest.raises(jf.JetFP8Error) as e:
         jf.gemm_fwd_frag(xq, xs, wqf, ws)
     assert e.value.status == jf.ERR_SHAPE
+
+
+@pytest.mark.parametrize("M", [1, 16, 17, 32])
+def test_wide_schedule_equals_row_major(jf, orc, M):
+    """Gate/up-shaped forward (28672 output columns, 1792 slices, K = 4096) over fragment-ordered weights runs the
+    wide small-M schedule (each wave owns whole slices, activations held in LDS): bitwise equal to the row-major
+    weights on the slice-sharing schedule, and sampled columns against the oracle."""
+    import torch
+    N, K = 28672, 4096
+    wb = _w(N, K, 11 + M)
+    w = bits_to_dev(wb)
+    wq, ws = jf.quantize_blocks(w, transposed=False)
+    wqf, wsf = jf.quantize_blocks_frag(w)
+    xb = _x(M, K, 12 + M)
+    xq, xs = jf.quantize_rows(bits_to_dev(xb))
+    y = jf.gemm_fwd(xq, xs, wq, ws)
+    yf = jf.gemm_fwd_frag(xq, xs, wqf, wsf)
+    torch.cuda.synchronize()
+    yb, yfb = dev_to_bits(y), dev_to_bits(yf)
+    assert np.array_equal(yfb, yb), M
+    cols = np.r_[0:128, 14336:14464, N - 128:N]
+    oxq, oxs = orc.quantize_rows(xb)
+    owq, ows = orc.quantize_blocks(wb[cols])
+    check_gemm_parity(f"wide decode {M}x{N}x{K} sampled column blocks", yfb[:, cols],
+                      orc.gemm_fwd(oxq, oxs, owq, ows, mode=orc.MFMA), orc.gemm_fwd(oxq, oxs, owq, ows, mode=orc.EXACT))
