@@ -367,6 +367,200 @@ static hipError_t launch_decode_wide(const uint8_t* A, const float* As, const ui
     return hipGetLastError();
 }
 
+// ---- small-M schedule for narrow outputs over fragment-ordered weights ------------------------------------
+// For fewer slices than that (QKV, O and down projections), the slice-sharing schedule above keeps too few weight
+// bytes in flight.  Here a block takes S adjacent 16-column slices (S = 2 when one slice per block would need
+// more blocks than there are CUs) and the slices' groups are dealt out to the 8 waves in rounds of 8 GPW groups
+// (group r R + 8 i + w to wave w):
+//   - each wave requests the operands of its groups for NBUF rounds at once: the fragment-ordered weights (whole
+//     lines) of every slice and one activation fragment per row tile, which serves all S slices;
+//   - for 17-32 rows the activation rows are loaded row-contiguous (8 whole lines per load) and moved into the
+//     fragment layout through 1 KB of the wave's own LDS per row tile, as in the slice-sharing schedule;
+//   - the products go to LDS, and after one barrier per round every thread runs the promotion chain of its outputs
+//     (one per slice) over the round's groups in ascending order: acc = fma(p, fl32(sa * sb), acc).
+// One round (GPW = 4, all operands in flight at once) when the contraction has at most 32 groups, else rounds of
+// 16 groups with two rounds in flight (GPW = 2, NBUF = 2; measured faster than 32-group rounds and than 3 rounds
+// in flight on the 14336-long contraction).
+template <int RT, int S, bool MULTI>
+struct SplitCfg {
+    static constexpr int GPW = MULTI ? 2 : 4, NBUF = MULTI ? 2 : 1, PB = MULTI ? 2 : 1, GMAX = MULTI ? 128 : 32;
+    static constexpr bool ROWC = RT >= 2;
+    static constexpr int WPE = (RT == 1 && S == 1 && !MULTI) ? 3 : 2;   // waves per SIMD that LDS and registers allow
+};
+
+template <int RT, int S, bool MULTI>
+__global__ __launch_bounds__(D_THREADS) __attribute__((amdgpu_waves_per_eu(SplitCfg<RT, S, MULTI>::WPE)))
+void gemm_decode_split_kernel(const uint8_t* __restrict__ A, const float* __restrict__ As,
+                              const uint8_t* __restrict__ Bf, const float* __restrict__ Bs,
+                              uint16_t* __restrict__ Cout, int I, int J, int Kc) {
+    using C = SplitCfg<RT, S, MULTI>;
+    constexpr int GPW = C::GPW, NBUF = C::NBUF, PB = C::PB, GMAX = C::GMAX;
+    constexpr bool ROWC = C::ROWC;
+    constexpr int R = D_WAVES * GPW, MR = 16 * RT;
+    constexpr int LPR = GPW * (2 * S + 2 * RT);                  // vector loads per wave per round
+    __shared__ v4f pbuf[S][PB][R][RT][64];
+    __shared__ float sa_lds[GMAX * MR + 64];                     // [g][m] (+ the last load's overhang)
+    __shared__ __attribute__((aligned(16))) uint8_t xbuf[ROWC ? D_WAVES * RT * 1024 : 16];
+    const int t = threadIdx.x, lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int sl0 = (int)blockIdx.x * S;
+    const int G = Kc / BK, nr = (G + R - 1) / R;
+
+    // activation row scales into LDS, before any other load (direct-to-LDS, 64 entries per load; entries of rows
+    // past I hold other scales or zeros: those rows are never stored)
+    {
+        const rsrc_t rsa = make_rsrc(As, G * I * 4);
+        for (int e0 = wave * 64; e0 < G * MR; e0 += D_THREADS) {
+            const int e = e0 + lane, g = e / MR, m = e % MR;
+            JETFP8_DEC_LOAD_LDS(rsa, (lds_void*)(sa_lds + e0), 4, (g * I + m) * 4, 0);
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // block scales of the slices' groups (S <= 2 slices never straddle a 128-row block): lane l holds group l (sb0)
+    // and group 64 + l (sb1)
+    const rsrc_t rbs = make_rsrc(Bs + (int64_t)(sl0 >> 3) * G, G * 4);
+    const float sb0 = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rbs, lane * 4, 0, 0));
+    const float sb1 = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rbs, lane * 4, 256, 0));
+
+    const rsrc_t rb = make_rsrc(Bf + (int64_t)sl0 * G * 2048, S * G * 2048);
+    const rsrc_t ra = make_rsrc(A, I * Kc);
+    int va[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+        va[rt] = ROWC ? (rt * 16 + (lane >> 3)) * Kc + (lane & 7) * 16 : (rt * 16 + (lane & 15)) * Kc + 32 * (lane >> 4);
+    // ROWC: lane l loads row l / 8 (the second load rows 8..15), 16-byte piece l % 8; written to the wave's slot
+    // with the pieces of a row XOR-permuted by the row, read back as lane t: row t % 16, pieces 2 (t / 16), +1
+    const int wpos = (lane >> 3) * 128 + (((lane & 7) ^ (lane >> 3)) << 4);
+    const int r8 = lane & 7, q2 = 2 * (lane >> 4);
+    const int rpos0 = r8 * 128 + ((q2 ^ r8) << 4), rpos1 = r8 * 128 + (((q2 + 1) ^ r8) << 4);
+    const bool hi_rows = (lane & 15) >= 8;
+
+    u32x4 wf[NBUF][GPW][S][2], af[NBUF][GPW][RT][2];
+    // round r's operands (groups past the contraction: weights at an offset past the range, which reads zeros;
+    // their activation loads stay in range and are never used)
+    auto load_round = [&](int r, u32x4 (&w)[GPW][S][2], u32x4 (&a)[GPW][RT][2]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < GPW; ++i) {
+            const int g = r * R + 8 * i + wave;
+            const int gc = g < G ? g : 0;
+#pragma unroll
+            for (int sx = 0; sx < S; ++sx) {
+                const int go = g < G ? (sx * G + g) * 2048 : S * G * 2048;
+                w[i][sx][0] = __builtin_amdgcn_raw_buffer_load_b128(rb, 16 * lane, go, 0);
+                w[i][sx][1] = __builtin_amdgcn_raw_buffer_load_b128(rb, 16 * lane + 1024, go, 0);
+            }
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                a[i][rt][0] = __builtin_amdgcn_raw_buffer_load_b128(ra, va[rt], gc * BK, 0);
+                a[i][rt][1] = __builtin_amdgcn_raw_buffer_load_b128(ra, va[rt] + (ROWC ? 8 * Kc : 16), gc * BK, 0);
+            }
+        }
+    };
+#pragma unroll
+    for (int k = 0; k < NBUF; ++k) load_round(k, wf[k], af[k]);
+
+    // promotion ownership: thread t < 16 MR holds, in each slice, element t & 3 of lane (t >> 2) & 63 of row tile
+    // t >> 8: output row (t >> 8) 16 + ((t >> 2) & 15), column 4 ((t >> 6) & 3) + (t & 3)
+    const int ln = (t >> 2) & 63, m = (t >> 8) * 16 + (ln & 15);
+    float acc[S];
+#pragma unroll
+    for (int sx = 0; sx < S; ++sx) acc[sx] = 0.0f;
+    auto round = [&](int r, u32x4 (&w)[GPW][S][2], u32x4 (&a)[GPW][RT][2]) __attribute__((always_inline)) {
+        const int pb = PB > 1 ? (r & 1) : 0;
+#pragma unroll
+        for (int i = 0; i < GPW; ++i) {
+            const int g = r * R + 8 * i + wave;
+            if (g < G) {
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt) {
+                    u32x4 f0 = a[i][rt][0], f1 = a[i][rt][1];
+                    if (ROWC) {
+                        uint8_t* slot = xbuf + (wave * RT + rt) * 1024;
+                        u32x4 lo[2], hi[2];
+#pragma unroll
+                        for (int h = 0; h < 2; ++h) {
+                            *reinterpret_cast<u32x4*>(slot + wpos) = a[i][rt][h];
+                            lo[h] = *reinterpret_cast<const u32x4*>(slot + rpos0);
+                            hi[h] = *reinterpret_cast<const u32x4*>(slot + rpos1);
+                        }
+                        f0 = hi_rows ? lo[1] : lo[0];
+                        f1 = hi_rows ? hi[1] : hi[0];
+                    }
+                    const v8i afrag = (v8i){(int)f0[0], (int)f0[1], (int)f0[2], (int)f0[3],
+                                            (int)f1[0], (int)f1[1], (int)f1[2], (int)f1[3]};
+#pragma unroll
+                    for (int sx = 0; sx < S; ++sx) {
+                        const v8i bfrag = (v8i){(int)w[i][sx][0][0], (int)w[i][sx][0][1], (int)w[i][sx][0][2],
+                                                (int)w[i][sx][0][3], (int)w[i][sx][1][0], (int)w[i][sx][1][1],
+                                                (int)w[i][sx][1][2], (int)w[i][sx][1][3]};
+                        pbuf[sx][pb][8 * i + wave][rt][lane] = mfma_group(bfrag, afrag);
+                    }
+                }
+            }
+        }
+        if (MULTI && r + NBUF < nr) load_round(r + NBUF, w, a);
+        // the row-scale loads came first, so with at most NBUF rounds' loads outstanding they are in LDS; this
+        // wave's products are in LDS; then every wave is here
+        __builtin_amdgcn_s_waitcnt((NBUF * LPR & 15) | ((NBUF * LPR >> 4) << 14) | (7 << 4));
+        __builtin_amdgcn_s_barrier();
+        if (t < 16 * MR) {
+            const float sbr = r * R < 64 ? sb0 : sb1;             // R divides 64: a round lies in one half
+#pragma unroll
+            for (int ig = 0; ig < R; ++ig) {
+                const int g = r * R + ig;
+                if (g < G) {
+                    const float sb = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sbr), g & 63));
+                    const float s = sa_lds[g * MR + m] * sb;                      // s = fl32(sa * sb)
+#pragma unroll
+                    for (int sx = 0; sx < S; ++sx) {
+                        const float* pf = reinterpret_cast<const float*>(&pbuf[sx][pb][0][0][0]) + t;
+                        acc[sx] = fmaf(pf[ig * RT * 256], s, acc[sx]);
+                    }
+                }
+            }
+        }
+    };
+    for (int r = 0; r < nr; r += NBUF) {
+#pragma unroll
+        for (int k = 0; k < NBUF; ++k)
+            if (r + k < nr) round(r + k, wf[k], af[k]);
+    }
+    if (t < 16 * MR && m < I) {
+#pragma unroll
+        for (int sx = 0; sx < S; ++sx)
+            Cout[(int64_t)m * J + (sl0 + sx) * 16 + 4 * (ln >> 4) + (t & 3)] = (uint16_t)f32_to_bf16_rne(acc[sx]);
+    }
+}
+
+// Whether a fragment-ordered forward GEMM can take the per-slice schedule: at most 32 rows and 128 groups.
+// Measured at 32 rows on the Llama-3-8B projections (against the slice-sharing schedule, bitwise equal): QKV
+// 12.6 -> 10.4 us (two slices per block), O 9.0 -> 8.1, down 23.5 -> 20.2; at one row QKV 9.9 -> 8.1, O 6.7 ->
+// 5.9, down 14.9 -> 12.2.
+static bool decode_split_fits(int64_t M, int64_t K) { return M <= 32 && K / BK <= 128; }
+
+template <int RT>
+static hipError_t launch_decode_split(const uint8_t* A, const float* As, const uint8_t* Bf, const float* Bs,
+                                      uint16_t* C, int64_t M, int64_t N, int64_t K, int cus, hipStream_t st) {
+    const int G = (int)(K / BK), slices = (int)(N / 16);
+    const dim3 block(D_THREADS);
+    const int i = (int)M, j = (int)N, kc = (int)K;
+    if (G > 32) {
+        hipLaunchKernelGGL((gemm_decode_split_kernel<RT, 1, true>), dim3((unsigned)slices), block, 0, st, A, As, Bf,
+                           Bs, C, i, j, kc);
+        return hipGetLastError();
+    }
+    if constexpr (RT == 2) {
+        if (slices > cus) {                 // slices is a multiple of 8 (N % 128 == 0)
+            hipLaunchKernelGGL((gemm_decode_split_kernel<RT, 2, false>), dim3((unsigned)(slices / 2)), block, 0, st,
+                               A, As, Bf, Bs, C, i, j, kc);
+            return hipGetLastError();
+        }
+    }
+    hipLaunchKernelGGL((gemm_decode_split_kernel<RT, 1, false>), dim3((unsigned)slices), block, 0, st, A, As, Bf, Bs,
+                       C, i, j, kc);
+    return hipGetLastError();
+}
+
 bool decode_rows_fit(int64_t rows, int64_t Kc) { return rows <= 64 && (Kc / BK) * rows <= D_SA_MAX; }
 
 hipError_t launch_decode_rows(const uint8_t* A, const float* As, const uint8_t* B, const float* Bs, uint16_t* C,
@@ -384,6 +578,9 @@ hipError_t launch_gemm_fwd_frag(const uint8_t* xq, const float* xs, const uint8_
     if (decode_wide_fits(M, N, K, cus))
         return M <= 16 ? launch_decode_wide<1>(xq, xs, wqf, ws, y, M, N, K, cus, st)
                        : launch_decode_wide<2>(xq, xs, wqf, ws, y, M, N, K, cus, st);
+    if (decode_split_fits(M, K))
+        return M <= 16 ? launch_decode_split<1>(xq, xs, wqf, ws, y, M, N, K, cus, st)
+                       : launch_decode_split<2>(xq, xs, wqf, ws, y, M, N, K, cus, st);
     return launch_rows<true>(xq, xs, wqf, ws, y, M, 0, M, N, K, K / BK, 1, st);
 }
 

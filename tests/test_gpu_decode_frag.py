@@ -8,6 +8,9 @@ weights in 128x128 blocks), chosen so the small-M GEMM kernel reads whole 128-by
   * jetfp8_gemm_fwd_frag is bitwise equal to jetfp8_gemm_fwd on the row-major codes for every small-M row-tile
     count (1, 16, 17, 32, 33, 64 rows), on a ragged contraction (11 groups) with more column slices than blocks and
     on a Llama-3-8B-shaped linear, and matches the oracle;
+  * the three small-M schedules for fragment-ordered weights (wide outputs: a wave per slice; fewer slices: a
+    block per one or two slices with the groups dealt out in rounds; more than 32 rows or 128 groups: the
+    slice-sharing schedule) each equal the row-major call bitwise and the oracle on sampled column blocks;
   * more than 64 rows is a shape error.
 """
 import numpy as np
@@ -129,4 +132,40 @@ def test_wide_schedule_equals_row_major(jf, orc, M):
     oxq, oxs = orc.quantize_rows(xb)
     owq, ows = orc.quantize_blocks(wb[cols])
     check_gemm_parity(f"wide decode {M}x{N}x{K} sampled column blocks", yfb[:, cols],
+                      orc.gemm_fwd(oxq, oxs, owq, ows, mode=orc.MFMA), orc.gemm_fwd(oxq, oxs, owq, ows, mode=orc.EXACT))
+
+
+@pytest.mark.parametrize("M,N,K", [
+    (1, 4096, 4096),      # one slice per block, one round of 32 groups, 16-row tile
+    (16, 6144, 4096),     # more slices than CUs, 16-row tile: still one slice per block
+    (17, 4096, 4096),     # 32-row tile (row-contiguous activation loads), one slice per block
+    (32, 6144, 4096),     # more slices than CUs, 32-row tile: two slices per block
+    (29, 2048, 640),      # 5 groups: three waves of the round idle
+    (32, 4096, 14336),    # down projection: 7 rounds of 16 groups, two in flight
+    (5, 1024, 4736),      # 37 groups: a ragged last round (5 groups)
+    (32, 128, 16384),     # 128 groups, the most the per-slice schedule takes; 8 slices
+    (32, 256, 16512),     # 129 groups: back on the slice-sharing schedule
+])
+def test_per_slice_schedule_equals_row_major(jf, orc, M, N, K):
+    """Forward GEMMs with fewer 16-column slices than the wide schedule needs (QKV, O, down shapes) run the
+    per-slice small-M schedule over fragment-ordered weights (a block per one or two slices, the slices' groups
+    dealt out to the waves in rounds, products promoted after one barrier per round): bitwise equal to the
+    row-major weights on the slice-sharing schedule, and the first and last column blocks against the oracle."""
+    import torch
+    wb = _w(N, K, 21 + M + N)
+    w = bits_to_dev(wb)
+    wq, ws = jf.quantize_blocks(w, transposed=False)
+    wqf, wsf = jf.quantize_blocks_frag(w)
+    del w
+    xb = _x(M, K, 22 + M)
+    xq, xs = jf.quantize_rows(bits_to_dev(xb))
+    y = jf.gemm_fwd(xq, xs, wq, ws)
+    yf = jf.gemm_fwd_frag(xq, xs, wqf, wsf)
+    torch.cuda.synchronize()
+    yb, yfb = dev_to_bits(y), dev_to_bits(yf)
+    assert np.array_equal(yfb, yb), (M, N, K)
+    cols = np.r_[0:128, N - 128:N] if N > 128 else np.r_[0:128]
+    oxq, oxs = orc.quantize_rows(xb)
+    owq, ows = orc.quantize_blocks(wb[cols])
+    check_gemm_parity(f"per-slice decode {M}x{N}x{K} first/last column blocks", yfb[:, cols],
                       orc.gemm_fwd(oxq, oxs, owq, ows, mode=orc.MFMA), orc.gemm_fwd(oxq, oxs, owq, ows, mode=orc.EXACT))
