@@ -375,16 +375,20 @@ static hipError_t launch_decode_wide(const uint8_t* A, const float* As, const ui
 //   - each wave requests the operands of its groups for NBUF rounds at once: the fragment-ordered weights (whole
 //     lines) of every slice and one activation fragment per row tile, which serves all S slices;
 //   - for 17-32 rows the activation rows are loaded row-contiguous (8 whole lines per load) and moved into the
-//     fragment layout through 1 KB of the wave's own LDS per row tile, as in the slice-sharing schedule;
+//     fragment layout through the wave's own LDS: a 2 KB slot per row tile holds both 8-row halves, so each lane
+//     reads back only its own 32 bytes (with two slices per block, for LDS room, a 1 KB slot taken one half at a
+//     time, as in the slice-sharing schedule);
 //   - the products go to LDS, and after one barrier per round every thread runs the promotion chain of its outputs
 //     (one per slice) over the round's groups in ascending order: acc = fma(p, fl32(sa * sb), acc).
 // One round (GPW = 4, all operands in flight at once) when the contraction has at most 32 groups, else rounds of
-// 16 groups with two rounds in flight (GPW = 2, NBUF = 2; measured faster than 32-group rounds and than 3 rounds
-// in flight on the 14336-long contraction).
+// 8 groups with four rounds in flight (GPW = 1, NBUF = 4).  On the 14336-long contraction at 32 rows that measured
+// 18.0 -> 17.4 us against 16-group rounds with two in flight, which beat 32-group rounds and three 16-group rounds
+// in flight; the 2 KB detour slot measured 19.6 -> 18.0 us there and O 7.4 -> 6.8 us.
 template <int RT, int S, bool MULTI>
 struct SplitCfg {
-    static constexpr int GPW = MULTI ? 2 : 4, NBUF = MULTI ? 2 : 1, PB = MULTI ? 2 : 1, GMAX = MULTI ? 128 : 32;
+    static constexpr int GPW = MULTI ? 1 : 4, NBUF = MULTI ? 4 : 1, PB = MULTI ? 2 : 1, GMAX = MULTI ? 128 : 32;
     static constexpr bool ROWC = RT >= 2;
+    static constexpr bool XFULL = S == 1;                        // a 2 KB detour slot per row tile (both halves)
     static constexpr int WPE = (RT == 1 && S == 1 && !MULTI) ? 3 : 2;   // waves per SIMD that LDS and registers allow
 };
 
@@ -395,12 +399,12 @@ void gemm_decode_split_kernel(const uint8_t* __restrict__ A, const float* __rest
                               uint16_t* __restrict__ Cout, int I, int J, int Kc) {
     using C = SplitCfg<RT, S, MULTI>;
     constexpr int GPW = C::GPW, NBUF = C::NBUF, PB = C::PB, GMAX = C::GMAX;
-    constexpr bool ROWC = C::ROWC;
+    constexpr bool ROWC = C::ROWC, XFULL = C::XFULL;
     constexpr int R = D_WAVES * GPW, MR = 16 * RT;
     constexpr int LPR = GPW * (2 * S + 2 * RT);                  // vector loads per wave per round
     __shared__ v4f pbuf[S][PB][R][RT][64];
     __shared__ float sa_lds[GMAX * MR + 64];                     // [g][m] (+ the last load's overhang)
-    __shared__ __attribute__((aligned(16))) uint8_t xbuf[ROWC ? D_WAVES * RT * 1024 : 16];
+    __shared__ __attribute__((aligned(16))) uint8_t xbuf[ROWC ? D_WAVES * RT * (XFULL ? 2048 : 1024) : 16];
     const int t = threadIdx.x, lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int sl0 = (int)blockIdx.x * S;
@@ -434,6 +438,7 @@ void gemm_decode_split_kernel(const uint8_t* __restrict__ A, const float* __rest
     const int r8 = lane & 7, q2 = 2 * (lane >> 4);
     const int rpos0 = r8 * 128 + ((q2 ^ r8) << 4), rpos1 = r8 * 128 + (((q2 + 1) ^ r8) << 4);
     const bool hi_rows = (lane & 15) >= 8;
+    const int fpos0 = (hi_rows ? 1024 : 0) + rpos0, fpos1 = (hi_rows ? 1024 : 0) + rpos1;
 
     u32x4 wf[NBUF][GPW][S][2], af[NBUF][GPW][RT][2];
     // round r's operands (groups past the contraction: weights at an offset past the range, which reads zeros;
@@ -474,7 +479,13 @@ void gemm_decode_split_kernel(const uint8_t* __restrict__ A, const float* __rest
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt) {
                     u32x4 f0 = a[i][rt][0], f1 = a[i][rt][1];
-                    if (ROWC) {
+                    if (ROWC && XFULL) {
+                        uint8_t* slot = xbuf + (wave * RT + rt) * 2048;
+                        *reinterpret_cast<u32x4*>(slot + wpos) = a[i][rt][0];
+                        *reinterpret_cast<u32x4*>(slot + 1024 + wpos) = a[i][rt][1];
+                        f0 = *reinterpret_cast<const u32x4*>(slot + fpos0);
+                        f1 = *reinterpret_cast<const u32x4*>(slot + fpos1);
+                    } else if (ROWC) {
                         uint8_t* slot = xbuf + (wave * RT + rt) * 1024;
                         u32x4 lo[2], hi[2];
 #pragma unroll

@@ -141,7 +141,7 @@ def test_wide_schedule_equals_row_major(jf, orc, M):
     (17, 4096, 4096),     # 32-row tile (row-contiguous activation loads), one slice per block
     (32, 6144, 4096),     # more slices than CUs, 32-row tile: two slices per block
     (29, 2048, 640),      # 5 groups: three waves of the round idle
-    (32, 4096, 14336),    # down projection: 7 rounds of 16 groups, two in flight
+    (32, 4096, 14336),    # down projection: 14 rounds of 8 groups, four in flight
     (5, 1024, 4736),      # 37 groups: a ragged last round (5 groups)
     (32, 128, 16384),     # 128 groups, the most the per-slice schedule takes; 8 slices
     (32, 256, 16512),     # 129 groups: back on the slice-sharing schedule
