@@ -468,8 +468,8 @@ def run_decode(args, torch, jf, workloads):
                    "step": "per linear: X rows quant (1x128), fwd GEMM against FP8 weights quantized beforehand",
                    "weights": "fragment order (jetfp8_gemm_fwd_frag)" if frag else "row-major (jetfp8_gemm_fwd)"},
         "roofline": {"bound": "hbm",
-                     "kernel": (f"gemm_decode_split_kernel<{rt}, S, MULTI> (narrow outputs), "
-                                f"gemm_decode_wide_kernel<{rt}> (wide outputs)"
+                     "kernel": (f"gemm_decode_wide_kernel<{rt}> (wide outputs), gemm_decode_split_kernel<{rt}, S> "
+                                f"(narrow outputs), gemm_decode_roles_kernel<{rt}> (long contractions)"
                                 if frag and rt <= 2 else f"gemm_decode_kernel<{rt}, {'true' if frag else 'false'}>"),
                      "achieved": round(gemm_bytes / (gemm_ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gemm_bytes / (gemm_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),

@@ -237,6 +237,10 @@ static hipError_t launch_rows(const uint8_t* A, const float* As, const uint8_t* 
 // the one the other schedules run (acc = fma(p, fl32(sa * sb), acc), groups ascending), so the bits are the
 // same.
 constexpr int WIDE_DEPTH = 6;                 // weight groups in flight per wave
+// weight groups refilled together once consumed: measured against a refill per group on the gate/up projection,
+// 24.3 -> 23.2 us at one row and 26.3 -> 25.3 at 32 rows (batches of 2 the same, of 6 slower at 32 rows)
+constexpr int WIDE_BATCH = 3;
+static_assert(WIDE_DEPTH % WIDE_BATCH == 0, "refill batches tile the prefetch ring");
 constexpr int WIDE_A_MAX = 131072;            // activation bytes in LDS: 16 RT rows x contraction
 constexpr int WIDE_SA_MAX = 2048;             // activation row scales in LDS: groups x 16 RT
 // chunk permutation of a 128-byte activation row in LDS (depends on m & 15: the 16 lanes reading one 16-byte
@@ -314,8 +318,6 @@ __global__ __launch_bounds__(D_THREADS) void gemm_decode_wide_kernel(
                 if (g < G) {
                     const v8i bfrag = (v8i){(int)lo[d][0], (int)lo[d][1], (int)lo[d][2], (int)lo[d][3],
                                             (int)hi[d][0], (int)hi[d][1], (int)hi[d][2], (int)hi[d][3]};
-                    lo[d] = __builtin_amdgcn_raw_buffer_load_b128(rb, 16 * lane, (g + WIDE_DEPTH) * 2048, 0);
-                    hi[d] = __builtin_amdgcn_raw_buffer_load_b128(rb, 16 * lane + 1024, (g + WIDE_DEPTH) * 2048, 0);
                     const float sb = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sbl), g));
                     const uint8_t* ag = a_lds + g * MR * BK;
 #pragma unroll
@@ -328,6 +330,14 @@ __global__ __launch_bounds__(D_THREADS) void gemm_decode_wide_kernel(
                         const float s = sa_lds[g * MR + rt * 16 + (int)rl] * sb;      // s = fl32(sa * sb)
 #pragma unroll
                         for (int v = 0; v < 4; ++v) acc[rt][v] = fmaf(p[v], s, acc[rt][v]);
+                    }
+                }
+                // refills in batches of WIDE_BATCH groups (6 KB of the slice in one go)
+                if ((d + 1) % WIDE_BATCH == 0) {
+#pragma unroll
+                    for (int e = d + 1 - WIDE_BATCH; e <= d; ++e) {
+                        lo[e] = __builtin_amdgcn_raw_buffer_load_b128(rb, 16 * lane, (g0 + e + WIDE_DEPTH) * 2048, 0);
+                        hi[e] = __builtin_amdgcn_raw_buffer_load_b128(rb, 16 * lane + 1024, (g0 + e + WIDE_DEPTH) * 2048, 0);
                     }
                 }
             }
@@ -368,47 +378,35 @@ static hipError_t launch_decode_wide(const uint8_t* A, const float* As, const ui
 }
 
 // ---- small-M schedule for narrow outputs over fragment-ordered weights ------------------------------------
-// For fewer slices than that (QKV, O and down projections), the slice-sharing schedule above keeps too few weight
+// For fewer slices than that (the QKV and O projections), the slice-sharing schedule above keeps too few weight
 // bytes in flight.  Here a block takes S adjacent 16-column slices (S = 2 when one slice per block would need
-// more blocks than there are CUs) and the slices' groups are dealt out to the 8 waves in rounds of 8 GPW groups
-// (group r R + 8 i + w to wave w):
-//   - each wave requests the operands of its groups for NBUF rounds at once: the fragment-ordered weights (whole
-//     lines) of every slice and one activation fragment per row tile, which serves all S slices;
+// more blocks than there are CUs) of a contraction of at most 32 groups, dealt out to the 8 waves 4 groups each
+// (group 8 i + w to wave w):
+//   - each wave requests all its operands at once: the fragment-ordered weights (whole lines) of every slice and
+//     one activation fragment per row tile, which serves all S slices;
 //   - for 17-32 rows the activation rows are loaded row-contiguous (8 whole lines per load) and moved into the
 //     fragment layout through the wave's own LDS: a 2 KB slot per row tile holds both 8-row halves, so each lane
 //     reads back only its own 32 bytes (with two slices per block, for LDS room, a 1 KB slot taken one half at a
-//     time, as in the slice-sharing schedule);
-//   - the products go to LDS, and after one barrier per round every thread runs the promotion chain of its outputs
-//     (one per slice) over the round's groups in ascending order: acc = fma(p, fl32(sa * sb), acc).
-// One round (GPW = 4, all operands in flight at once) when the contraction has at most 32 groups, else rounds of
-// 8 groups with four rounds in flight (GPW = 1, NBUF = 4).  On the 14336-long contraction at 32 rows that measured
-// 18.0 -> 17.4 us against 16-group rounds with two in flight, which beat 32-group rounds and three 16-group rounds
-// in flight; the 2 KB detour slot measured 19.6 -> 18.0 us there and O 7.4 -> 6.8 us.
-template <int RT, int S, bool MULTI>
-struct SplitCfg {
-    static constexpr int GPW = MULTI ? 1 : 4, NBUF = MULTI ? 4 : 1, PB = MULTI ? 2 : 1, GMAX = MULTI ? 128 : 32;
-    static constexpr bool ROWC = RT >= 2;
-    static constexpr bool XFULL = S == 1;                        // a 2 KB detour slot per row tile (both halves)
-    static constexpr int WPE = (RT == 1 && S == 1 && !MULTI) ? 3 : 2;   // waves per SIMD that LDS and registers allow
-};
+//     time, as in the slice-sharing schedule; the 2 KB slot measured O 7.4 -> 6.8 us at 32 rows);
+//   - the products go to LDS, and after one barrier every thread runs the promotion chain of its outputs (one per
+//     slice) over the groups in ascending order: acc = fma(p, fl32(sa * sb), acc).
+constexpr int SP_GPW = 4, SP_GMAX = D_WAVES * SP_GPW;
 
-template <int RT, int S, bool MULTI>
-__global__ __launch_bounds__(D_THREADS) __attribute__((amdgpu_waves_per_eu(SplitCfg<RT, S, MULTI>::WPE)))
+template <int RT, int S>
+__global__ __launch_bounds__(D_THREADS) __attribute__((amdgpu_waves_per_eu((RT == 1 && S == 1) ? 3 : 2)))
 void gemm_decode_split_kernel(const uint8_t* __restrict__ A, const float* __restrict__ As,
                               const uint8_t* __restrict__ Bf, const float* __restrict__ Bs,
                               uint16_t* __restrict__ Cout, int I, int J, int Kc) {
-    using C = SplitCfg<RT, S, MULTI>;
-    constexpr int GPW = C::GPW, NBUF = C::NBUF, PB = C::PB, GMAX = C::GMAX;
-    constexpr bool ROWC = C::ROWC, XFULL = C::XFULL;
-    constexpr int R = D_WAVES * GPW, MR = 16 * RT;
-    constexpr int LPR = GPW * (2 * S + 2 * RT);                  // vector loads per wave per round
-    __shared__ v4f pbuf[S][PB][R][RT][64];
-    __shared__ float sa_lds[GMAX * MR + 64];                     // [g][m] (+ the last load's overhang)
+    constexpr int GPW = SP_GPW, R = SP_GMAX, MR = 16 * RT;
+    constexpr bool ROWC = RT >= 2, XFULL = S == 1;
+    constexpr int LPR = GPW * (2 * S + 2 * RT);                  // vector loads per wave
+    __shared__ v4f pbuf[S][R][RT][64];
+    __shared__ float sa_lds[SP_GMAX * MR + 64];                  // [g][m] (+ the last load's overhang)
     __shared__ __attribute__((aligned(16))) uint8_t xbuf[ROWC ? D_WAVES * RT * (XFULL ? 2048 : 1024) : 16];
     const int t = threadIdx.x, lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int sl0 = (int)blockIdx.x * S;
-    const int G = Kc / BK, nr = (G + R - 1) / R;
+    const int G = Kc / BK;
 
     // activation row scales into LDS, before any other load (direct-to-LDS, 64 entries per load; entries of rows
     // past I hold other scales or zeros: those rows are never stored)
@@ -420,11 +418,9 @@ void gemm_decode_split_kernel(const uint8_t* __restrict__ A, const float* __rest
         }
     }
     __builtin_amdgcn_sched_barrier(0);
-    // block scales of the slices' groups (S <= 2 slices never straddle a 128-row block): lane l holds group l (sb0)
-    // and group 64 + l (sb1)
+    // block scales of the slices' groups (S <= 2 slices never straddle a 128-row block): lane l holds group l
     const rsrc_t rbs = make_rsrc(Bs + (int64_t)(sl0 >> 3) * G, G * 4);
-    const float sb0 = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rbs, lane * 4, 0, 0));
-    const float sb1 = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rbs, lane * 4, 256, 0));
+    const float sbl = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rbs, lane * 4, 0, 0));
 
     const rsrc_t rb = make_rsrc(Bf + (int64_t)sl0 * G * 2048, S * G * 2048);
     const rsrc_t ra = make_rsrc(A, I * Kc);
@@ -440,49 +436,184 @@ void gemm_decode_split_kernel(const uint8_t* __restrict__ A, const float* __rest
     const bool hi_rows = (lane & 15) >= 8;
     const int fpos0 = (hi_rows ? 1024 : 0) + rpos0, fpos1 = (hi_rows ? 1024 : 0) + rpos1;
 
-    u32x4 wf[NBUF][GPW][S][2], af[NBUF][GPW][RT][2];
-    // round r's operands (groups past the contraction: weights at an offset past the range, which reads zeros;
-    // their activation loads stay in range and are never used)
-    auto load_round = [&](int r, u32x4 (&w)[GPW][S][2], u32x4 (&a)[GPW][RT][2]) __attribute__((always_inline)) {
+    // all operands of the wave's groups (a group past the contraction: weights at an offset past the range, which
+    // reads zeros; its activation loads stay in range and are never used)
+    u32x4 w[GPW][S][2], a[GPW][RT][2];
 #pragma unroll
-        for (int i = 0; i < GPW; ++i) {
-            const int g = r * R + 8 * i + wave;
-            const int gc = g < G ? g : 0;
+    for (int i = 0; i < GPW; ++i) {
+        const int g = 8 * i + wave;
+        const int gc = g < G ? g : 0;
 #pragma unroll
-            for (int sx = 0; sx < S; ++sx) {
-                const int go = g < G ? (sx * G + g) * 2048 : S * G * 2048;
-                w[i][sx][0] = __builtin_amdgcn_raw_buffer_load_b128(rb, 16 * lane, go, 0);
-                w[i][sx][1] = __builtin_amdgcn_raw_buffer_load_b128(rb, 16 * lane + 1024, go, 0);
-            }
+        for (int sx = 0; sx < S; ++sx) {
+            const int go = g < G ? (sx * G + g) * 2048 : S * G * 2048;
+            w[i][sx][0] = __builtin_amdgcn_raw_buffer_load_b128(rb, 16 * lane, go, 0);
+            w[i][sx][1] = __builtin_amdgcn_raw_buffer_load_b128(rb, 16 * lane + 1024, go, 0);
+        }
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            a[i][rt][0] = __builtin_amdgcn_raw_buffer_load_b128(ra, va[rt], gc * BK, 0);
+            a[i][rt][1] = __builtin_amdgcn_raw_buffer_load_b128(ra, va[rt] + (ROWC ? 8 * Kc : 16), gc * BK, 0);
+        }
+    }
+
+    // (all of them issued before any product is formed: without the fence the scheduler reuses the first groups'
+    // registers for the last group's loads, which then wait for a product)
+    __builtin_amdgcn_sched_barrier(0);
+
+    // every product is formed, those of groups past the contraction (zero weights) without being stored: with the
+    // products in branches the compiler sinks their operand loads into them, which issues them late
+#pragma unroll
+    for (int i = 0; i < GPW; ++i) {
+        const int g = 8 * i + wave;
+        {
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt) {
-                a[i][rt][0] = __builtin_amdgcn_raw_buffer_load_b128(ra, va[rt], gc * BK, 0);
-                a[i][rt][1] = __builtin_amdgcn_raw_buffer_load_b128(ra, va[rt] + (ROWC ? 8 * Kc : 16), gc * BK, 0);
+                u32x4 f0 = a[i][rt][0], f1 = a[i][rt][1];
+                if (ROWC && XFULL) {
+                    uint8_t* slot = xbuf + (wave * RT + rt) * 2048;
+                    *reinterpret_cast<u32x4*>(slot + wpos) = a[i][rt][0];
+                    *reinterpret_cast<u32x4*>(slot + 1024 + wpos) = a[i][rt][1];
+                    f0 = *reinterpret_cast<const u32x4*>(slot + fpos0);
+                    f1 = *reinterpret_cast<const u32x4*>(slot + fpos1);
+                } else if (ROWC) {
+                    uint8_t* slot = xbuf + (wave * RT + rt) * 1024;
+                    u32x4 lo[2], hi[2];
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        *reinterpret_cast<u32x4*>(slot + wpos) = a[i][rt][h];
+                        lo[h] = *reinterpret_cast<const u32x4*>(slot + rpos0);
+                        hi[h] = *reinterpret_cast<const u32x4*>(slot + rpos1);
+                    }
+                    f0 = hi_rows ? lo[1] : lo[0];
+                    f1 = hi_rows ? hi[1] : hi[0];
+                }
+                const v8i afrag = (v8i){(int)f0[0], (int)f0[1], (int)f0[2], (int)f0[3],
+                                        (int)f1[0], (int)f1[1], (int)f1[2], (int)f1[3]};
+#pragma unroll
+                for (int sx = 0; sx < S; ++sx) {
+                    const v8i bfrag = (v8i){(int)w[i][sx][0][0], (int)w[i][sx][0][1], (int)w[i][sx][0][2],
+                                            (int)w[i][sx][0][3], (int)w[i][sx][1][0], (int)w[i][sx][1][1],
+                                            (int)w[i][sx][1][2], (int)w[i][sx][1][3]};
+                    const v4f p = mfma_group(bfrag, afrag);
+                    if (g < G) pbuf[sx][8 * i + wave][rt][lane] = p;
+                }
             }
         }
-    };
-#pragma unroll
-    for (int k = 0; k < NBUF; ++k) load_round(k, wf[k], af[k]);
+    }
+    // the row-scale loads came first, so with at most this wave's operand loads outstanding they are in LDS (all
+    // were consumed above anyway); this wave's products are in LDS; then every wave is here
+    __builtin_amdgcn_s_waitcnt((LPR & 15) | ((LPR >> 4) << 14) | (7 << 4));
+    __builtin_amdgcn_s_barrier();
 
     // promotion ownership: thread t < 16 MR holds, in each slice, element t & 3 of lane (t >> 2) & 63 of row tile
     // t >> 8: output row (t >> 8) 16 + ((t >> 2) & 15), column 4 ((t >> 6) & 3) + (t & 3)
     const int ln = (t >> 2) & 63, m = (t >> 8) * 16 + (ln & 15);
-    float acc[S];
+    if (t < 16 * MR) {
+        float acc[S];
 #pragma unroll
-    for (int sx = 0; sx < S; ++sx) acc[sx] = 0.0f;
-    auto round = [&](int r, u32x4 (&w)[GPW][S][2], u32x4 (&a)[GPW][RT][2]) __attribute__((always_inline)) {
-        const int pb = PB > 1 ? (r & 1) : 0;
+        for (int sx = 0; sx < S; ++sx) acc[sx] = 0.0f;
 #pragma unroll
-        for (int i = 0; i < GPW; ++i) {
-            const int g = r * R + 8 * i + wave;
+        for (int g = 0; g < R; ++g) {
+            if (g < G) {
+                const float sb = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sbl), g));
+                const float s = sa_lds[g * MR + m] * sb;                          // s = fl32(sa * sb)
+#pragma unroll
+                for (int sx = 0; sx < S; ++sx) {
+                    const float* pf = reinterpret_cast<const float*>(&pbuf[sx][0][0][0]) + t;
+                    acc[sx] = fmaf(pf[g * RT * 256], s, acc[sx]);
+                }
+            }
+        }
+        if (m < I) {
+#pragma unroll
+            for (int sx = 0; sx < S; ++sx)
+                Cout[(int64_t)m * J + (sl0 + sx) * 16 + 4 * (ln >> 4) + (t & 3)] = (uint16_t)f32_to_bf16_rne(acc[sx]);
+        }
+    }
+}
+
+// ---- small-M schedule for long contractions over fragment-ordered weights ----------------------------------
+// For more than 32 groups (the down projection) the per-slice schedule's rounds pay for their promotion chain on
+// the critical path: after each round's barrier every wave promotes before it forms the next round's products.
+// Here a block of 16 waves takes one 16-column slice and splits the work by role:
+//   - waves 0-7 (producers) take the groups in rounds of 8, group 8 r + w to wave w, request their operands
+//     RL_NBUF rounds ahead, form the products (for 17-32 rows through the 2 KB row-contiguous detour above) and park
+//     them in LDS;
+//   - waves 8-15 (consumers) hold the row scales in LDS and run the promotion chain, one output per thread: after
+//     the barrier that closes round r they promote its 8 groups in ascending order, acc = fma(p, fl32(sa * sb),
+//     acc), while the producers form round r + 1.
+// One barrier per round for both roles; products are double-buffered, and a buffer is refilled only after the
+// consumers left it (they pass the next barrier after finishing it).  Measured on the down projection (14336-long
+// contraction) against the per-slice schedule's 8-group rounds: 17.3 -> 15.9 us at 32 rows, 16.8 -> 15.5 at 17,
+// the same at 1-16 rows.  Blocks this large fit one per CU, which is why the shorter contractions keep the
+// per-slice schedule (QKV at 32 rows measured 8.2 -> 9.0 us on it).
+constexpr int RL_THREADS = 1024, RL_NBUF = 4, RL_GMAX = 128;
+
+template <int RT>
+__global__ __launch_bounds__(RL_THREADS) void gemm_decode_roles_kernel(
+    const uint8_t* __restrict__ A, const float* __restrict__ As, const uint8_t* __restrict__ Bf,
+    const float* __restrict__ Bs, uint16_t* __restrict__ Cout, int I, int J, int Kc) {
+    constexpr int S = 1, NBUF = RL_NBUF, GMAX = RL_GMAX;
+    constexpr bool ROWC = RT >= 2, XFULL = true;
+    constexpr int R = D_WAVES, MR = 16 * RT;
+    __shared__ v4f pbuf[S][2][R][RT][64];
+    __shared__ float sa_lds[GMAX * MR + 64];                     // [g][m] (+ the last load's overhang)
+    __shared__ __attribute__((aligned(16))) uint8_t xbuf[ROWC ? D_WAVES * RT * (XFULL ? 2048 : 1024) : 16];
+    const int t = threadIdx.x, lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int sl0 = (int)blockIdx.x * S;
+    const int G = Kc / BK, nr = (G + R - 1) / R;
+
+    if (wave < D_WAVES) {
+        // ---- producer ----
+        const rsrc_t rb = make_rsrc(Bf + (int64_t)sl0 * G * 2048, S * G * 2048);
+        const rsrc_t ra = make_rsrc(A, I * Kc);
+        int va[RT];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+            va[rt] = ROWC ? (rt * 16 + (lane >> 3)) * Kc + (lane & 7) * 16
+                          : (rt * 16 + (lane & 15)) * Kc + 32 * (lane >> 4);
+        // ROWC: lane l loads row l / 8 (the second load rows 8..15), 16-byte piece l % 8; written to the wave's
+        // slot with the pieces of a row XOR-permuted by the row, read back as lane t: row t % 16, pieces 2 (t / 16),
+        // 2 (t / 16) + 1
+        const int wpos = (lane >> 3) * 128 + (((lane & 7) ^ (lane >> 3)) << 4);
+        const int r8 = lane & 7, q2 = 2 * (lane >> 4);
+        const int rpos0 = r8 * 128 + ((q2 ^ r8) << 4), rpos1 = r8 * 128 + (((q2 + 1) ^ r8) << 4);
+        const bool hi_rows = (lane & 15) >= 8;
+        const int fpos0 = (hi_rows ? 1024 : 0) + rpos0, fpos1 = (hi_rows ? 1024 : 0) + rpos1;
+
+        u32x4 wf[NBUF][S][2], af[NBUF][RT][2];
+        // round r's operands (a group past the contraction: weights at an offset past the range, which reads
+        // zeros; its activation loads stay in range and are never used)
+        auto load_round = [&](int r, u32x4 (&w)[S][2], u32x4 (&a)[RT][2]) __attribute__((always_inline)) {
+            const int g = r * R + wave;
+            const int gc = g < G ? g : 0;
+#pragma unroll
+            for (int sx = 0; sx < S; ++sx) {
+                const int go = g < G ? (sx * G + g) * 2048 : S * G * 2048;
+                w[sx][0] = __builtin_amdgcn_raw_buffer_load_b128(rb, 16 * lane, go, 0);
+                w[sx][1] = __builtin_amdgcn_raw_buffer_load_b128(rb, 16 * lane + 1024, go, 0);
+            }
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                a[rt][0] = __builtin_amdgcn_raw_buffer_load_b128(ra, va[rt], gc * BK, 0);
+                a[rt][1] = __builtin_amdgcn_raw_buffer_load_b128(ra, va[rt] + (ROWC ? 8 * Kc : 16), gc * BK, 0);
+            }
+        };
+#pragma unroll
+        for (int k = 0; k < NBUF; ++k)
+            if (k < nr) load_round(k, wf[k], af[k]);
+
+        auto round = [&](int r, u32x4 (&w)[S][2], u32x4 (&a)[RT][2]) __attribute__((always_inline)) {
+            const int g = r * R + wave;
             if (g < G) {
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt) {
-                    u32x4 f0 = a[i][rt][0], f1 = a[i][rt][1];
+                    u32x4 f0 = a[rt][0], f1 = a[rt][1];
                     if (ROWC && XFULL) {
                         uint8_t* slot = xbuf + (wave * RT + rt) * 2048;
-                        *reinterpret_cast<u32x4*>(slot + wpos) = a[i][rt][0];
-                        *reinterpret_cast<u32x4*>(slot + 1024 + wpos) = a[i][rt][1];
+                        *reinterpret_cast<u32x4*>(slot + wpos) = a[rt][0];
+                        *reinterpret_cast<u32x4*>(slot + 1024 + wpos) = a[rt][1];
                         f0 = *reinterpret_cast<const u32x4*>(slot + fpos0);
                         f1 = *reinterpret_cast<const u32x4*>(slot + fpos1);
                     } else if (ROWC) {
@@ -490,7 +621,7 @@ void gemm_decode_split_kernel(const uint8_t* __restrict__ A, const float* __rest
                         u32x4 lo[2], hi[2];
 #pragma unroll
                         for (int h = 0; h < 2; ++h) {
-                            *reinterpret_cast<u32x4*>(slot + wpos) = a[i][rt][h];
+                            *reinterpret_cast<u32x4*>(slot + wpos) = a[rt][h];
                             lo[h] = *reinterpret_cast<const u32x4*>(slot + rpos0);
                             hi[h] = *reinterpret_cast<const u32x4*>(slot + rpos1);
                         }
@@ -501,74 +632,99 @@ void gemm_decode_split_kernel(const uint8_t* __restrict__ A, const float* __rest
                                             (int)f1[0], (int)f1[1], (int)f1[2], (int)f1[3]};
 #pragma unroll
                     for (int sx = 0; sx < S; ++sx) {
-                        const v8i bfrag = (v8i){(int)w[i][sx][0][0], (int)w[i][sx][0][1], (int)w[i][sx][0][2],
-                                                (int)w[i][sx][0][3], (int)w[i][sx][1][0], (int)w[i][sx][1][1],
-                                                (int)w[i][sx][1][2], (int)w[i][sx][1][3]};
-                        pbuf[sx][pb][8 * i + wave][rt][lane] = mfma_group(bfrag, afrag);
+                        const v8i bfrag = (v8i){(int)w[sx][0][0], (int)w[sx][0][1], (int)w[sx][0][2],
+                                                (int)w[sx][0][3], (int)w[sx][1][0], (int)w[sx][1][1],
+                                                (int)w[sx][1][2], (int)w[sx][1][3]};
+                        pbuf[sx][r & 1][wave][rt][lane] = mfma_group(bfrag, afrag);
                     }
                 }
             }
+            if (r + NBUF < nr) load_round(r + NBUF, w, a);
+            // this wave's products are in LDS, then every wave is here (the consumers finished round r - 1,
+            // so the buffer round r + 1 will fill is free)
+            __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+            __builtin_amdgcn_s_barrier();
+        };
+        for (int r = 0; r < nr; r += NBUF) {
+#pragma unroll
+            for (int k = 0; k < NBUF; ++k)
+                if (r + k < nr) round(r + k, wf[k], af[k]);
         }
-        if (MULTI && r + NBUF < nr) load_round(r + NBUF, w, a);
-        // the row-scale loads came first, so with at most NBUF rounds' loads outstanding they are in LDS; this
-        // wave's products are in LDS; then every wave is here
-        __builtin_amdgcn_s_waitcnt((NBUF * LPR & 15) | ((NBUF * LPR >> 4) << 14) | (7 << 4));
-        __builtin_amdgcn_s_barrier();
-        if (t < 16 * MR) {
-            const float sbr = r * R < 64 ? sb0 : sb1;             // R divides 64: a round lies in one half
+    } else {
+        // ---- consumer ----
+        const int tc = t - 64 * D_WAVES, cw = wave - D_WAVES;
+        // activation row scales into LDS (direct-to-LDS, 64 entries per load; entries of rows past I hold other
+        // scales or zeros: those rows are never stored), block scales of the slices' groups (S <= 2 slices never
+        // straddle a 128-row block): lane l holds group l (sb0) and group 64 + l (sb1)
+        const rsrc_t rsa = make_rsrc(As, G * I * 4);
+        for (int e0 = cw * 64; e0 < G * MR; e0 += 64 * D_WAVES) {
+            const int e = e0 + lane, g = e / MR, m = e % MR;
+            JETFP8_DEC_LOAD_LDS(rsa, (lds_void*)(sa_lds + e0), 4, (g * I + m) * 4, 0);
+        }
+        const rsrc_t rbs = make_rsrc(Bs + (int64_t)(sl0 >> 3) * G, G * 4);
+        const float sb0 = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rbs, lane * 4, 0, 0));
+        const float sb1 = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rbs, lane * 4, 256, 0));
+        __builtin_amdgcn_s_waitcnt(0);
+        // output ownership: consumer thread tc < 16 MR holds, in each slice, element tc & 3 of lane (tc >> 2) & 63
+        // of row tile tc >> 8: output row (tc >> 8) 16 + ((tc >> 2) & 15), column 4 ((tc >> 6) & 3) + (tc & 3)
+        const int ln = (tc >> 2) & 63, m = (tc >> 8) * 16 + (ln & 15);
+        float acc[S];
 #pragma unroll
-            for (int ig = 0; ig < R; ++ig) {
-                const int g = r * R + ig;
-                if (g < G) {
-                    const float sb = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sbr), g & 63));
-                    const float s = sa_lds[g * MR + m] * sb;                      // s = fl32(sa * sb)
+        for (int sx = 0; sx < S; ++sx) acc[sx] = 0.0f;
+        for (int r = 0; r < nr; ++r) {
+            __builtin_amdgcn_s_barrier();
+            if (tc < 16 * MR) {
+                const float sbr = r * R < 64 ? sb0 : sb1;         // R divides 64: a round lies in one half
 #pragma unroll
-                    for (int sx = 0; sx < S; ++sx) {
-                        const float* pf = reinterpret_cast<const float*>(&pbuf[sx][pb][0][0][0]) + t;
-                        acc[sx] = fmaf(pf[ig * RT * 256], s, acc[sx]);
+                for (int ig = 0; ig < R; ++ig) {
+                    const int g = r * R + ig;
+                    if (g < G) {
+                        const float sb = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sbr), g & 63));
+                        const float s = sa_lds[g * MR + m] * sb;                  // s = fl32(sa * sb)
+#pragma unroll
+                        for (int sx = 0; sx < S; ++sx) {
+                            const float* pf = reinterpret_cast<const float*>(&pbuf[sx][r & 1][0][0][0]) + tc;
+                            acc[sx] = fmaf(pf[ig * RT * 256], s, acc[sx]);
+                        }
                     }
                 }
             }
+            // this round's product reads are done before the next barrier
+            __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
         }
-    };
-    for (int r = 0; r < nr; r += NBUF) {
+        if (tc < 16 * MR && m < I) {
 #pragma unroll
-        for (int k = 0; k < NBUF; ++k)
-            if (r + k < nr) round(r + k, wf[k], af[k]);
-    }
-    if (t < 16 * MR && m < I) {
-#pragma unroll
-        for (int sx = 0; sx < S; ++sx)
-            Cout[(int64_t)m * J + (sl0 + sx) * 16 + 4 * (ln >> 4) + (t & 3)] = (uint16_t)f32_to_bf16_rne(acc[sx]);
+            for (int sx = 0; sx < S; ++sx)
+                Cout[(int64_t)m * J + (sl0 + sx) * 16 + 4 * (ln >> 4) + (tc & 3)] = (uint16_t)f32_to_bf16_rne(acc[sx]);
+        }
     }
 }
 
-// Whether a fragment-ordered forward GEMM can take the per-slice schedule: at most 32 rows and 128 groups.
+// Whether a fragment-ordered forward GEMM can take the per-slice schedules: at most 32 rows and 128 groups.
 // Measured at 32 rows on the Llama-3-8B projections (against the slice-sharing schedule, bitwise equal): QKV
 // 12.6 -> 10.4 us (two slices per block), O 9.0 -> 8.1, down 23.5 -> 20.2; at one row QKV 9.9 -> 8.1, O 6.7 ->
 // 5.9, down 14.9 -> 12.2.
-static bool decode_split_fits(int64_t M, int64_t K) { return M <= 32 && K / BK <= 128; }
+static bool decode_split_fits(int64_t M, int64_t K) { return M <= 32 && K / BK <= RL_GMAX; }
 
 template <int RT>
 static hipError_t launch_decode_split(const uint8_t* A, const float* As, const uint8_t* Bf, const float* Bs,
                                       uint16_t* C, int64_t M, int64_t N, int64_t K, int cus, hipStream_t st) {
     const int G = (int)(K / BK), slices = (int)(N / 16);
-    const dim3 block(D_THREADS);
     const int i = (int)M, j = (int)N, kc = (int)K;
-    if (G > 32) {
-        hipLaunchKernelGGL((gemm_decode_split_kernel<RT, 1, true>), dim3((unsigned)slices), block, 0, st, A, As, Bf,
+    if (G > SP_GMAX) {
+        hipLaunchKernelGGL((gemm_decode_roles_kernel<RT>), dim3((unsigned)slices), dim3(RL_THREADS), 0, st, A, As, Bf,
                            Bs, C, i, j, kc);
         return hipGetLastError();
     }
     if constexpr (RT == 2) {
         if (slices > cus) {                 // slices is a multiple of 8 (N % 128 == 0)
-            hipLaunchKernelGGL((gemm_decode_split_kernel<RT, 2, false>), dim3((unsigned)(slices / 2)), block, 0, st,
+            hipLaunchKernelGGL((gemm_decode_split_kernel<RT, 2>), dim3((unsigned)(slices / 2)), dim3(D_THREADS), 0, st,
                                A, As, Bf, Bs, C, i, j, kc);
             return hipGetLastError();
         }
     }
-    hipLaunchKernelGGL((gemm_decode_split_kernel<RT, 1, false>), dim3((unsigned)slices), block, 0, st, A, As, Bf, Bs,
-                       C, i, j, kc);
+    hipLaunchKernelGGL((gemm_decode_split_kernel<RT, 1>), dim3((unsigned)slices), dim3(D_THREADS), 0, st, A, As, Bf,
+                       Bs, C, i, j, kc);
     return hipGetLastError();
 }
 

@@ -141,16 +141,17 @@ def test_wide_schedule_equals_row_major(jf, orc, M):
     (17, 4096, 4096),     # 32-row tile (row-contiguous activation loads), one slice per block
     (32, 6144, 4096),     # more slices than CUs, 32-row tile: two slices per block
     (29, 2048, 640),      # 5 groups: three waves of the round idle
-    (32, 4096, 14336),    # down projection: 14 rounds of 8 groups, four in flight
-    (5, 1024, 4736),      # 37 groups: a ragged last round (5 groups)
-    (32, 128, 16384),     # 128 groups, the most the per-slice schedule takes; 8 slices
+    (32, 4096, 14336),    # down projection: producer and consumer waves, 14 rounds of 8 groups
+    (5, 1024, 4736),      # 37 groups (producers and consumers): a ragged last round (5 groups)
+    (32, 128, 16384),     # 128 groups, the most the per-slice schedules take; 8 slices
     (32, 256, 16512),     # 129 groups: back on the slice-sharing schedule
 ])
 def test_per_slice_schedule_equals_row_major(jf, orc, M, N, K):
     """Forward GEMMs with fewer 16-column slices than the wide schedule needs (QKV, O, down shapes) run the
-    per-slice small-M schedule over fragment-ordered weights (a block per one or two slices, the slices' groups
-    dealt out to the waves in rounds, products promoted after one barrier per round): bitwise equal to the
-    row-major weights on the slice-sharing schedule, and the first and last column blocks against the oracle."""
+    per-slice small-M schedules over fragment-ordered weights (up to 32 groups: a block per one or two slices, the
+    groups dealt out to the waves, products promoted after one barrier; longer contractions: producer waves form
+    rounds of 8 group products while consumer waves promote the round before): bitwise equal to the row-major
+    weights on the slice-sharing schedule, and the first and last column blocks against the oracle."""
     import torch
     wb = _w(N, K, 21 + M + N)
     w = bits_to_dev(wb)
