@@ -69,8 +69,8 @@ def parse():
 
 
 CSRC = os.path.join(ROOT, "fp8_precision_rl_amd", "csrc")
-GEMM_SOURCES = [os.path.join(CSRC, f) for f in ("jetfp8_gemm.hip", "jetfp8_mfma.h")]
-DECODE_SOURCES = [os.path.join(CSRC, f) for f in ("jetfp8_decode.hip", "jetfp8_mfma.h")]
+GEMM_SOURCES = [os.path.join(CSRC, f) for f in ("jetfp8_gemm.hip", "jetfp8_mfma.h", "jetfp8_common.h")]
+DECODE_SOURCES = [os.path.join(CSRC, f) for f in ("jetfp8_decode.hip", "jetfp8_mfma.h", "jetfp8_common.h")]
 
 
 def source_digest(paths=GEMM_SOURCES) -> str:
