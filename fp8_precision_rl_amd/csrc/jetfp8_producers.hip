@@ -64,6 +64,15 @@ __device__ __forceinline__ uint32_t f64_to_f32_odd_bits(double v) {
 
 __device__ __forceinline__ uint32_t f32_bits_to_bf16_rne(uint32_t u) { return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16; }
 
+// Two fp32 values rounded to bf16, nearest even, packed low / high: one V_CVT_PK_BF16_F32.  It equals
+// f32_bits_to_bf16_rne on every finite fp32 pattern (all 2^32 - 2^24 of them compared on gfx950, with the
+// library's denormal mode).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16x2_rne(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
+}
+
 // exp(-g) for the SwiGLU fast path: 2^t with t = -g log2(e) split as t_hi + t_lo, where t_hi is the fp32
 // product and t_lo its rounding error (exact by fma) plus the low part of log2(e); then
 // 2^t = 2^t_hi * (1 + t_lo ln 2 + O(t_lo^2)), |t_lo| <= 2^-17.  Relative error: that of the hardware exp2
@@ -92,9 +101,9 @@ __device__ __noinline__ uint32_t swiglu_bf16_exact(float g, float u) {
     return f32_bits_to_bf16_rne(b);
 }
 
-// bf16 bits of silu(g) * u from the fast fp32 evaluation, and whether that value must instead be taken from
-// swiglu_bf16_exact (the fast one is then not used).
-__device__ __forceinline__ uint32_t swiglu_bf16_fast(float g, float u, bool& exact) {
+// silu(g) * u from the fast fp32 evaluation (rounded to bf16 by the caller), and whether the bf16 value must
+// instead be taken from swiglu_bf16_exact (the fast one is then not used).
+__device__ __forceinline__ float swiglu_fast(float g, float u, bool& exact) {
     const float sil = g * __builtin_amdgcn_rcpf(1.0f + exp_neg(g));
     const float h = sil * u;
     const uint32_t hb = __float_as_uint(h) & 0x7FFFFFFFu;
@@ -105,7 +114,7 @@ __device__ __forceinline__ uint32_t swiglu_bf16_fast(float g, float u, bool& exa
     // it is g / 2, exact to far below that), so the fast h is within 4.3 ulps of silu(g) u: a quarter of the
     // screened window.
     exact = (g < -87.0f) | (hb - 0x03800000u >= 0x7F000000u - 0x03800000u) | (((hb - 0x7FF0u) & 0xFFFFu) <= 0x20u);
-    return f32_bits_to_bf16_rne(__float_as_uint(h));
+    return h;
 }
 
 }  // namespace
@@ -167,7 +176,7 @@ __global__ __launch_bounds__(RN_WAVES * 64) __attribute__((amdgpu_waves_per_eu(N
             for (int k = 0; k < 4; ++k) {
                 const float y0 = (elem_of(v[c], 2 * k) * r) * elem_of(wv, 2 * k);
                 const float y1 = (elem_of(v[c], 2 * k + 1) * r) * elem_of(wv, 2 * k + 1);
-                hw[k] = f32_to_bf16_rne(y0) | (f32_to_bf16_rne(y1) << 16);
+                hw[k] = bf16x2_rne(y0, y1);
             }
             const uint4 yv = make_uint4(hw[0], hw[1], hw[2], hw[3]);
             float scale;
@@ -217,22 +226,26 @@ __global__ __launch_bounds__(SG_WAVES * 64) void swiglu_quant_kernel(const uint1
 #pragma unroll
     for (int p = 0; p < SG_PASSES; ++p) {
         const int64_t row = r0 + p * SG_WAVES + wave;
-        // fast values of the lane's 8 elements without branches, then one rarely taken branch that replaces the
-        // flagged ones by the exact path
-        uint32_t hb[8], need = 0;
+        // fast values of the lane's 8 elements without branches, rounded to bf16 in pairs, then one rarely taken
+        // branch that replaces the flagged ones by the exact path
+        float hf[8];
+        uint32_t need = 0;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             bool ex;
-            hb[i] = swiglu_bf16_fast(elem_of(gv[p], i), elem_of(uv[p], i), ex);
+            hf[i] = swiglu_fast(elem_of(gv[p], i), elem_of(uv[p], i), ex);
             need |= (uint32_t)ex << i;
-        }
-        if (__builtin_expect(need != 0, 0)) {
-            for (int i = 0; i < 8; ++i)
-                if ((need >> i) & 1u) hb[i] = swiglu_bf16_exact(elem_of(gv[p], i), elem_of(uv[p], i));
         }
         uint32_t hw[4];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) hw[k] = hb[2 * k] | (hb[2 * k + 1] << 16);
+        for (int k = 0; k < 4; ++k) hw[k] = bf16x2_rne(hf[2 * k], hf[2 * k + 1]);
+        if (__builtin_expect(need != 0, 0)) {
+            for (int i = 0; i < 8; ++i)
+                if ((need >> i) & 1u) {
+                    const uint32_t e = swiglu_bf16_exact(elem_of(gv[p], i), elem_of(uv[p], i));
+                    hw[i >> 1] = (i & 1) ? ((hw[i >> 1] & 0xFFFFu) | (e << 16)) : ((hw[i >> 1] & 0xFFFF0000u) | e);
+                }
+        }
         const uint4 hv = make_uint4(hw[0], hw[1], hw[2], hw[3]);
         float scale;
         const uint2 codes = quantize_lane8(hv, scale);
