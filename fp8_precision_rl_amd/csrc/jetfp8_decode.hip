@@ -700,22 +700,31 @@ __global__ __launch_bounds__(RL_THREADS) void gemm_decode_roles_kernel(
     }
 }
 
-// Whether a fragment-ordered forward GEMM can take the per-slice schedules: at most 32 rows and 128 groups.
-// Measured at 32 rows on the Llama-3-8B projections (against the slice-sharing schedule, bitwise equal): QKV
-// 12.6 -> 10.4 us (two slices per block), O 9.0 -> 8.1, down 23.5 -> 20.2; at one row QKV 9.9 -> 8.1, O 6.7 ->
-// 5.9, down 14.9 -> 12.2.
-static bool decode_split_fits(int64_t M, int64_t K) { return M <= 32 && K / BK <= RL_GMAX; }
+// Which small-M schedule a fragment-ordered forward GEMM of at most 32 rows takes besides the wide one:
+//   - at most 32 groups: the one-round per-slice kernel (with fewer than 4 slices per CU; from 4 per CU on, the wide
+//     kernel fits, since the activations of 32 groups fit in LDS);
+//   - 33-128 groups: the role-split kernel, when its one-block-per-slice rounds stay short: at most one slice per
+//     CU, or two for contractions of at least 64 groups; otherwise the slice-sharing kernel, whose persistent blocks
+//     stream on across slices.
+// Measured against the slice-sharing kernel at 32 rows (fragment-ordered weights, one process): QKV 12.6 -> 8.5 us,
+// O 9.0 -> 6.6, down (14336 x 4096) 23.5 -> 15.4, 16384 x 8192 43.3 -> 39.5; but 5120 x 13824 (3.4 slices per CU,
+// 40 groups) 24.7 -> 28.6 and 5120 x 27648 45.9 -> 61.8 on the role-split kernel, which is why those keep the
+// slice-sharing kernel.
+enum class SmallM { kWide, kSplit, kRoles, kShared };
+static SmallM decode_schedule(int64_t M, int64_t N, int64_t K, int cus) {
+    const int64_t G = K / BK, slices = N / 16;
+    if (M > 32) return SmallM::kShared;
+    if (decode_wide_fits(M, N, K, cus)) return SmallM::kWide;
+    if (G <= SP_GMAX) return SmallM::kSplit;
+    if (G <= RL_GMAX && (slices <= cus || (slices <= 2 * (int64_t)cus && G >= 64))) return SmallM::kRoles;
+    return SmallM::kShared;
+}
 
 template <int RT>
 static hipError_t launch_decode_split(const uint8_t* A, const float* As, const uint8_t* Bf, const float* Bs,
                                       uint16_t* C, int64_t M, int64_t N, int64_t K, int cus, hipStream_t st) {
-    const int G = (int)(K / BK), slices = (int)(N / 16);
+    const int slices = (int)(N / 16);
     const int i = (int)M, j = (int)N, kc = (int)K;
-    if (G > SP_GMAX) {
-        hipLaunchKernelGGL((gemm_decode_roles_kernel<RT>), dim3((unsigned)slices), dim3(RL_THREADS), 0, st, A, As, Bf,
-                           Bs, C, i, j, kc);
-        return hipGetLastError();
-    }
     if constexpr (RT == 2) {
         if (slices > cus) {                 // slices is a multiple of 8 (N % 128 == 0)
             hipLaunchKernelGGL((gemm_decode_split_kernel<RT, 2>), dim3((unsigned)(slices / 2)), dim3(D_THREADS), 0, st,
@@ -725,6 +734,14 @@ static hipError_t launch_decode_split(const uint8_t* A, const float* As, const u
     }
     hipLaunchKernelGGL((gemm_decode_split_kernel<RT, 1>), dim3((unsigned)slices), dim3(D_THREADS), 0, st, A, As, Bf,
                        Bs, C, i, j, kc);
+    return hipGetLastError();
+}
+
+template <int RT>
+static hipError_t launch_decode_roles(const uint8_t* A, const float* As, const uint8_t* Bf, const float* Bs,
+                                      uint16_t* C, int64_t M, int64_t N, int64_t K, hipStream_t st) {
+    hipLaunchKernelGGL((gemm_decode_roles_kernel<RT>), dim3((unsigned)(N / 16)), dim3(RL_THREADS), 0, st, A, As, Bf,
+                       Bs, C, (int)M, (int)N, (int)K);
     return hipGetLastError();
 }
 
@@ -742,12 +759,19 @@ bool gemm_fwd_frag_fits(int64_t M, int64_t K) { return decode_rows_fit(M, K); }
 hipError_t launch_gemm_fwd_frag(const uint8_t* xq, const float* xs, const uint8_t* wqf, const float* ws, uint16_t* y,
                                 int64_t M, int64_t N, int64_t K, hipStream_t st) {
     const int cus = device_cu_count();
-    if (decode_wide_fits(M, N, K, cus))
+    switch (decode_schedule(M, N, K, cus)) {
+    case SmallM::kWide:
         return M <= 16 ? launch_decode_wide<1>(xq, xs, wqf, ws, y, M, N, K, cus, st)
                        : launch_decode_wide<2>(xq, xs, wqf, ws, y, M, N, K, cus, st);
-    if (decode_split_fits(M, K))
+    case SmallM::kSplit:
         return M <= 16 ? launch_decode_split<1>(xq, xs, wqf, ws, y, M, N, K, cus, st)
                        : launch_decode_split<2>(xq, xs, wqf, ws, y, M, N, K, cus, st);
+    case SmallM::kRoles:
+        return M <= 16 ? launch_decode_roles<1>(xq, xs, wqf, ws, y, M, N, K, st)
+                       : launch_decode_roles<2>(xq, xs, wqf, ws, y, M, N, K, st);
+    case SmallM::kShared:
+        break;
+    }
     return launch_rows<true>(xq, xs, wqf, ws, y, M, 0, M, N, K, K / BK, 1, st);
 }
 

@@ -145,6 +145,10 @@ def test_wide_schedule_equals_row_major(jf, orc, M):
     (5, 1024, 4736),      # 37 groups (producers and consumers): a ragged last round (5 groups)
     (32, 128, 16384),     # 128 groups, the most the per-slice schedules take; 8 slices
     (32, 256, 16512),     # 129 groups: back on the slice-sharing schedule
+    (17, 6144, 8192),     # 64 groups, 1.5 slices per CU (on 256 CUs): producer and consumer waves
+    (32, 8192, 8192),     # 64 groups, 2 slices per CU: producer and consumer waves
+    (32, 8192, 5120),     # 40 groups, 2 slices per CU: the slice-sharing schedule
+    (16, 12288, 5120),    # 40 groups, 3 slices per CU, too few for the wide schedule: the slice-sharing schedule
 ])
 def test_per_slice_schedule_equals_row_major(jf, orc, M, N, K):
     """Forward GEMMs with fewer 16-column slices than the wide schedule needs (QKV, O, down shapes) run the
