@@ -356,6 +356,158 @@ __global__ __launch_bounds__(D_THREADS) void gemm_decode_wide_kernel(
     }
 }
 
+// ---- wide outputs, activations streamed through LDS in windows -------------------------------------------
+// The wide schedule above with the activations staged window by window instead of all at once, so the contraction
+// length and the row count (up to 64) are no longer bounded by LDS.  Each wave owns whole slices as above; the
+// block steps through windows of WW_WIN groups in lockstep, one barrier per window, with two window buffers in LDS:
+// after the barrier that opens window s every wave issues its share of window s + 1's direct-to-LDS loads (codes
+// and row scales), then runs window s for its slice.  The weight stream is one sequence over the wave's slices
+// (position = round * padded groups + group), refilled WIDE_BATCH groups at a time exactly as above, so a window
+// holds the same number of refill loads on every wave (past its last slice a wave refills from an empty
+// descriptor): the loads issued after a wave's window loads are exactly the window's refills, which fixes the wait
+// that makes them visible.
+constexpr int WW_WIN = WIDE_DEPTH;
+constexpr int WW_GMAX = 128;
+constexpr int WW_REFILLS = 2 * WW_WIN;              // weight loads per window and wave (lo and hi of each group)
+
+template <int RT>
+__global__ __launch_bounds__(D_THREADS) void gemm_decode_wwide_kernel(
+    const uint8_t* __restrict__ A, const float* __restrict__ As, const uint8_t* __restrict__ Bf,
+    const float* __restrict__ Bs, uint16_t* __restrict__ Cout, int I, int J, int Kc) {
+    constexpr int MR = 16 * RT;
+    constexpr int WIN_A = WW_WIN * MR * BK;                          // activation bytes per window
+    constexpr int WIN_S = WW_WIN * MR;                               // row scales per window ([g][m])
+    __shared__ __attribute__((aligned(16))) uint8_t a_lds[2][WIN_A];
+    __shared__ float sa_lds[2][WIN_S + 64];                          // (+ the last load's overhang)
+    const int t = threadIdx.x, lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int wpb = (int)(blockDim.x >> 6);
+    const int G = Kc / BK, slices = J / 16, nwin = (G + WW_WIN - 1) / WW_WIN, gpad = nwin * WW_WIN;
+    const int W = (int)gridDim.x * wpb;                              // waves in the grid
+    const int gw = wave * (int)gridDim.x + (int)blockIdx.x;         // slices gw, gw + W, ...
+    // slice rounds of the block: those of its wave 0, which has the most
+    const int nround = ((int)blockIdx.x < slices) ? (slices - (int)blockIdx.x + W - 1) / W : 0;
+    const int nstep = nround * nwin;
+    const rsrc_t ra = make_rsrc(A, I * Kc);
+    const rsrc_t rsa = make_rsrc(As, G * I * 4);
+
+    // window s's loads into buffer s & 1: WW_WIN groups x MR / 8 regions of 8 rows (lane l: row l / 8, 16-byte
+    // piece (l % 8) ^ wide_swz(row)); rows past I read zeros; groups past the contraction read other bytes that are
+    // never used.  Row scales: 64 entries [g][m] per load.
+    auto stage = [&](int st) __attribute__((always_inline)) {
+        const int v = st % nwin, q = st & 1;
+        for (int r2 = wave; r2 < WW_WIN * (MR / 8); r2 += wpb) {
+            const int gi = r2 / (MR / 8), m = (r2 % (MR / 8)) * 8 + (lane >> 3), g = v * WW_WIN + gi;
+            const int vo = m * Kc + g * BK + (((lane & 7) ^ wide_swz(m)) << 4);
+            JETFP8_DEC_LOAD_LDS(ra, (lds_void*)(&a_lds[q][0] + r2 * 1024), 16, vo, 0);
+        }
+        for (int e0 = wave * 64; e0 < WIN_S; e0 += wpb * 64) {
+            const int e = e0 + lane, gi = e / MR, m = e % MR, g = v * WW_WIN + gi;
+            JETFP8_DEC_LOAD_LDS(rsa, (lds_void*)(&sa_lds[q][0] + e0), 4, (g * I + m) * 4, 0);
+        }
+    };
+    // the weight stream: position p -> slice round p / gpad, group p % gpad
+    u32x4 lo[WW_WIN], hi[WW_WIN];
+    auto fetch = [&](int p, int d) __attribute__((always_inline)) {
+        const int r = p / gpad, g = p - r * gpad, sl = gw + r * W;
+        const bool ok = r < nround && sl < slices;
+        const rsrc_t rb = make_rsrc(Bf + (int64_t)(ok ? sl : 0) * G * 2048, ok ? G * 2048 : 0);
+        lo[d] = __builtin_amdgcn_raw_buffer_load_b128(rb, 16 * lane, g * 2048, 0);
+        hi[d] = __builtin_amdgcn_raw_buffer_load_b128(rb, 16 * lane + 1024, g * 2048, 0);
+    };
+
+    if (nstep > 0) stage(0);
+#pragma unroll
+    for (int d = 0; d < WW_WIN; ++d) fetch(d, d);
+
+    const uint32_t rl = lane & 15, cp = 2 * (lane >> 4), sw = (uint32_t)wide_swz((int)rl);
+    const int fa0 = (int)(rl * BK + ((cp ^ sw) << 4)), fa1 = (int)(rl * BK + (((cp + 1) ^ sw) << 4));
+    v4f acc[RT];
+    float sb0 = 0.0f, sb1 = 0.0f;
+    for (int st = 0; st < nstep; ++st) {
+        const int r = st / nwin, v = st - r * nwin, sl = gw + r * W;
+        const bool live = sl < slices;                               // wave-uniform
+        // this wave's loads of window st are done (only the previous window's refills came after them), then
+        // every wave's
+        __builtin_amdgcn_s_waitcnt((WW_REFILLS & 15) | ((WW_REFILLS >> 4) << 14) | (7 << 4) | (0 << 8));
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        if (st + 1 < nstep) stage(st + 1);
+        if (v == 0) {
+            // a new slice: its block scales (lane l: groups l and 64 + l), accumulators cleared
+            const rsrc_t rbs = make_rsrc(Bs + (int64_t)((live ? sl : 0) >> 3) * G, live ? G * 4 : 0);
+            sb0 = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rbs, lane * 4, 0, 0));
+            sb1 = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rbs, lane * 4, 256, 0));
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) acc[rt] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
+        }
+        const uint8_t* aw = &a_lds[st & 1][0];
+        const float* sw_ = &sa_lds[st & 1][0];
+        const int p0 = r * gpad + v * WW_WIN;
+#pragma unroll
+        for (int d = 0; d < WW_WIN; ++d) {
+            const int g = v * WW_WIN + d;
+            if (live && g < G) {
+                const v8i bfrag = (v8i){(int)lo[d][0], (int)lo[d][1], (int)lo[d][2], (int)lo[d][3],
+                                        (int)hi[d][0], (int)hi[d][1], (int)hi[d][2], (int)hi[d][3]};
+                const float sbg = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(g < 64 ? sb0 : sb1), g & 63));
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt) {
+                    const uint8_t* ag = aw + (d * MR + rt * 16) * BK;
+                    const uint4 f0 = *reinterpret_cast<const uint4*>(ag + fa0);
+                    const uint4 f1 = *reinterpret_cast<const uint4*>(ag + fa1);
+                    const v8i afrag = (v8i){(int)f0.x, (int)f0.y, (int)f0.z, (int)f0.w,
+                                            (int)f1.x, (int)f1.y, (int)f1.z, (int)f1.w};
+                    const v4f pr = mfma_group(bfrag, afrag);
+                    const float s = sw_[d * MR + rt * 16 + (int)rl] * sbg;          // s = fl32(sa * sb)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[rt][e] = fmaf(pr[e], s, acc[rt][e]);
+                }
+            }
+            if ((d + 1) % WIDE_BATCH == 0) {
+#pragma unroll
+                for (int e = d + 1 - WIDE_BATCH; e <= d; ++e) fetch(p0 + e + WW_WIN, e);
+            }
+        }
+        if (live && v == nwin - 1) {
+            // lane l: output row rt * 16 + (l & 15), columns 16 sl + 4 (l >> 4) .. + 3
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                const int m = rt * 16 + (int)rl;
+                if (m < I) {
+                    uint2 w2;
+                    w2.x = f32_to_bf16_rne(acc[rt][0]) | (f32_to_bf16_rne(acc[rt][1]) << 16);
+                    w2.y = f32_to_bf16_rne(acc[rt][2]) | (f32_to_bf16_rne(acc[rt][3]) << 16);
+                    *reinterpret_cast<uint2*>(&Cout[(int64_t)m * J + sl * 16 + 4 * (lane >> 4)]) = w2;
+                }
+            }
+        }
+        // this wave's reads of the window are done before the next barrier
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    }
+    // every load has landed before the block exits
+    __builtin_amdgcn_s_waitcnt(0);
+}
+
+// Measured against the slice-sharing kernel (fragment-ordered weights, one process): Llama-3-8B gate/up at 48 and 64
+// rows 69.9 -> 30.2 and 75.7 -> 31.4 us; 5120 x 55296 at 32 and 64 rows 86.0 -> 56.7 and 188.9 -> 65.1; 16384 x 16384
+// (128 groups) at one row 54.6 -> 49.4.
+static bool decode_wwide_fits(int64_t M, int64_t N, int64_t K, int cus) {
+    return M <= 64 && K / BK <= WW_GMAX && N / 16 >= 4 * (int64_t)cus;
+}
+
+template <int RT>
+static hipError_t launch_decode_wwide(const uint8_t* A, const float* As, const uint8_t* Bf, const float* Bs,
+                                      uint16_t* C, int64_t M, int64_t N, int64_t K, int cus, hipStream_t st) {
+    const int64_t slices = N / 16;
+    const int wpb = (int)std::min<int64_t>(D_WAVES, (slices + cus - 1) / cus);
+    const int grid = (int)std::min<int64_t>(cus, (slices + wpb - 1) / wpb);
+    hipLaunchKernelGGL((gemm_decode_wwide_kernel<RT>), dim3((unsigned)grid), dim3(64 * wpb), 0, st, A, As, Bf, Bs, C,
+                       (int)M, (int)N, (int)K);
+    return hipGetLastError();
+}
+
 // Whether a fragment-ordered forward GEMM takes the wide schedule: at most 32 rows, the activations fit in LDS,
 // at most 64 groups, and at least 4 slices per CU.  Measured on the Llama-3-8B gate/up projection (1792 slices):
 // 37.7 -> 26.4 us at 32 rows, 30.5 -> 24.8 at 16, 27.5 -> 24.4 at 1; with 1-1.5 slices per CU (O, QKV) it is
@@ -700,7 +852,9 @@ __global__ __launch_bounds__(RL_THREADS) void gemm_decode_roles_kernel(
     }
 }
 
-// Which small-M schedule a fragment-ordered forward GEMM of at most 32 rows takes besides the wide one:
+// Which small-M schedule a fragment-ordered forward GEMM takes: the wide one when its activations fit in LDS, else
+// the windowed wide one for at least 4 slices per CU (up to 64 rows and 128 groups; where both fit the first measured
+// faster: gate/up at 32 rows 25.5 against 28.0 us, its waves run unsynchronized), else for at most 32 rows:
 //   - at most 32 groups: the one-round per-slice kernel (with fewer than 4 slices per CU; from 4 per CU on, the wide
 //     kernel fits, since the activations of 32 groups fit in LDS);
 //   - 33-128 groups: the role-split kernel, when its one-block-per-slice rounds stay short: at most one slice per
@@ -708,13 +862,14 @@ __global__ __launch_bounds__(RL_THREADS) void gemm_decode_roles_kernel(
 //     stream on across slices.
 // Measured against the slice-sharing kernel at 32 rows (fragment-ordered weights, one process): QKV 12.6 -> 8.5 us,
 // O 9.0 -> 6.6, down (14336 x 4096) 23.5 -> 15.4, 16384 x 8192 43.3 -> 39.5; but 5120 x 13824 (3.4 slices per CU,
-// 40 groups) 24.7 -> 28.6 and 5120 x 27648 45.9 -> 61.8 on the role-split kernel, which is why those keep the
-// slice-sharing kernel.
-enum class SmallM { kWide, kSplit, kRoles, kShared };
+// 40 groups) 24.7 -> 28.6 and 5120 x 27648 45.9 -> 61.8 on the role-split kernel, which is why those do not take it
+// (5120 x 13824 keeps the slice-sharing kernel; 5120 x 27648 has enough slices for the windowed wide one).
+enum class SmallM { kWide, kWWide, kSplit, kRoles, kShared };
 static SmallM decode_schedule(int64_t M, int64_t N, int64_t K, int cus) {
     const int64_t G = K / BK, slices = N / 16;
-    if (M > 32) return SmallM::kShared;
     if (decode_wide_fits(M, N, K, cus)) return SmallM::kWide;
+    if (decode_wwide_fits(M, N, K, cus)) return SmallM::kWWide;
+    if (M > 32) return SmallM::kShared;
     if (G <= SP_GMAX) return SmallM::kSplit;
     if (G <= RL_GMAX && (slices <= cus || (slices <= 2 * (int64_t)cus && G >= 64))) return SmallM::kRoles;
     return SmallM::kShared;
@@ -763,6 +918,10 @@ hipError_t launch_gemm_fwd_frag(const uint8_t* xq, const float* xs, const uint8_
     case SmallM::kWide:
         return M <= 16 ? launch_decode_wide<1>(xq, xs, wqf, ws, y, M, N, K, cus, st)
                        : launch_decode_wide<2>(xq, xs, wqf, ws, y, M, N, K, cus, st);
+    case SmallM::kWWide:
+        return M <= 16 ? launch_decode_wwide<1>(xq, xs, wqf, ws, y, M, N, K, cus, st)
+                       : M <= 32 ? launch_decode_wwide<2>(xq, xs, wqf, ws, y, M, N, K, cus, st)
+                                 : launch_decode_wwide<4>(xq, xs, wqf, ws, y, M, N, K, cus, st);
     case SmallM::kSplit:
         return M <= 16 ? launch_decode_split<1>(xq, xs, wqf, ws, y, M, N, K, cus, st)
                        : launch_decode_split<2>(xq, xs, wqf, ws, y, M, N, K, cus, st);

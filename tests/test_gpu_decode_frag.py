@@ -8,8 +8,8 @@ weights in 128x128 blocks), chosen so the small-M GEMM kernel reads whole 128-by
   * jetfp8_gemm_fwd_frag is bitwise equal to jetfp8_gemm_fwd on the row-major codes for every small-M row-tile
     count (1, 16, 17, 32, 33, 64 rows), on a ragged contraction (11 groups) with more column slices than blocks and
     on a Llama-3-8B-shaped linear, and matches the oracle;
-  * the three small-M schedules for fragment-ordered weights (wide outputs: a wave per slice; fewer slices: a
-    block per one or two slices with the groups dealt out in rounds; more than 32 rows or 128 groups: the
+  * the small-M schedules for fragment-ordered weights (wide outputs: a wave per slice, the activations in LDS at
+    once or in windows; fewer slices: a block per one or two slices, or producer and consumer waves; otherwise the
     slice-sharing schedule) each equal the row-major call bitwise and the oracle on sampled column blocks;
   * more than 64 rows is a shape error.
 """
@@ -173,4 +173,36 @@ def test_per_slice_schedule_equals_row_major(jf, orc, M, N, K):
     oxq, oxs = orc.quantize_rows(xb)
     owq, ows = orc.quantize_blocks(wb[cols])
     check_gemm_parity(f"per-slice decode {M}x{N}x{K} first/last column blocks", yfb[:, cols],
+                      orc.gemm_fwd(oxq, oxs, owq, ows, mode=orc.MFMA), orc.gemm_fwd(oxq, oxs, owq, ows, mode=orc.EXACT))
+
+
+@pytest.mark.parametrize("M,N,K", [
+    (48, 16384, 4096),    # 48 rows (4 row tiles), at least 4 slices per CU: activation windows
+    (64, 16384, 1152),    # 64 rows, 9 groups: a ragged last window (6 + 3)
+    (32, 16384, 5120),    # 32 rows whose activations (160 KB) do not fit in LDS at once
+    (3, 16384, 8320),     # 65 groups, too many for the unwindowed wide schedule, at 3 rows
+    (33, 16384, 2048),    # 33 rows: 4 row tiles, rows 33-63 empty
+])
+def test_windowed_wide_schedule_equals_row_major(jf, orc, M, N, K):
+    """Wide outputs whose activations do not fit in LDS at once (more than 32 rows, or a long contraction) run the
+    wide small-M schedule with the activations streamed through LDS in windows of 6 groups: bitwise equal to the
+    row-major weights on the slice-sharing or large-tile schedules, and the first and last column blocks against
+    the oracle."""
+    import torch
+    wb = _w(N, K, 31 + M + K)
+    w = bits_to_dev(wb)
+    wq, ws = jf.quantize_blocks(w, transposed=False)
+    wqf, wsf = jf.quantize_blocks_frag(w)
+    del w
+    xb = _x(M, K, 32 + M)
+    xq, xs = jf.quantize_rows(bits_to_dev(xb))
+    y = jf.gemm_fwd(xq, xs, wq, ws)
+    yf = jf.gemm_fwd_frag(xq, xs, wqf, wsf)
+    torch.cuda.synchronize()
+    yb, yfb = dev_to_bits(y), dev_to_bits(yf)
+    assert np.array_equal(yfb, yb), (M, N, K)
+    cols = np.r_[0:128, N - 128:N]
+    oxq, oxs = orc.quantize_rows(xb)
+    owq, ows = orc.quantize_blocks(wb[cols])
+    check_gemm_parity(f"windowed wide decode {M}x{N}x{K} first/last column blocks", yfb[:, cols],
                       orc.gemm_fwd(oxq, oxs, owq, ows, mode=orc.MFMA), orc.gemm_fwd(oxq, oxs, owq, ows, mode=orc.EXACT))
