@@ -661,6 +661,15 @@ void gemm_decode_split_kernel(const uint8_t* __restrict__ A, const float* __rest
     // t >> 8: output row (t >> 8) 16 + ((t >> 2) & 15), column 4 ((t >> 6) & 3) + (t & 3)
     const int ln = (t >> 2) & 63, m = (t >> 8) * 16 + (ln & 15);
     if (t < 16 * MR) {
+        // every product and row scale of the chain read first (entries of groups past the contraction are in
+        // bounds and unused): in the guarded loop below each group's reads waited for the previous group's
+        float pv[S][R], sav[R];
+#pragma unroll
+        for (int g = 0; g < R; ++g) {
+            sav[g] = sa_lds[g * MR + m];
+#pragma unroll
+            for (int sx = 0; sx < S; ++sx) pv[sx][g] = reinterpret_cast<const float*>(&pbuf[sx][0][0][0])[g * RT * 256 + t];
+        }
         float acc[S];
 #pragma unroll
         for (int sx = 0; sx < S; ++sx) acc[sx] = 0.0f;
@@ -668,12 +677,9 @@ void gemm_decode_split_kernel(const uint8_t* __restrict__ A, const float* __rest
         for (int g = 0; g < R; ++g) {
             if (g < G) {
                 const float sb = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sbl), g));
-                const float s = sa_lds[g * MR + m] * sb;                          // s = fl32(sa * sb)
+                const float s = sav[g] * sb;                                      // s = fl32(sa * sb)
 #pragma unroll
-                for (int sx = 0; sx < S; ++sx) {
-                    const float* pf = reinterpret_cast<const float*>(&pbuf[sx][0][0][0]) + t;
-                    acc[sx] = fmaf(pf[g * RT * 256], s, acc[sx]);
-                }
+                for (int sx = 0; sx < S; ++sx) acc[sx] = fmaf(pv[sx][g], s, acc[sx]);
             }
         }
         if (m < I) {
@@ -827,17 +833,24 @@ __global__ __launch_bounds__(RL_THREADS) void gemm_decode_roles_kernel(
             __builtin_amdgcn_s_barrier();
             if (tc < 16 * MR) {
                 const float sbr = r * R < 64 ? sb0 : sb1;         // R divides 64: a round lies in one half
+                // the round's products and row scales read first (a group past the contraction is in bounds: the
+                // rounds cover at most RL_GMAX groups, a multiple of the round; its entries are unused)
+                float pv[S][R], sav[R];
+#pragma unroll
+                for (int ig = 0; ig < R; ++ig) {
+                    sav[ig] = sa_lds[(r * R + ig) * MR + m];
+#pragma unroll
+                    for (int sx = 0; sx < S; ++sx)
+                        pv[sx][ig] = reinterpret_cast<const float*>(&pbuf[sx][r & 1][0][0][0])[ig * RT * 256 + tc];
+                }
 #pragma unroll
                 for (int ig = 0; ig < R; ++ig) {
                     const int g = r * R + ig;
                     if (g < G) {
                         const float sb = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sbr), g & 63));
-                        const float s = sa_lds[g * MR + m] * sb;                  // s = fl32(sa * sb)
+                        const float s = sav[ig] * sb;                             // s = fl32(sa * sb)
 #pragma unroll
-                        for (int sx = 0; sx < S; ++sx) {
-                            const float* pf = reinterpret_cast<const float*>(&pbuf[sx][r & 1][0][0][0]) + tc;
-                            acc[sx] = fmaf(pf[ig * RT * 256], s, acc[sx]);
-                        }
+                        for (int sx = 0; sx < S; ++sx) acc[sx] = fmaf(pv[sx][ig], s, acc[sx]);
                     }
                 }
             }
