@@ -311,35 +311,47 @@ __global__ __launch_bounds__(D_THREADS) void gemm_decode_wide_kernel(
         v4f acc[RT];
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) acc[rt] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
-        for (int g0 = 0; g0 < G; g0 += WIDE_DEPTH) {
+        // one group: its product per row tile, promoted in registers
+        auto group = [&](int g, int d) __attribute__((always_inline)) {
+            const v8i bfrag = (v8i){(int)lo[d][0], (int)lo[d][1], (int)lo[d][2], (int)lo[d][3],
+                                    (int)hi[d][0], (int)hi[d][1], (int)hi[d][2], (int)hi[d][3]};
+            const float sb = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sbl), g));
+            const uint8_t* ag = a_lds + g * MR * BK;
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                const uint4 f0 = *reinterpret_cast<const uint4*>(ag + rt * 16 * BK + fa0);
+                const uint4 f1 = *reinterpret_cast<const uint4*>(ag + rt * 16 * BK + fa1);
+                const v8i afrag = (v8i){(int)f0.x, (int)f0.y, (int)f0.z, (int)f0.w,
+                                        (int)f1.x, (int)f1.y, (int)f1.z, (int)f1.w};
+                const v4f p = mfma_group(bfrag, afrag);
+                const float s = sa_lds[g * MR + rt * 16 + (int)rl] * sb;      // s = fl32(sa * sb)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) acc[rt][v] = fmaf(p[v], s, acc[rt][v]);
+            }
+        };
+        // refills in batches of WIDE_BATCH groups (6 KB of the slice in one go)
+        auto refill = [&](int g0, int d) __attribute__((always_inline)) {
+#pragma unroll
+            for (int e = d + 1 - WIDE_BATCH; e <= d; ++e) {
+                lo[e] = __builtin_amdgcn_raw_buffer_load_b128(rb, 16 * lane, (g0 + e + WIDE_DEPTH) * 2048, 0);
+                hi[e] = __builtin_amdgcn_raw_buffer_load_b128(rb, 16 * lane + 1024, (g0 + e + WIDE_DEPTH) * 2048, 0);
+            }
+        };
+        // whole steps of WIDE_DEPTH groups without a guard (so the compiler can schedule across their groups), then
+        // the guarded last step
+        int g0 = 0;
+        for (; g0 + WIDE_DEPTH <= G; g0 += WIDE_DEPTH) {
 #pragma unroll
             for (int d = 0; d < WIDE_DEPTH; ++d) {
-                const int g = g0 + d;
-                if (g < G) {
-                    const v8i bfrag = (v8i){(int)lo[d][0], (int)lo[d][1], (int)lo[d][2], (int)lo[d][3],
-                                            (int)hi[d][0], (int)hi[d][1], (int)hi[d][2], (int)hi[d][3]};
-                    const float sb = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sbl), g));
-                    const uint8_t* ag = a_lds + g * MR * BK;
+                group(g0 + d, d);
+                if ((d + 1) % WIDE_BATCH == 0) refill(g0, d);
+            }
+        }
+        if (g0 < G) {
 #pragma unroll
-                    for (int rt = 0; rt < RT; ++rt) {
-                        const uint4 f0 = *reinterpret_cast<const uint4*>(ag + rt * 16 * BK + fa0);
-                        const uint4 f1 = *reinterpret_cast<const uint4*>(ag + rt * 16 * BK + fa1);
-                        const v8i afrag = (v8i){(int)f0.x, (int)f0.y, (int)f0.z, (int)f0.w,
-                                                (int)f1.x, (int)f1.y, (int)f1.z, (int)f1.w};
-                        const v4f p = mfma_group(bfrag, afrag);
-                        const float s = sa_lds[g * MR + rt * 16 + (int)rl] * sb;      // s = fl32(sa * sb)
-#pragma unroll
-                        for (int v = 0; v < 4; ++v) acc[rt][v] = fmaf(p[v], s, acc[rt][v]);
-                    }
-                }
-                // refills in batches of WIDE_BATCH groups (6 KB of the slice in one go)
-                if ((d + 1) % WIDE_BATCH == 0) {
-#pragma unroll
-                    for (int e = d + 1 - WIDE_BATCH; e <= d; ++e) {
-                        lo[e] = __builtin_amdgcn_raw_buffer_load_b128(rb, 16 * lane, (g0 + e + WIDE_DEPTH) * 2048, 0);
-                        hi[e] = __builtin_amdgcn_raw_buffer_load_b128(rb, 16 * lane + 1024, (g0 + e + WIDE_DEPTH) * 2048, 0);
-                    }
-                }
+            for (int d = 0; d < WIDE_DEPTH; ++d) {
+                if (g0 + d < G) group(g0 + d, d);
+                if ((d + 1) % WIDE_BATCH == 0) refill(g0, d);
             }
         }
         // lane l: output row rt * 16 + (l & 15), columns 16 sl + 4 (l >> 4) .. + 3
