@@ -741,9 +741,11 @@ template <int RT>
 __global__ __launch_bounds__(RL_THREADS) void gemm_decode_roles_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ As, const uint8_t* __restrict__ Bf,
     const float* __restrict__ Bs, uint16_t* __restrict__ Cout, int I, int J, int Kc) {
-    constexpr int S = 1, NBUF = RL_NBUF, GMAX = RL_GMAX;
-    constexpr bool ROWC = RT >= 2, XFULL = true;
+    // 4 row tiles (33-64 rows): two rounds in flight and the 1 KB detour slot, for registers and LDS
+    constexpr int S = 1, NBUF = RT == 4 ? 2 : RL_NBUF, GMAX = RL_GMAX;
+    constexpr bool ROWC = RT >= 2, XFULL = RT <= 2;
     constexpr int R = D_WAVES, MR = 16 * RT;
+    constexpr int OPT = (16 * MR + 64 * D_WAVES - 1) / (64 * D_WAVES);   // outputs per consumer thread
     __shared__ v4f pbuf[S][2][R][RT][64];
     __shared__ float sa_lds[GMAX * MR + 64];                     // [g][m] (+ the last load's overhang)
     __shared__ __attribute__((aligned(16))) uint8_t xbuf[ROWC ? D_WAVES * RT * (XFULL ? 2048 : 1024) : 16];
@@ -853,44 +855,57 @@ __global__ __launch_bounds__(RL_THREADS) void gemm_decode_roles_kernel(
         const float sb0 = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rbs, lane * 4, 0, 0));
         const float sb1 = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rbs, lane * 4, 256, 0));
         __builtin_amdgcn_s_waitcnt(0);
-        // output ownership: consumer thread tc < 16 MR holds, in each slice, element tc & 3 of lane (tc >> 2) & 63
-        // of row tile tc >> 8: output row (tc >> 8) 16 + ((tc >> 2) & 15), column 4 ((tc >> 6) & 3) + (tc & 3)
-        const int ln = (tc >> 2) & 63, m = (tc >> 8) * 16 + (ln & 15);
-        float acc[S];
+        // output ownership: consumer thread tc holds outputs u = tc + 512 h (h < OPT, u < 16 MR): in each slice,
+        // element u & 3 of lane (u >> 2) & 63 of row tile u >> 8, i.e. output row (u >> 8) 16 + ((u >> 2) & 15),
+        // column 4 ((u >> 6) & 3) + (u & 3)
+        float acc[OPT][S];
 #pragma unroll
-        for (int sx = 0; sx < S; ++sx) acc[sx] = 0.0f;
+        for (int h = 0; h < OPT; ++h)
+#pragma unroll
+            for (int sx = 0; sx < S; ++sx) acc[h][sx] = 0.0f;
         for (int r = 0; r < nr; ++r) {
             __builtin_amdgcn_s_barrier();
-            if (tc < 16 * MR) {
-                const float sbr = r * R < 64 ? sb0 : sb1;         // R divides 64: a round lies in one half
-                // the round's products and row scales read first (a group past the contraction is in bounds: the
-                // rounds cover at most RL_GMAX groups, a multiple of the round; its entries are unused)
-                float pv[S][R], sav[R];
+            const float sbr = r * R < 64 ? sb0 : sb1;             // R divides 64: a round lies in one half
 #pragma unroll
-                for (int ig = 0; ig < R; ++ig) {
-                    sav[ig] = sa_lds[(r * R + ig) * MR + m];
+            for (int h = 0; h < OPT; ++h) {
+                const int u = tc + 64 * D_WAVES * h;
+                const int m = (u >> 8) * 16 + ((u >> 2) & 15);
+                if (u < 16 * MR) {
+                    // the round's products and row scales read first (a group past the contraction is in bounds:
+                    // the rounds cover at most RL_GMAX groups, a multiple of the round; its entries are unused)
+                    float pv[S][R], sav[R];
 #pragma unroll
-                    for (int sx = 0; sx < S; ++sx)
-                        pv[sx][ig] = reinterpret_cast<const float*>(&pbuf[sx][r & 1][0][0][0])[ig * RT * 256 + tc];
-                }
+                    for (int ig = 0; ig < R; ++ig) {
+                        sav[ig] = sa_lds[(r * R + ig) * MR + m];
 #pragma unroll
-                for (int ig = 0; ig < R; ++ig) {
-                    const int g = r * R + ig;
-                    if (g < G) {
-                        const float sb = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sbr), g & 63));
-                        const float s = sav[ig] * sb;                             // s = fl32(sa * sb)
+                        for (int sx = 0; sx < S; ++sx)
+                            pv[sx][ig] = reinterpret_cast<const float*>(&pbuf[sx][r & 1][0][0][0])[ig * RT * 256 + u];
+                    }
 #pragma unroll
-                        for (int sx = 0; sx < S; ++sx) acc[sx] = fmaf(pv[sx][ig], s, acc[sx]);
+                    for (int ig = 0; ig < R; ++ig) {
+                        const int g = r * R + ig;
+                        if (g < G) {
+                            const float sb = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sbr), g & 63));
+                            const float s = sav[ig] * sb;                         // s = fl32(sa * sb)
+#pragma unroll
+                            for (int sx = 0; sx < S; ++sx) acc[h][sx] = fmaf(pv[sx][ig], s, acc[h][sx]);
+                        }
                     }
                 }
             }
             // this round's product reads are done before the next barrier
             __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
         }
-        if (tc < 16 * MR && m < I) {
 #pragma unroll
-            for (int sx = 0; sx < S; ++sx)
-                Cout[(int64_t)m * J + (sl0 + sx) * 16 + 4 * (ln >> 4) + (tc & 3)] = (uint16_t)f32_to_bf16_rne(acc[sx]);
+        for (int h = 0; h < OPT; ++h) {
+            const int u = tc + 64 * D_WAVES * h;
+            const int m = (u >> 8) * 16 + ((u >> 2) & 15);
+            if (u < 16 * MR && m < I) {
+#pragma unroll
+                for (int sx = 0; sx < S; ++sx)
+                    Cout[(int64_t)m * J + (sl0 + sx) * 16 + 4 * ((u >> 6) & 3) + (u & 3)] =
+                        (uint16_t)f32_to_bf16_rne(acc[h][sx]);
+            }
         }
     }
 }
@@ -912,8 +927,8 @@ static SmallM decode_schedule(int64_t M, int64_t N, int64_t K, int cus) {
     const int64_t G = K / BK, slices = N / 16;
     if (decode_wide_fits(M, N, K, cus)) return SmallM::kWide;
     if (decode_wwide_fits(M, N, K, cus)) return SmallM::kWWide;
-    if (M > 32) return SmallM::kShared;
-    if (G <= SP_GMAX) return SmallM::kSplit;
+    if (M > 64) return SmallM::kShared;
+    if (M <= 32 && G <= SP_GMAX) return SmallM::kSplit;
     if (G <= RL_GMAX && (slices <= cus || (slices <= 2 * (int64_t)cus && G >= 64))) return SmallM::kRoles;
     return SmallM::kShared;
 }
@@ -970,7 +985,8 @@ hipError_t launch_gemm_fwd_frag(const uint8_t* xq, const float* xs, const uint8_
                        : launch_decode_split<2>(xq, xs, wqf, ws, y, M, N, K, cus, st);
     case SmallM::kRoles:
         return M <= 16 ? launch_decode_roles<1>(xq, xs, wqf, ws, y, M, N, K, st)
-                       : launch_decode_roles<2>(xq, xs, wqf, ws, y, M, N, K, st);
+                       : M <= 32 ? launch_decode_roles<2>(xq, xs, wqf, ws, y, M, N, K, st)
+                                 : launch_decode_roles<4>(xq, xs, wqf, ws, y, M, N, K, st);
     case SmallM::kShared:
         break;
     }
