@@ -912,12 +912,13 @@ __global__ __launch_bounds__(RL_THREADS) void gemm_decode_roles_kernel(
 
 // Which small-M schedule a fragment-ordered forward GEMM takes: the wide one when its activations fit in LDS, else
 // the windowed wide one for at least 4 slices per CU (up to 64 rows and 128 groups; where both fit the first measured
-// faster: gate/up at 32 rows 25.5 against 28.0 us, its waves run unsynchronized), else for at most 32 rows:
-//   - at most 32 groups: the one-round per-slice kernel (with fewer than 4 slices per CU; from 4 per CU on, the wide
-//     kernel fits, since the activations of 32 groups fit in LDS);
-//   - 33-128 groups: the role-split kernel, when its one-block-per-slice rounds stay short: at most one slice per
-//     CU, or two for contractions of at least 64 groups; otherwise the slice-sharing kernel, whose persistent blocks
-//     stream on across slices.
+// faster: gate/up at 32 rows 25.5 against 28.0 us, its waves run unsynchronized), else:
+//   - at most 32 rows and 32 groups: the one-round per-slice kernel (with fewer than 4 slices per CU; from 4 per CU
+//     on, the wide kernel fits, since the activations of 32 groups fit in LDS);
+//   - 33-128 groups (and any contraction at 33-64 rows): the role-split kernel, when its one-block-per-slice rounds
+//     stay short: at most one slice per CU, or two for contractions of at least 64 groups or for more than 32 rows
+//     (at 48 rows QKV measured 20.9 -> 18.2 us, 4096 x 8192 20.8 -> 18.0); otherwise the slice-sharing kernel,
+//     whose persistent blocks stream on across slices.
 // Measured against the slice-sharing kernel at 32 rows (fragment-ordered weights, one process): QKV 12.6 -> 8.5 us,
 // O 9.0 -> 6.6, down (14336 x 4096) 23.5 -> 15.4, 16384 x 8192 43.3 -> 39.5; but 5120 x 13824 (3.4 slices per CU,
 // 40 groups) 24.7 -> 28.6 and 5120 x 27648 45.9 -> 61.8 on the role-split kernel, which is why those do not take it
@@ -929,7 +930,7 @@ static SmallM decode_schedule(int64_t M, int64_t N, int64_t K, int cus) {
     if (decode_wwide_fits(M, N, K, cus)) return SmallM::kWWide;
     if (M > 64) return SmallM::kShared;
     if (M <= 32 && G <= SP_GMAX) return SmallM::kSplit;
-    if (G <= RL_GMAX && (slices <= cus || (slices <= 2 * (int64_t)cus && G >= 64))) return SmallM::kRoles;
+    if (G <= RL_GMAX && (slices <= cus || (slices <= 2 * (int64_t)cus && (G >= 64 || M > 32)))) return SmallM::kRoles;
     return SmallM::kShared;
 }
 

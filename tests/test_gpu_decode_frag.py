@@ -152,7 +152,8 @@ def test_wide_schedule_equals_row_major(jf, orc, M):
     (48, 4096, 14336),    # 48 rows (4 row tiles), 112 groups: producer and consumer waves, two outputs per consumer
     (64, 4096, 4096),     # 64 rows, 32 groups, one slice per CU: producer and consumer waves
     (40, 2048, 640),      # 40 rows, 5 groups: one ragged round, rows 40-63 empty
-    (48, 6144, 4096),     # 48 rows, 1.5 slices per CU and 32 groups: the slice-sharing schedule
+    (48, 6144, 4096),     # 48 rows, 1.5 slices per CU and 32 groups: producer and consumer waves
+    (48, 12288, 4096),    # 48 rows, 3 slices per CU, too few for the wide schedules: the slice-sharing schedule
 ])
 def test_per_slice_schedule_equals_row_major(jf, orc, M, N, K):
     """Forward GEMMs with fewer 16-column slices than the wide schedule needs (QKV, O, down shapes) run the
