@@ -290,6 +290,19 @@ def producer_traffic(path=os.path.join(ROOT, "profiles", "producers_traffic.json
     return {k: v["bytes"] for k, v in rec["kernels"].items()}
 
 
+def timed_steps(torch, st, steps, step, with_events):
+    """Time `steps` calls of step(c, ev) on stream st between two HIP events; ev collects per-launch event
+    pairs when with_events.  Returns (ms per step, ev)."""
+    ev = [] if with_events else None
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(st)
+    for c in range(steps):
+        step(c, ev)
+    t1.record(st)
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / steps, ev
+
+
 def run_producers(args, torch, jf, workloads, wl):
     lin = {n: (K, N) for n, K, N in wl.linears}
     C, F, R = lin["qkv"][0], lin["down"][0], wl.M
@@ -321,14 +334,8 @@ def run_producers(args, torch, jf, workloads, wl):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    ev = []
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0.record(st)
-    for _ in range(args.steps):
-        step(ev)
-    t1.record(st)
-    torch.cuda.synchronize()
-    ms_step = t0.elapsed_time(t1) / args.steps
+    ms_step, _ = timed_steps(torch, st, args.steps, lambda c, ev: step(ev), with_events=False)
+    ms_step_ev, ev = timed_steps(torch, st, args.steps, lambda c, ev: step(ev), with_events=True)
     per = {}
     for kind, a, b in ev:
         per.setdefault(kind, [0.0, 0])
@@ -351,7 +358,9 @@ def run_producers(args, torch, jf, workloads, wl):
                 "channels x50, norm weight 1+0.1N(0,1); gate 2N(0,1) with 1% outlier channels x20, up N(0,1))",
         "config": {"workload": f"{wl.name} producers", "tokens": R, "hidden": C, "ffn": F,
                    "step": "2 x RMSNorm->1x128 [tokens x hidden] + 1 x SwiGLU->1x128 [tokens x 2 ffn -> ffn]"},
-        "roofline": dict(kern[dom], bound="hbm", kernel=f"{dom}_quant_kernel"),
+        "roofline": dict(kern[dom], bound="hbm", kernel=f"{dom}_quant_kernel",
+                         timing=f"HIP events around each launch, over {args.steps} more steps "
+                                f"({ms_step_ev * 1e3:.1f} us per step with the events)"),
         "per_kernel": kern,
     }
     if not args.no_cpu_baseline:
@@ -439,14 +448,12 @@ def run_decode(args, torch, jf, workloads):
     for c in range(args.warmup):
         step(c)
     torch.cuda.synchronize()
-    ev = []
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0.record(st)
-    for c in range(args.steps):
-        step(c, ev)
-    t1.record(st)
-    torch.cuda.synchronize()
-    ms_step = t0.elapsed_time(t1) / args.steps
+    # the step time comes from K plain steps; the per-launch durations from K more steps with a pair of HIP
+    # events around each GEMM (recording them costs the stream a few microseconds per launch)
+    # (the weight copies keep cycling from one region to the next)
+    W, K = args.warmup, args.steps
+    ms_step, _ = timed_steps(torch, st, K, lambda c, ev: step(W + c, ev), with_events=False)
+    ms_step_ev, ev = timed_steps(torch, st, K, lambda c, ev: step(W + K + c, ev), with_events=True)
     step_bytes = sum(decode_gemm_bytes(M, L["N"], L["K"]) + 3 * M * L["K"] + (L["K"] // 128) * M * 4 for L in lin)
     gemm_ms = sum(a.elapsed_time(b) for _, _, a, b in ev)
     gemm_bytes = sum(n for _, n, _, _ in ev)
@@ -475,7 +482,9 @@ def run_decode(args, torch, jf, workloads):
                      "frac": round(gemm_bytes / (gemm_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                      "traffic": decode_traffic() if M == wl.M else None,
                      "launches": len(ev), "mean_launch_us": round(1e3 * gemm_ms / len(ev), 2),
-                     "bytes_per_launch_mean": round(gemm_bytes / len(ev))},
+                     "bytes_per_launch_mean": round(gemm_bytes / len(ev)),
+                     "timing": f"HIP events around each launch, over {args.steps} more steps "
+                               f"({ms_step_ev * 1e3:.1f} us per step with the events)"},
         "per_linear": {k: {"mean_launch_us": round(1e3 * v[0] / v[1], 2),
                            "gbs": round(v[2] / (v[0] / v[1] * 1e-3) / 1e9, 1)} for k, v in per.items()},
     }
