@@ -95,24 +95,35 @@ def _dt(t, dtype, name):
         raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
 
 
+_torch = None
+
+
+def _torch_mod():
+    global _torch
+    if _torch is None:
+        import torch
+        _torch = torch
+    return _torch
+
+
 def _need(t, shape, dtype, name, device=None):
     """Host-side check of one operand before its pointer reaches the C ABI (which trusts the sizes it is
-    given): a contiguous device tensor of exactly this shape and dtype, on `device` when given."""
-    import torch
+    given): a contiguous device tensor of exactly this shape and dtype, on `device` when given.  Kept to a few
+    attribute reads (a decode step issues eight calls in well under 100 us)."""
     if t is None:
         raise ValueError(f"{name}: required")
-    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+    if not isinstance(t, _torch_mod().Tensor) or not t.is_cuda:
         raise ValueError(f"{name}: expected a device tensor")
     if dtype is not None and t.dtype != dtype:
         raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
-    if tuple(t.shape) != tuple(int(d) for d in shape):
-        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.shape != shape:                      # torch.Size compares element by element with a tuple
+        raise ValueError(f"{name}: expected shape {tuple(int(d) for d in shape)}, got {tuple(t.shape)}")
     if device is not None and t.device != device:
         raise ValueError(f"{name}: on {t.device}, other operands on {device}")
 
 
 def _bf16_u8_f32():
-    import torch
+    torch = _torch_mod()
     return torch.bfloat16, torch.uint8, torch.float32
 
 
