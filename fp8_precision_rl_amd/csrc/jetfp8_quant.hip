@@ -123,16 +123,53 @@ __global__ __launch_bounds__(256) void quant_cols_t_kernel(const uint16_t* __res
     if (ok && l < 8) sT[(int64_t)rb * C + c + l] = my_scale;
 }
 
+// Four codes of one group packed little-endian into a uint32: encode8's arithmetic (fast quotient, per-element
+// midpoint screen, exact fix of a screened element) on four elements.
+__device__ __forceinline__ uint32_t encode4(const float x[4], const GroupScale& g) {
+    constexpr uint32_t kSmall = 2u * (0x3C800000u + 3u) - 2u;    // (2 |q| pattern - 2) <= kSmall: 0 < |q| <= 2^-6 + 3 ulps
+    float q[4];
+    uint32_t smin = 0xFFFFFFFFu;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        q[i] = x[i] * g.rcp;
+        smin = min(smin, (__float_as_uint(q[i]) << 1) - 2u);    // +-0 wraps to the top
+    }
+    if (g.tiny) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) q[i] = approx_quotient(x[i], g);
+        smin = 0;
+    }
+    uint32_t k_mid;
+    asm("s_mov_b32 %0, 0xfff80004" : "=s"(k_mid));
+    if (smin <= kSmall) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t b = __float_as_uint(q[i]);
+            const bool small = (b << 1) - 2u <= kSmall;
+            if (small || ((b + k_mid) << 12) <= (8u << 12)) q[i] = resolve_at_midpoint(x[i], cell_midpoint(q[i], small), g);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (((__float_as_uint(q[i]) + k_mid) << 12) <= (8u << 12))
+                q[i] = resolve_at_midpoint(x[i], cell_midpoint(q[i], false), g);
+        }
+    }
+    return cvt2_e4m3<true>(q[2], q[3], cvt2_e4m3<false>(q[0], q[1], __float_as_uint(q[1])));
+}
+
 // 1x128 and 128x1 groups of the same tensor from one read (the activation / gradient feeding a forward or DGrad
 // GEMM and a WGrad GEMM): codes q [R][C] with scales s [C/128][R], and transposed codes qT [C][R] with scales
-// sT [R/128][C].  A 256-thread block owns a 128x128 tile, so each of its rows is one 1x128 group and each of its
-// columns one 128x1 group.  Lane l of DPP row k of wave w holds the 8x8 sub-tile of rows 8 (4w + k) .. +7 and
-// columns 8 l .. +7 (eight 16-byte loads; a DPP row reads 256 contiguous bytes of each of its rows):
+// sT [R/128][C].  A 512-thread block owns a 128x128 tile, so each of its rows is one 1x128 group and each of its
+// columns one 128x1 group.  Lane l of DPP row k of wave w holds the 4x8 sub-tile of rows 16 w + 4 k .. +3 and
+// columns 8 l .. +7 (four 16-byte loads; a DPP row reads 256 contiguous bytes of each of its rows):
 //   - a row's group lies in one DPP row: its amax is a 16-lane row reduction, and the 16 lanes write the row's
 //     128 codes as one contiguous run;
 //   - a column's group spans the whole block: per-lane maxima, then across the wave's four DPP rows, then
-//     across the four waves through LDS; the transposed codes are staged in LDS and leave as whole
-//     128-byte transposed rows.
+//     across the eight waves through LDS; each lane encodes its four values of each of its 8 columns into one
+//     word, the words are staged in LDS and leave as whole 128-byte transposed rows.
+// 4x8 sub-tiles (72 VGPRs, 6 waves per SIMD) instead of 8x8 ones in 256-thread blocks (96 VGPRs capped, 5 waves):
+// bitwise the same codes, measured 4.38 -> 4.83 TB/s at 65536 x 27648, +1-3 % at 65536 x 5120 and x 7168.
 // Memory access goes through raw buffer descriptors built from block-uniform bases (scalar registers) with
 // 32-bit lane offsets, so no 64-bit address arithmetic runs on the vector unit.  A descriptor spans exactly
 // the bytes its accesses touch; the launcher checks that every span and offset fits in 31 bits.
@@ -141,46 +178,42 @@ __device__ __forceinline__ rsrc_q_t span_rsrc(const void* base, int64_t bytes) {
 }
 
 // Word index in row c of the transposed-code staging buffer for logical word w (0..31): its 16-byte chunk w / 4 is
-// XORed with the row's 8-column group (c / 8) % 8, so a staging write instruction (16 columns 8 apart x 4 words)
-// covers all eight chunks.
+// XORed with the row's 8-column group (c / 8) % 8, so a staging write instruction (16 columns 8 apart) covers all
+// eight chunks.
 __device__ __forceinline__ int tcode_word(int c, int w) { return (((w >> 2) ^ ((c >> 3) & 7)) << 2) | (w & 3); }
 
-// At most 96 VGPRs, so 5 waves per SIMD fit instead of 4 (97 unconstrained): more loads in flight per CU
-// (measured +6 % on 16384-row tensors, no spills).
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5, 8))) void quant_dual_kernel(const uint16_t* __restrict__ x, int64_t R, int64_t C,
-                                                         uint8_t* __restrict__ q, float* __restrict__ s,
-                                                         uint8_t* __restrict__ qT, float* __restrict__ sT,
-                                                         uint32_t col_blocks) {
-    __shared__ uint32_t red[4][16][4];
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(6, 8))) void quant_dual_kernel(
+    const uint16_t* __restrict__ x, int64_t R, int64_t C, uint8_t* __restrict__ q, float* __restrict__ s,
+    uint8_t* __restrict__ qT, float* __restrict__ sT, uint32_t col_blocks) {
+    __shared__ uint32_t red[8][16][4];
     // [column][4-row word] with the 16-byte chunks of a row XOR-swizzled by the column's 8-column group
-    // (tcode_word): rows stay 16-byte aligned, so a lane's two code words go in as one 8-byte write and the
-    // transposed rows come out as 16-byte reads.  The swizzle spreads a write instruction over every chunk: with
-    // the plain 36-word pitch (8 x 36 = 0 mod 32 banks) the 16 lanes of a write fell on one or two banks.
+    // (tcode_word): rows stay 16-byte aligned, so the transposed rows come out as 16-byte reads, and the 16 lanes
+    // of a write instruction spread over the banks.
     __shared__ __attribute__((aligned(16))) uint32_t tcodes[128][32];
     const int t = threadIdx.x, lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-    const int l16 = lane & 15, rs = lane >> 4, rb8 = 4 * wave + rs;
+    const int l16 = lane & 15, rs = lane >> 4, rb4 = 4 * wave + rs;     // rb4: the lane's 4-row word of a column
     const uint32_t cb = blockIdx.x % col_blocks, rb = blockIdx.x / col_blocks;
     const int64_t r0 = (int64_t)rb * 128, c0 = (int64_t)cb * 128;
-    // this wave's 32 rows start at wr; the lane's 8x8 sub-tile is rows wr + 8 rs .. +7, columns c0 + 8 l16 ..
-    const int64_t wr = r0 + 32 * wave;
+    // this wave's 16 rows start at wr; the lane's 4x8 sub-tile is rows wr + 4 rs .. +3, columns c0 + 8 l16 ..
+    const int64_t wr = r0 + 16 * wave;
     const int Ci = (int)C;
-    const int64_t span = 31 * C + 128;                       // elements from (wr, c0) to (wr + 31, c0 + 127)
+    const int64_t span = 15 * C + 128;                       // elements from (wr, c0) to (wr + 15, c0 + 127)
     const rsrc_q_t rx = span_rsrc(x + wr * C + c0, 2 * span);
     const rsrc_q_t rq = span_rsrc(q + wr * C + c0, span);
-    const int lo = 8 * rs * Ci + 8 * l16;                    // element offset of the lane's first row
-    uint4 v[8];
+    const int lo = 4 * rs * Ci + 8 * l16;                    // element offset of the lane's first row
+    uint4 v[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 4; ++i) {
         const u32x4_q w = __builtin_amdgcn_raw_buffer_load_b128(rx, 2 * lo, 2 * i * Ci, 0);
         v[i] = make_uint4(w[0], w[1], w[2], w[3]);
     }
 
     // magnitude maxima from the sign-cleared words: per row of the sub-tile (8 values) and per column (two
-    // columns per word, over the 8 rows); the column maxima then over the wave's 4 DPP rows
-    uint32_t cm[4] = {0u, 0u, 0u, 0u}, rmax[8];
+    // columns per word, over the 4 rows); the column maxima then over the wave's 4 DPP rows
+    uint32_t cm[4] = {0u, 0u, 0u, 0u}, rmax[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 4; ++i) {
         const uint32_t m0 = mag2(v[i].x), m1 = mag2(v[i].y), m2 = mag2(v[i].z), m3 = mag2(v[i].w);
         cm[0] = pkmax16(cm[0], m0);
         cm[1] = pkmax16(cm[1], m1);
@@ -202,7 +235,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5, 8))) voi
     // 1x128 groups: one per row
     float row_scale = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 4; ++i) {
         float f[8];
         unpack8(v[i], f);
         const GroupScale gs = make_group_scale(bf16_to_f32(row16_max_u32(rmax[i])));
@@ -211,13 +244,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5, 8))) voi
         __builtin_amdgcn_raw_buffer_store_b64(o, rq, lo, i * Ci, 0);
         if (l16 == i) row_scale = gs.s;
     }
-    if (l16 < 8) s[(c0 / 128) * R + wr + (8 * rs + l16)] = row_scale;
+    if (l16 < 4) s[(c0 / 128) * R + wr + (4 * rs + l16)] = row_scale;
 
     // 128x1 groups: one per column
     __syncthreads();
 #pragma unroll
-    for (int w = 0; w < 4; ++w)
-        cm[w] = pkmax16(pkmax16(red[0][l16][w], red[1][l16][w]), pkmax16(red[2][l16][w], red[3][l16][w]));
+    for (int w = 0; w < 4; ++w) {
+        const uint32_t a = pkmax16(pkmax16(red[0][l16][w], red[1][l16][w]), pkmax16(red[2][l16][w], red[3][l16][w]));
+        const uint32_t b = pkmax16(pkmax16(red[4][l16][w], red[5][l16][w]), pkmax16(red[6][l16][w], red[7][l16][w]));
+        cm[w] = pkmax16(a, b);
+    }
     auto elem = [&](int i, int j) -> float {
         const uint32_t w = (j >> 1) == 0 ? v[i].x : (j >> 1) == 1 ? v[i].y : (j >> 1) == 2 ? v[i].z : v[i].w;
         return bf16_to_f32((j & 1) ? (w >> 16) : (w & 0xFFFFu));
@@ -225,13 +261,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5, 8))) voi
     float col_scale_a = 0.0f, col_scale_b = 0.0f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-        float f[8];
+        float f[4];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) f[i] = elem(i, j);
+        for (int i = 0; i < 4; ++i) f[i] = elem(i, j);
         const uint32_t half = (j & 1) ? (cm[j >> 1] >> 16) : (cm[j >> 1] & 0xFFFFu);
         const GroupScale gs = make_group_scale(bf16_to_f32(half));
-        const uint2 out = encode8(f, gs);
-        *reinterpret_cast<uint2*>(&tcodes[8 * l16 + j][tcode_word(8 * l16 + j, 2 * rb8)]) = out;
+        tcodes[8 * l16 + j][tcode_word(8 * l16 + j, rb4)] = encode4(f, gs);
         if (j == rs) col_scale_a = gs.s;
         if (j == rs + 4) col_scale_b = gs.s;
     }
@@ -242,13 +277,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5, 8))) voi
         st[8 * l16 + rs + 4] = col_scale_b;
     }
     __syncthreads();
-    // thread t writes bytes 64 (t & 1) .. +63 of transposed row c0 + t / 2 (rows r0 .. r0 + 127 of it)
+    // thread t writes bytes 32 (t & 3) .. +31 of transposed row c0 + t / 4 (rows r0 .. r0 + 127 of it)
     const rsrc_q_t rqt = span_rsrc(qT + c0 * R + r0, 127 * R + 128);
-    const int oc = t >> 1, hf = t & 1;
-    const int to = oc * (int)R + 64 * hf;
+    const int oc = t >> 2, qt = t & 3;
+    const int to = oc * (int)R + 32 * qt;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const uint4 w4 = *reinterpret_cast<const uint4*>(&tcodes[oc][tcode_word(oc, 16 * hf + 4 * k)]);
+    for (int k = 0; k < 2; ++k) {
+        const uint4 w4 = *reinterpret_cast<const uint4*>(&tcodes[oc][tcode_word(oc, 8 * qt + 4 * k)]);
         const u32x4_q o = {w4.x, w4.y, w4.z, w4.w};
         __builtin_amdgcn_raw_buffer_store_b128(o, rqt, to + 16 * k, 0, 0);
     }
@@ -258,9 +293,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5, 8))) voi
 // WGrad groups X along the token axis): the 1x128 codes q [R][C] with their scales s [C/128][R] are
 // dequantized, x' = fl32(decode(code) * s) with one fp32 product, and x' is quantized in 128x1 groups along R
 // as the bf16 path does (the encode arithmetic and its exactness argument hold for any finite fp32 x').
-// Output: qT [C][R], sT [R/128][C].  Layout of the work as quant_dual_kernel: a 128x128 tile per 256-thread
-// block, an 8x8 sub-tile per lane (8 rows x 8 codes), column maxima across the wave's DPP rows and the
-// block's waves, transposed codes staged in LDS.  2 bytes of traffic per element instead of 3.
+// Output: qT [C][R], sT [R/128][C].  A 128x128 tile per 256-thread block, an 8x8 sub-tile per lane (8 rows x 8
+// codes), column maxima across the wave's DPP rows and the block's waves, transposed codes staged in LDS as in
+// quant_dual_kernel.  2 bytes of traffic per element instead of 3.
 __global__ __launch_bounds__(256) void quant_requant_cols_kernel(const uint8_t* __restrict__ q,
                                                                  const float* __restrict__ s, int64_t R,
                                                                  int64_t C, uint8_t* __restrict__ qT,
@@ -456,9 +491,10 @@ hipError_t launch_quant_dual(const uint16_t* x, int64_t R, int64_t C, uint8_t* q
                              hipStream_t st) {
     // R and C are multiples of 128 (whole groups both ways)
     const int64_t col_blocks = C / 128, row_blocks = R / 128;
-    // buffer spans and offsets in 31 bits: 32 bf16 rows (2 * (31 C + 128) bytes) and 128 transposed rows
+    // buffer spans and offsets in 31 bits: a wave's 16 bf16 rows (2 (15 C + 128) bytes; the check allows 32) and
+    // 128 transposed rows
     if (!quant_dual_fits(R, C)) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(quant_dual_kernel, dim3((unsigned)(col_blocks * row_blocks)), dim3(256), 0, st, x, R, C, q, s,
+    hipLaunchKernelGGL(quant_dual_kernel, dim3((unsigned)(col_blocks * row_blocks)), dim3(512), 0, st, x, R, C, q, s,
                        qT, sT, (uint32_t)col_blocks);
     return hipGetLastError();
 }
