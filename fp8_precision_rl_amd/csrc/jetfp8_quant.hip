@@ -167,9 +167,13 @@ __device__ __forceinline__ uint32_t encode4(const float x[4], const GroupScale& 
 //     128 codes as one contiguous run;
 //   - a column's group spans the whole block: per-lane maxima, then across the wave's four DPP rows, then
 //     across the eight waves through LDS; each lane encodes its four values of each of its 8 columns into one
-//     word, the words are staged in LDS and leave as whole 128-byte transposed rows.
-// 4x8 sub-tiles (72 VGPRs, 6 waves per SIMD) instead of 8x8 ones in 256-thread blocks (96 VGPRs capped, 5 waves):
-// bitwise the same codes, measured 4.38 -> 4.83 TB/s at 65536 x 27648, +1-3 % at 65536 x 5120 and x 7168.
+//     word, the words are staged in LDS and leave as whole 128-byte transposed rows;
+//   - each group's scale (and its reciprocal) is formed once, by one lane, and read from LDS by the lanes that
+//     encode with it (a row's 16 lanes, a column's 32).
+// 4x8 sub-tiles instead of 8x8 ones in 256-thread blocks (96 VGPRs capped, 5 waves per SIMD) hold half the values
+// per lane, and forming each scale once drops the per-lane scale arithmetic: 49 VGPRs, 8 waves per SIMD.
+// Bitwise the same codes; measured on 65536-row tensors 4.20 -> 4.87 TB/s at x 5120, 4.64 -> 4.94 at dY 7168,
+// and 4.39 -> 4.70 at x 27648.
 // Memory access goes through raw buffer descriptors built from block-uniform bases (scalar registers) with
 // 32-bit lane offsets, so no 64-bit address arithmetic runs on the vector unit.  A descriptor spans exactly
 // the bytes its accesses touch; the launcher checks that every span and offset fits in 31 bits.
@@ -186,6 +190,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(6, 8))) voi
     const uint16_t* __restrict__ x, int64_t R, int64_t C, uint8_t* __restrict__ q, float* __restrict__ s,
     uint8_t* __restrict__ qT, float* __restrict__ sT, uint32_t col_blocks) {
     __shared__ uint32_t red[8][16][4];
+    __shared__ float4 cscale[128];           // (s, r, p2, rcp) of the tile's 128 column groups
+    __shared__ float4 rscale[8][16];         // the same for each wave's 16 rows
     // [column][4-row word] with the 16-byte chunks of a row XOR-swizzled by the column's 8-column group
     // (tcode_word): rows stay 16-byte aligned, so the transposed rows come out as 16-byte reads, and the 16 lanes
     // of a write instruction spread over the banks.
@@ -232,49 +238,65 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(6, 8))) voi
         for (int w = 0; w < 4; ++w) red[wave][l16][w] = cm[w];
     }
 
-    // 1x128 groups: one per row
-    float row_scale = 0.0f;
+    // 1x128 groups: one per row; lane i of each DPP row forms the scale of its row i (i < 4) for the 16 lanes
+    {
+        uint32_t am[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) am[i] = row16_max_u32(rmax[i]);
+        const uint32_t mine = l16 == 0 ? am[0] : l16 == 1 ? am[1] : l16 == 2 ? am[2] : am[3];
+        if (l16 < 4) {
+            const GroupScale gs = make_group_scale(bf16_to_f32(mine));
+            rscale[wave][4 * rs + l16] = make_float4(gs.s, gs.r, gs.p2, gs.rcp);
+            s[(c0 / 128) * R + wr + (4 * rs + l16)] = gs.s;
+        }
+    }
+    __builtin_amdgcn_wave_barrier();
+    asm volatile("" ::: "memory");
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         float f[8];
         unpack8(v[i], f);
-        const GroupScale gs = make_group_scale(bf16_to_f32(row16_max_u32(rmax[i])));
+        const float4 cs = rscale[wave][4 * rs + i];
+        GroupScale gs;
+        gs.s = cs.x;
+        gs.r = cs.y;
+        gs.p2 = cs.z;
+        gs.rcp = cs.w;
+        gs.tiny = cs.z != 1.0f;
         const uint2 out = encode8(f, gs);
         const u32x2_q o = {out.x, out.y};
         __builtin_amdgcn_raw_buffer_store_b64(o, rq, lo, i * Ci, 0);
-        if (l16 == i) row_scale = gs.s;
     }
-    if (l16 < 4) s[(c0 / 128) * R + wr + (4 * rs + l16)] = row_scale;
 
-    // 128x1 groups: one per column
+    // 128x1 groups: one per column; each column's scale formed once, by thread c
     __syncthreads();
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-        const uint32_t a = pkmax16(pkmax16(red[0][l16][w], red[1][l16][w]), pkmax16(red[2][l16][w], red[3][l16][w]));
-        const uint32_t b = pkmax16(pkmax16(red[4][l16][w], red[5][l16][w]), pkmax16(red[6][l16][w], red[7][l16][w]));
-        cm[w] = pkmax16(a, b);
+    if (t < 128) {
+        const int l = t >> 3, w = (t & 7) >> 1;
+        const uint32_t a = pkmax16(pkmax16(red[0][l][w], red[1][l][w]), pkmax16(red[2][l][w], red[3][l][w]));
+        const uint32_t b = pkmax16(pkmax16(red[4][l][w], red[5][l][w]), pkmax16(red[6][l][w], red[7][l][w]));
+        const uint32_t m = pkmax16(a, b);
+        const GroupScale gs = make_group_scale(bf16_to_f32((t & 1) ? (m >> 16) : (m & 0xFFFFu)));
+        cscale[t] = make_float4(gs.s, gs.r, gs.p2, gs.rcp);
+        sT[(int64_t)rb * C + c0 + t] = gs.s;
     }
+    __syncthreads();
     auto elem = [&](int i, int j) -> float {
         const uint32_t w = (j >> 1) == 0 ? v[i].x : (j >> 1) == 1 ? v[i].y : (j >> 1) == 2 ? v[i].z : v[i].w;
         return bf16_to_f32((j & 1) ? (w >> 16) : (w & 0xFFFFu));
     };
-    float col_scale_a = 0.0f, col_scale_b = 0.0f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         float f[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) f[i] = elem(i, j);
-        const uint32_t half = (j & 1) ? (cm[j >> 1] >> 16) : (cm[j >> 1] & 0xFFFFu);
-        const GroupScale gs = make_group_scale(bf16_to_f32(half));
+        const float4 cs = cscale[8 * l16 + j];
+        GroupScale gs;
+        gs.s = cs.x;
+        gs.r = cs.y;
+        gs.p2 = cs.z;
+        gs.rcp = cs.w;
+        gs.tiny = cs.z != 1.0f;
         tcodes[8 * l16 + j][tcode_word(8 * l16 + j, rb4)] = encode4(f, gs);
-        if (j == rs) col_scale_a = gs.s;
-        if (j == rs + 4) col_scale_b = gs.s;
-    }
-    // wave 0 writes the tile's 128 column scales: lane (l, k) those of columns 8 l + k and 8 l + k + 4
-    if (wave == 0) {
-        float* st = sT + (int64_t)rb * C + c0;
-        st[8 * l16 + rs] = col_scale_a;
-        st[8 * l16 + rs + 4] = col_scale_b;
     }
     __syncthreads();
     // thread t writes bytes 32 (t & 3) .. +31 of transposed row c0 + t / 4 (rows r0 .. r0 + 127 of it)
