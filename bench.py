@@ -278,14 +278,15 @@ def producers_cpu_baseline(C, F, rows_rn, rows_sg, workloads):
 PRODUCER_SOURCES = [os.path.join(ROOT, "fp8_precision_rl_amd", "csrc", f) for f in ("jetfp8_producers.hip", "jetfp8_common.h")]
 
 
-def producer_traffic(path=os.path.join(ROOT, "profiles", "producers_traffic.json")):
+def producer_traffic(workload, path=os.path.join(ROOT, "profiles", "producers_traffic.json")):
     """Per-launch HBM bytes of the producer kernels from rocprofv3 FETCH_SIZE / WRITE_SIZE (scaled by a 1 GiB
-    copy), or None when the record is missing or was taken on other kernel sources."""
+    copy), or None when the record is missing, was taken at another workload's shapes or on other kernel
+    sources."""
     try:
         rec = json.load(open(path))
     except (OSError, ValueError):
         return None
-    if rec.get("source_sha256") != source_digest(PRODUCER_SOURCES):
+    if rec.get("workload") != workload or rec.get("source_sha256") != source_digest(PRODUCER_SOURCES):
         return None
     return {k: v["bytes"] for k, v in rec["kernels"].items()}
 
@@ -345,7 +346,7 @@ def run_producers(args, torch, jf, workloads, wl):
     kern = {k: {"mean_launch_us": round(1e3 * v[0] / v[1], 2), "bytes_per_launch": byts[k],
                 "achieved": round(byts[k] / (v[0] / v[1] * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(byts[k] / (v[0] / v[1] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)} for k, v in per.items()}
-    traffic = producer_traffic()
+    traffic = producer_traffic(f"{wl.name} producers")
     for k in kern:
         kern[k]["traffic"] = traffic.get(k) if traffic else None
     dom = max(kern, key=lambda k: per[k][0])

@@ -120,63 +120,70 @@ __device__ __forceinline__ float swiglu_fast(float g, float u, bool& exact) {
 }  // namespace
 
 // ---------------------------------------------------------------------------------------------------------
-// RMSNorm -> 1x128.  A block of 8 waves owns 8 consecutive rows, one per wave.  A wave holds its row in
-// registers: chunk c covers columns 512 c .. +511, lane l columns 512 c + 8 l .. +7, so the 16 lanes of a DPP
-// row hold one 128-column group.  The group scales of the 8 rows are staged in LDS and written as 32-byte runs
-// per group.  (One row per wave measured fastest: 4 rows per wave, with or without the next row's loads issued
-// ahead, left all blocks loading, then all computing, in step.)
-constexpr int RN_ROWS = 8, RN_WAVES = 8, RN_PASSES = RN_ROWS / RN_WAVES;
+// RMSNorm -> 1x128.  A block of 8 waves owns 8 / WPR consecutive rows, WPR waves per row.  A wave holds its part of
+// the row in registers: its k-th chunk covers columns 512 c .. +511 (c = part * NCH / WPR + k), lane l columns
+// 512 c + 8 l .. +7, so the 16 lanes of a DPP row hold one 128-column group.  With WPR = 2 the two halves of the
+// sum of squares meet in LDS and are added in a fixed order, so a lane holds half the values and more waves fit
+// per SIMD: rows of 4096 48 VGPRs and 8 waves per SIMD (80 capped, 6 waves, with one wave per row), rows of 5120
+// 69 VGPRs (128, 4 waves, through the 16-chunk instantiation): measured 52.8 -> 51.5 us at 16384 x 4096 and
+// 268.9 -> 242.3 us at 65536 x 5120, bitwise the same codes, scales and rstd.  The group scales of the block's
+// rows are staged in LDS and written as runs per group.  (One row per wave of four, with or without the next
+// row's loads issued ahead, left all blocks loading, then all computing, in step.)
+constexpr int RN_WAVES = 8;
 
-// NCH = 8 (rows of 4096) is capped at 80 VGPRs (81 unconstrained), so 6 waves per SIMD fit instead of 5: measured
-// 12 % faster, no spills, the same bits.  The other widths are left to the compiler (a cap spills them).
-template <int NCH>
-__global__ __launch_bounds__(RN_WAVES * 64) __attribute__((amdgpu_waves_per_eu(NCH == 8 ? 6 : 1, 8))) void rmsnorm_quant_kernel(
+template <int NCH, int WPR>
+__global__ __launch_bounds__(RN_WAVES * 64) void rmsnorm_quant_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, int64_t R, int64_t C, float eps,
     uint8_t* __restrict__ q, float* __restrict__ s, float* __restrict__ rstd, uint16_t* __restrict__ y) {
-    __shared__ float sc[NCH * 4][RN_ROWS];
+    constexpr int ROWS = RN_WAVES / WPR, HCH = NCH / WPR;
+    __shared__ float sc[NCH * 4][ROWS];
+    __shared__ double pss[ROWS][WPR];
     const int t = threadIdx.x, wave = t >> 6, lane = t & 63, lane16 = lane & 15, gl = lane >> 4;
-    const int64_t r0 = (int64_t)blockIdx.x * RN_ROWS;
+    const int64_t r0 = (int64_t)blockIdx.x * ROWS;
     const double eps_d = (double)eps;
-
+    const int rr = wave / WPR, part = wave % WPR;
+    const int64_t row = r0 + rr;
+    const bool live = row < R;                                   // wave-uniform
+    const int64_t rowc = live ? row : 0;                         // in-bounds stand-in row (nothing stored)
+    uint4 v[HCH];
 #pragma unroll
-    for (int p = 0; p < RN_PASSES; ++p) {
-        const int rr = p * RN_WAVES + wave;
-        const int64_t row = r0 + rr;
-        if (row >= R) break;                                     // wave-uniform
-        uint4 v[NCH];
+    for (int k = 0; k < HCH; ++k) {
+        const int64_t col = (int64_t)(part * HCH + k) * 512 + lane * 8;
+        v[k] = ld16(x + rowc * C + (col < C ? col : 0));         // in-bounds stand-in past C: not used
+    }
+    double pa[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
-        for (int c = 0; c < NCH; ++c) {
-            const int64_t col = (int64_t)c * 512 + lane * 8;
-            v[c] = ld16(x + row * C + (col < C ? col : 0));       // in-bounds stand-in past C: not used
-        }
-        // sum of squares in fp64 (8 partial sums per lane, then the wave)
-        double part[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int k = 0; k < HCH; ++k) {
+        if ((int64_t)(part * HCH + k) * 512 + lane * 8 < C) {
 #pragma unroll
-        for (int c = 0; c < NCH; ++c) {
-            if ((int64_t)c * 512 + lane * 8 < C) {
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const double f = (double)elem_of(v[c], i);
-                    part[i] = fma(f, f, part[i]);
-                }
+            for (int i = 0; i < 8; ++i) {
+                const double f = (double)elem_of(v[k], i);
+                pa[i] = fma(f, f, pa[i]);
             }
         }
-        const double ss = wave_sum(((part[0] + part[1]) + (part[2] + part[3])) + ((part[4] + part[5]) + (part[6] + part[7])));
-        const float r = (float)(1.0 / sqrt(ss / (double)C + eps_d));
-        if (rstd && lane == 0) rstd[row] = r;
-
+    }
+    double ss = wave_sum(((pa[0] + pa[1]) + (pa[2] + pa[3])) + ((pa[4] + pa[5]) + (pa[6] + pa[7])));
+    if (WPR > 1) {
+        if (lane == 0) pss[rr][part] = ss;
+        __syncthreads();
+        ss = pss[rr][0] + pss[rr][1];
+    }
+    const float r = (float)(1.0 / sqrt(ss / (double)C + eps_d));
+    if (live) {
+        if (rstd && lane == 0 && part == 0) rstd[row] = r;
 #pragma unroll
-        for (int c = 0; c < NCH; ++c) {
+        for (int k = 0; k < HCH; ++k) {
+            const int c = part * HCH + k;
             const int64_t col = (int64_t)c * 512 + lane * 8;
             if (c * 512 >= C) break;                              // whole chunk past the row (uniform)
             const bool ok = col < C;
             const uint4 wv = ld16(w + (ok ? col : 0));
             uint32_t hw[4];
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const float y0 = (elem_of(v[c], 2 * k) * r) * elem_of(wv, 2 * k);
-                const float y1 = (elem_of(v[c], 2 * k + 1) * r) * elem_of(wv, 2 * k + 1);
-                hw[k] = bf16x2_rne(y0, y1);
+            for (int kk = 0; kk < 4; ++kk) {
+                const float y0 = (elem_of(v[k], 2 * kk) * r) * elem_of(wv, 2 * kk);
+                const float y1 = (elem_of(v[k], 2 * kk + 1) * r) * elem_of(wv, 2 * kk + 1);
+                hw[kk] = bf16x2_rne(y0, y1);
             }
             const uint4 yv = make_uint4(hw[0], hw[1], hw[2], hw[3]);
             float scale;
@@ -190,9 +197,9 @@ __global__ __launch_bounds__(RN_WAVES * 64) __attribute__((amdgpu_waves_per_eu(N
     }
     __syncthreads();
     const int G = (int)(C / 128);
-    for (int i = t; i < G * RN_ROWS; i += RN_WAVES * 64) {
-        const int g = i / RN_ROWS, rr = i % RN_ROWS;
-        if (r0 + rr < R) s[(int64_t)g * R + r0 + rr] = sc[g][rr];
+    for (int i = t; i < G * ROWS; i += RN_WAVES * 64) {
+        const int g = i / ROWS, rq = i % ROWS;
+        if (r0 + rq < R) s[(int64_t)g * R + r0 + rq] = sc[g][rq];
     }
 }
 
@@ -266,12 +273,15 @@ __global__ __launch_bounds__(SG_WAVES * 64) void swiglu_quant_kernel(const uint1
 hipError_t launch_rmsnorm_quant(const uint16_t* x, const uint16_t* w, int64_t R, int64_t C, float eps, uint8_t* q,
                                 float* s, float* rstd, uint16_t* y, hipStream_t st) {
     if (C > kRmsNormMaxCols) return hipErrorInvalidValue;
-    const dim3 grid((unsigned)((R + RN_ROWS - 1) / RN_ROWS)), block(RN_WAVES * 64);
+    const dim3 block(RN_WAVES * 64);
+    const dim3 grid1((unsigned)((R + RN_WAVES - 1) / RN_WAVES)), grid2((unsigned)((R + RN_WAVES / 2 - 1) / (RN_WAVES / 2)));
     const int nch = (int)((C + 511) / 512);
-    if (nch <= 2) hipLaunchKernelGGL(rmsnorm_quant_kernel<2>, grid, block, 0, st, x, w, R, C, eps, q, s, rstd, y);
-    else if (nch <= 4) hipLaunchKernelGGL(rmsnorm_quant_kernel<4>, grid, block, 0, st, x, w, R, C, eps, q, s, rstd, y);
-    else if (nch <= 8) hipLaunchKernelGGL(rmsnorm_quant_kernel<8>, grid, block, 0, st, x, w, R, C, eps, q, s, rstd, y);
-    else hipLaunchKernelGGL(rmsnorm_quant_kernel<16>, grid, block, 0, st, x, w, R, C, eps, q, s, rstd, y);
+    if (nch <= 2) hipLaunchKernelGGL((rmsnorm_quant_kernel<2, 1>), grid1, block, 0, st, x, w, R, C, eps, q, s, rstd, y);
+    else if (nch <= 4) hipLaunchKernelGGL((rmsnorm_quant_kernel<4, 1>), grid1, block, 0, st, x, w, R, C, eps, q, s, rstd, y);
+    else if (nch <= 8) hipLaunchKernelGGL((rmsnorm_quant_kernel<8, 2>), grid2, block, 0, st, x, w, R, C, eps, q, s, rstd, y);
+    else if (nch <= 10) hipLaunchKernelGGL((rmsnorm_quant_kernel<10, 2>), grid2, block, 0, st, x, w, R, C, eps, q, s, rstd, y);
+    else if (nch <= 12) hipLaunchKernelGGL((rmsnorm_quant_kernel<12, 2>), grid2, block, 0, st, x, w, R, C, eps, q, s, rstd, y);
+    else hipLaunchKernelGGL((rmsnorm_quant_kernel<16, 2>), grid2, block, 0, st, x, w, R, C, eps, q, s, rstd, y);
     return hipGetLastError();
 }
 

@@ -68,7 +68,10 @@ def _special_rows(xb, rng):
 
 
 @pytest.mark.parametrize("R,C,eps", [(64, 4096, 1e-5), (37, 640, 1e-6), (1, 128, 1e-5), (70, 8192, 1e-5),
-                                     (33, 1536, 1e-5), (40, 2048, 0.5)])
+                                     (33, 1536, 1e-5), (40, 2048, 0.5),
+                                     (37, 5120, 1e-5),     # two waves per row, 5 chunks each
+                                     (9, 4224, 1e-5),      # two waves per row: the second's last chunks partial / past the row
+                                     (5, 6016, 1e-6)])     # 12-chunk instantiation, ragged last chunk
 def test_rmsnorm_bit_exact(jf, prod, R, C, eps):
     xb, wb = workloads.host_rmsnorm_inputs(R * 31 + C, R, C)
     xb = _special_rows(xb, np.random.default_rng(R + C))
@@ -88,13 +91,16 @@ def test_rmsnorm_optional_outputs_absent(jf):
     assert torch.equal(q1, q2) and torch.equal(s1.view(torch.int32), s2.view(torch.int32))
 
 
-def test_rmsnorm_full_size_sampled_rows(jf, prod):
-    """The 16384 x 4096 RMSNorm of the Llama-3-8B-shaped workload (device-generated inputs); 48 sampled rows."""
+@pytest.mark.parametrize("R,C", [(16384, 4096), (65536, 5120)])
+def test_rmsnorm_full_size_sampled_rows(jf, prod, R, C):
+    """The RMSNorms of the Llama-3-8B-shaped (16384 x 4096) and Qwen2.5-32B-shaped (65536 x 5120) workloads
+    (device-generated inputs); 48 sampled rows."""
     import torch
-    x, w = workloads.device_rmsnorm_inputs(11, 16384, 4096)
+    print(f"rmsnorm full size R={R} C={C}", flush=True)
+    x, w = workloads.device_rmsnorm_inputs(11, R, C)
     q, s, r = jf.rmsnorm_quantize(x, w, 1e-5)
     torch.cuda.synchronize()
-    rows = np.sort(np.random.default_rng(3).choice(16384, 48, replace=False))
+    rows = np.sort(np.random.default_rng(3).choice(R, 48, replace=False))
     xb, wb = dev_to_bits(x[torch.from_numpy(rows).cuda()]), dev_to_bits(w)
     r_ref, near = prod.rmsnorm_rstd(xb, 1e-5)
     rg = r.cpu().numpy()[rows]
