@@ -190,7 +190,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(6, 8))) voi
     const uint16_t* __restrict__ x, int64_t R, int64_t C, uint8_t* __restrict__ q, float* __restrict__ s,
     uint8_t* __restrict__ qT, float* __restrict__ sT, uint32_t col_blocks) {
     __shared__ uint32_t red[8][16][4];
-    __shared__ float4 cscale[128];           // (s, r, p2, rcp) of the tile's 128 column groups
+    __shared__ float4 cscale[8][16];         // (s, r, p2, rcp) of column 8 l + j at [j][l]: a read of one j by
+                                             // the 16 lanes of a DPP row covers 256 contiguous bytes
     __shared__ float4 rscale[8][16];         // the same for each wave's 16 rows
     // [column][4-row word] with the 16-byte chunks of a row XOR-swizzled by the column's 8-column group
     // (tcode_word): rows stay 16-byte aligned, so the transposed rows come out as 16-byte reads, and the 16 lanes
@@ -276,7 +277,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(6, 8))) voi
         const uint32_t b = pkmax16(pkmax16(red[4][l][w], red[5][l][w]), pkmax16(red[6][l][w], red[7][l][w]));
         const uint32_t m = pkmax16(a, b);
         const GroupScale gs = make_group_scale(bf16_to_f32((t & 1) ? (m >> 16) : (m & 0xFFFFu)));
-        cscale[t] = make_float4(gs.s, gs.r, gs.p2, gs.rcp);
+        cscale[t & 7][t >> 3] = make_float4(gs.s, gs.r, gs.p2, gs.rcp);
         sT[(int64_t)rb * C + c0 + t] = gs.s;
     }
     __syncthreads();
@@ -289,7 +290,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(6, 8))) voi
         float f[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) f[i] = elem(i, j);
-        const float4 cs = cscale[8 * l16 + j];
+        const float4 cs = cscale[j][l16];
         GroupScale gs;
         gs.s = cs.x;
         gs.r = cs.y;
