@@ -165,3 +165,32 @@ def test_all_x_amax_pairs_sampled(jf, orc):
         qq = q.cpu().numpy()
         bad = np.argwhere(qq != oq)
         assert bad.size == 0, [(hex(int(g[r, c])), hex(int(g[r, 0])), hex(int(qq[r, c])), hex(int(oq[r, c]))) for r, c in bad[:5]]
+
+
+def test_all_x_amax_pairs_sampled_dual(jf, orc):
+    """The same (x, amax) pairs through the fused 1x128 + 128x1 kernel, as its 128x1 groups: each pair group is
+    one column of a 128-row matrix (so the column path's 4-value encoder sees every pair), padded with all-zero
+    columns to a multiple of 128.  The column codes and scales must be those of the oracle's 1x128 quantization
+    of the groups; the matrix's own 1x128 rows are checked too.  JETFP8_FULL_SWEEP=1 checks all pairs."""
+    import torch
+    full = os.environ.get("JETFP8_FULL_SWEEP") == "1"
+    all_a = np.arange(1, 0x7F80, dtype=np.uint32)
+    amax = all_a if full else np.unique(np.concatenate([all_a[::29], [1, 2, 0x7F, 0x80, 0x81, 0x3F80, 0x43E0, 0x7F7F]]))
+    chunk = 2048 if not full else 1024
+    for i in range(0, amax.size, chunk):
+        print(f"dual pairs: amax values {i} .. {min(i + chunk, amax.size)} of {amax.size}", flush=True)
+        g = _pair_groups(amax[i:i + chunk].astype(np.uint16))
+        n = g.shape[0]
+        npad = -(-n // 128) * 128
+        xt = np.zeros((npad, 128), np.uint16)
+        xt[:n] = g
+        x = np.ascontiguousarray(xt.T)                              # [128, npad]: column j = group j
+        q, s, qT, sT = jf.quantize_dual(bits_to_dev(x))
+        torch.cuda.synchronize()
+        oq, os_ = orc.quantize_rows(xt)
+        assert np.array_equal(sT.cpu().numpy()[0].view(np.uint32), os_[0].view(np.uint32)), i
+        qq = qT.cpu().numpy()
+        bad = np.argwhere(qq != oq)
+        assert bad.size == 0, [(hex(int(xt[r, c])), hex(int(xt[r, 0])), hex(int(qq[r, c])), hex(int(oq[r, c]))) for r, c in bad[:5]]
+        orq, ors = orc.quantize_rows(x)
+        assert np.array_equal(q.cpu().numpy(), orq) and np.array_equal(s.cpu().numpy().view(np.uint32), ors.view(np.uint32)), i
