@@ -138,7 +138,7 @@ __global__ __launch_bounds__(RN_WAVES * 64) void rmsnorm_quant_kernel(
     constexpr int ROWS = RN_WAVES / WPR, HCH = NCH / WPR;
     __shared__ float sc[NCH * 4][ROWS];
     __shared__ double pss[ROWS][WPR];
-    const int t = threadIdx.x, wave = t >> 6, lane = t & 63, lane16 = lane & 15, gl = lane >> 4;
+    const int t = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(t >> 6), lane = t & 63, lane16 = lane & 15, gl = lane >> 4;
     const int64_t r0 = (int64_t)blockIdx.x * ROWS;
     const double eps_d = (double)eps;
     const int rr = wave / WPR, part = wave % WPR;
@@ -226,7 +226,7 @@ __global__ __launch_bounds__(SG_WAVES * 64) void swiglu_quant_kernel(const uint1
                                                                       float* __restrict__ s, uint16_t* __restrict__ h,
                                                                       uint32_t col_blocks) {
     __shared__ float sc[4][SG_ROWS];
-    const int t = threadIdx.x, wave = t >> 6, lane = t & 63, gl = lane >> 4, lane16 = lane & 15;
+    const int t = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(t >> 6), lane = t & 63, gl = lane >> 4, lane16 = lane & 15;
     const uint32_t cb = blockIdx.x % col_blocks, rb = blockIdx.x / col_blocks;
     const int64_t c0 = (int64_t)cb * SG_COLS, r0 = (int64_t)rb * SG_ROWS;
     const int col = (int)c0 + lane * 8;

@@ -44,7 +44,7 @@ __global__ __launch_bounds__(QR_WAVES * 64) void quant_rows_kernel(const uint16_
                                                                    float* __restrict__ s, uint32_t col_blocks) {
     constexpr int QR_ROWS = QR_WAVES * QR_PASSES;
     __shared__ float sc[4][QR_ROWS];
-    const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
+    const int t = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(t >> 6), lane = t & 63;
     const int gl = lane >> 4, lane16 = lane & 15;
     const uint32_t cb = blockIdx.x % col_blocks, rb = blockIdx.x / col_blocks;
     const int64_t c0 = (int64_t)cb * QR_COLS, r0 = (int64_t)rb * QR_ROWS;
@@ -84,7 +84,7 @@ __global__ __launch_bounds__(QR_WAVES * 64) void quant_rows_kernel(const uint16_
 __global__ __launch_bounds__(256) void quant_cols_t_kernel(const uint16_t* __restrict__ x, int64_t R, int64_t C,
                                                            uint8_t* __restrict__ qT, float* __restrict__ sT,
                                                            uint32_t col_blocks) {
-    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int t = threadIdx.x, lane = t & 63, wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int l = lane & 15, k = lane >> 4;
     const uint32_t cb = blockIdx.x % col_blocks, rb = blockIdx.x / col_blocks;
     const int64_t r0 = (int64_t)rb * 128;
