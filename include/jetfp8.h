@@ -43,7 +43,8 @@
  *                             128 * rows + 128 >= 2^31;
  *       requantize_cols_t ... (cols / 128) * (rows / 128) > 2^31 - 1, 32 * cols + 128 >= 2^31, or
  *                             128 * rows + 128 >= 2^31;
- *       swiglu_quantize ..... ceil(cols / 512) * ceil(rows / 32) >= 2^31.
+ *       swiglu_quantize ..... ceil(cols / 512) * ceil(rows / 32) >= 2^31, or 128 * cols >= 2^31 (32 rows of
+ *                             gate_up in bytes).
  *   - Thread safety: calls are independent; concurrent calls on different streams are allowed.
  */
 #ifndef JETFP8_H

@@ -206,6 +206,7 @@ def test_launch_size_limits_are_shape_errors(lib):
     assert rq(lib, cols=1 << 26) == -2                              # 32 * cols + 128 >= 2^31
     assert rq(lib, rows=1 << 24) == -2
     assert lib.jetfp8_swiglu_quantize(P, 1 << 16, 1 << 29, P, P, None, None) == -2   # grid
+    assert lib.jetfp8_swiglu_quantize(P, 32, 1 << 24, P, P, None, None) == -2        # 128 * cols >= 2^31
     for fn in ("jetfp8_gemm_fwd", "jetfp8_gemm_dgrad"):
         f = getattr(lib, fn)
         assert f(P, P, P, P, P, 256, 1 << 24, 1 << 24, None) == -2  # 256 * contraction >= 2^31
