@@ -316,40 +316,38 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(6, 8))) voi
 // WGrad groups X along the token axis): the 1x128 codes q [R][C] with their scales s [C/128][R] are
 // dequantized, x' = fl32(decode(code) * s) with one fp32 product, and x' is quantized in 128x1 groups along R
 // as the bf16 path does (the encode arithmetic and its exactness argument hold for any finite fp32 x').
-// Output: qT [C][R], sT [R/128][C].  A 128x128 tile per 256-thread block, an 8x8 sub-tile per lane (8 rows x 8
-// codes), column maxima across the wave's DPP rows and the block's waves, transposed codes staged in LDS as in
-// quant_dual_kernel.  2 bytes of traffic per element instead of 3.
-__global__ __launch_bounds__(256) void quant_requant_cols_kernel(const uint8_t* __restrict__ q,
+// Output: qT [C][R], sT [R/128][C].  The work is laid out as in quant_dual_kernel: a 128x128 tile per 512-thread
+// block, a 4x8 sub-tile per lane (4 rows x 8 codes), column maxima across the wave's DPP rows and the block's
+// waves, each column scale formed once and shared through LDS, transposed codes staged in LDS.  (With 8x8
+// sub-tiles in 256-thread blocks, 85 VGPRs and 5 waves per SIMD: 198.6 -> 167.0 us at 65536 x 5120 and 1200 ->
+// 850 us at 65536 x 27648, bitwise the same.)  2 bytes of traffic per element instead of 3.
+__global__ __launch_bounds__(512) void quant_requant_cols_kernel(const uint8_t* __restrict__ q,
                                                                  const float* __restrict__ s, int64_t R,
                                                                  int64_t C, uint8_t* __restrict__ qT,
                                                                  float* __restrict__ sT, uint32_t col_blocks) {
-    __shared__ uint32_t red[4][16][8];
-    // [column][4-row word] with the 16-byte chunks of a row XOR-swizzled by the column's 8-column group
-    // (tcode_word): rows stay 16-byte aligned, so a lane's two code words go in as one 8-byte write and the
-    // transposed rows come out as 16-byte reads.  The swizzle spreads a write instruction over every chunk: with
-    // the plain 36-word pitch (8 x 36 = 0 mod 32 banks) the 16 lanes of a write fell on one or two banks.
-    __shared__ __attribute__((aligned(16))) uint32_t tcodes[128][32];
+    __shared__ uint32_t red[8][16][8];
+    __shared__ float4 cscale[8][16];         // (s, r, p2, rcp) of column 8 l + j at [j][l], as in quant_dual_kernel
+    __shared__ __attribute__((aligned(16))) uint32_t tcodes[128][32];   // as in quant_dual_kernel
     const int t = threadIdx.x, lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-    const int l16 = lane & 15, rs = lane >> 4, rb8 = 4 * wave + rs;
+    const int l16 = lane & 15, rs = lane >> 4, rb4 = 4 * wave + rs;
     const uint32_t cb = blockIdx.x % col_blocks, rb = blockIdx.x / col_blocks;
     const int64_t r0 = (int64_t)rb * 128, c0 = (int64_t)cb * 128;
-    const int64_t wr = r0 + 32 * wave;
+    const int64_t wr = r0 + 16 * wave;
     const int Ci = (int)C;
-    const rsrc_q_t rcodes = span_rsrc(q + wr * C + c0, 31 * C + 128);
-    const int lo = 8 * rs * Ci + 8 * l16;
-    u32x2_q cw[8];
+    const rsrc_q_t rcodes = span_rsrc(q + wr * C + c0, 15 * C + 128);
+    const int lo = 4 * rs * Ci + 8 * l16;
+    u32x2_q cw[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) cw[i] = __builtin_amdgcn_raw_buffer_load_b64(rcodes, lo, i * Ci, 0);
-    // saved scales of the lane's 8 rows (group c0 / 128 of each row): 32 contiguous bytes
-    const float4* sp = reinterpret_cast<const float4*>(s + (c0 / 128) * R + wr + 8 * rs);
-    const float4 sa = sp[0], sb = sp[1];
-    const float sr[8] = {sa.x, sa.y, sa.z, sa.w, sb.x, sb.y, sb.z, sb.w};
+    for (int i = 0; i < 4; ++i) cw[i] = __builtin_amdgcn_raw_buffer_load_b64(rcodes, lo, i * Ci, 0);
+    // saved scales of the lane's 4 rows (group c0 / 128 of each row): 16 contiguous bytes
+    const float4 sa = *reinterpret_cast<const float4*>(s + (c0 / 128) * R + wr + 4 * rs);
+    const float sr[4] = {sa.x, sa.y, sa.z, sa.w};
 
     // dequantize: element (i, j) is byte j of the lane's row i
-    float xv[8][8];
+    float xv[4][8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int w = 0; w < 2; ++w) {
             const auto lo2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)cw[i][w], false);   // bytes 0, 1 of the word
@@ -360,14 +358,14 @@ __global__ __launch_bounds__(256) void quant_requant_cols_kernel(const uint8_t* 
             xv[i][4 * w + 3] = hi2[1] * sr[i];
         }
 
-    // column maxima of the magnitude bits (fp32 patterns order like the magnitudes): this lane's 8 rows,
-    // then the wave's 4 DPP rows, then the block's 4 waves
+    // column maxima of the magnitude bits (fp32 patterns order like the magnitudes): this lane's 4 rows, then
+    // the wave's 4 DPP rows, then the block's 8 waves; each column's scale formed once, by thread c
     uint32_t cm[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         uint32_t m = 0;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) m = max(m, __float_as_uint(xv[i][j]) & 0x7FFFFFFFu);
+        for (int i = 0; i < 4; ++i) m = max(m, __float_as_uint(xv[i][j]) & 0x7FFFFFFFu);
         m = max(m, (uint32_t)__shfl_xor((int)m, 16, 64));
         m = max(m, (uint32_t)__shfl_xor((int)m, 32, 64));
         cm[j] = m;
@@ -377,31 +375,37 @@ __global__ __launch_bounds__(256) void quant_requant_cols_kernel(const uint8_t* 
         for (int j = 0; j < 8; ++j) red[wave][l16][j] = cm[j];
     }
     __syncthreads();
-    float col_scale_a = 0.0f, col_scale_b = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const uint32_t m = max(max(red[0][l16][j], red[1][l16][j]), max(red[2][l16][j], red[3][l16][j]));
-        float f[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) f[i] = xv[i][j];
-        const GroupScale gs = make_group_scale(__uint_as_float(m));
-        const uint2 out = encode8(f, gs);
-        *reinterpret_cast<uint2*>(&tcodes[8 * l16 + j][tcode_word(8 * l16 + j, 2 * rb8)]) = out;
-        if (j == rs) col_scale_a = gs.s;
-        if (j == rs + 4) col_scale_b = gs.s;
-    }
-    if (wave == 0) {
-        float* st = sT + (int64_t)rb * C + c0;
-        st[8 * l16 + rs] = col_scale_a;
-        st[8 * l16 + rs + 4] = col_scale_b;
+    if (t < 128) {
+        const int l = t >> 3, j = t & 7;
+        const uint32_t a = max(max(red[0][l][j], red[1][l][j]), max(red[2][l][j], red[3][l][j]));
+        const uint32_t b = max(max(red[4][l][j], red[5][l][j]), max(red[6][l][j], red[7][l][j]));
+        const GroupScale gs = make_group_scale(__uint_as_float(max(a, b)));
+        cscale[j][l] = make_float4(gs.s, gs.r, gs.p2, gs.rcp);
+        sT[(int64_t)rb * C + c0 + t] = gs.s;
     }
     __syncthreads();
-    const rsrc_q_t rqt = span_rsrc(qT + c0 * R + r0, 127 * R + 128);
-    const int oc = t >> 1, hf = t & 1;
-    const int to = oc * (int)R + 64 * hf;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const uint4 w4 = *reinterpret_cast<const uint4*>(&tcodes[oc][tcode_word(oc, 16 * hf + 4 * k)]);
+    for (int j = 0; j < 8; ++j) {
+        float f[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) f[i] = xv[i][j];
+        const float4 cs = cscale[j][l16];
+        GroupScale gs;
+        gs.s = cs.x;
+        gs.r = cs.y;
+        gs.p2 = cs.z;
+        gs.rcp = cs.w;
+        gs.tiny = cs.z != 1.0f;
+        tcodes[8 * l16 + j][tcode_word(8 * l16 + j, rb4)] = encode4(f, gs);
+    }
+    __syncthreads();
+    // thread t writes bytes 32 (t & 3) .. +31 of transposed row c0 + t / 4 (rows r0 .. r0 + 127 of it)
+    const rsrc_q_t rqt = span_rsrc(qT + c0 * R + r0, 127 * R + 128);
+    const int oc = t >> 2, qt = t & 3;
+    const int to = oc * (int)R + 32 * qt;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const uint4 w4 = *reinterpret_cast<const uint4*>(&tcodes[oc][tcode_word(oc, 8 * qt + 4 * k)]);
         const u32x4_q o = {w4.x, w4.y, w4.z, w4.w};
         __builtin_amdgcn_raw_buffer_store_b128(o, rqt, to + 16 * k, 0, 0);
     }
@@ -527,7 +531,7 @@ hipError_t launch_quant_requant_cols(const uint8_t* q, const float* s, int64_t R
     // R and C are multiples of 128; buffer spans and offsets in 31 bits (32 code rows, 128 transposed rows)
     const int64_t col_blocks = C / 128, row_blocks = R / 128;
     if (!quant_requant_cols_fits(R, C)) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(quant_requant_cols_kernel, dim3((unsigned)(col_blocks * row_blocks)), dim3(256), 0, st, q, s,
+    hipLaunchKernelGGL(quant_requant_cols_kernel, dim3((unsigned)(col_blocks * row_blocks)), dim3(512), 0, st, q, s,
                        R, C, qT, sT, (uint32_t)col_blocks);
     return hipGetLastError();
 }
