@@ -449,12 +449,12 @@ def run_decode(args, torch, jf, workloads):
     for c in range(args.warmup):
         step(c)
     torch.cuda.synchronize()
-    # the step time comes from K plain steps; the per-launch durations from K more steps with a pair of HIP
-    # events around each GEMM (recording them costs the stream a few microseconds per launch)
-    # (the weight copies keep cycling from one region to the next)
-    W, K = args.warmup, args.steps
-    ms_step, _ = timed_steps(torch, st, K, lambda c, ev: step(W + c, ev), with_events=False)
-    ms_step_ev, ev = timed_steps(torch, st, K, lambda c, ev: step(W + K + c, ev), with_events=True)
+    # the step time comes from the timed steps run plainly; the per-launch durations from as many more steps with
+    # a pair of HIP events around each GEMM (recording them costs the stream a few microseconds per launch); the
+    # weight copies keep cycling from one region to the next
+    nw, ns = args.warmup, args.steps
+    ms_step, _ = timed_steps(torch, st, ns, lambda c, ev: step(nw + c, ev), with_events=False)
+    ms_step_ev, ev = timed_steps(torch, st, ns, lambda c, ev: step(nw + ns + c, ev), with_events=True)
     step_bytes = sum(decode_gemm_bytes(M, L["N"], L["K"]) + 3 * M * L["K"] + (L["K"] // 128) * M * 4 for L in lin)
     gemm_ms = sum(a.elapsed_time(b) for _, _, a, b in ev)
     gemm_bytes = sum(n for _, n, _, _ in ev)

@@ -128,8 +128,8 @@ __device__ __forceinline__ float swiglu_fast(float g, float u, bool& exact) {
 // per SIMD: rows of 4096 48 VGPRs and 8 waves per SIMD (80 capped, 6 waves, with one wave per row), rows of 5120
 // 69 VGPRs (128, 4 waves, through the 16-chunk instantiation): measured 52.8 -> 51.5 us at 16384 x 4096 and
 // 268.9 -> 242.3 us at 65536 x 5120, bitwise the same codes, scales and rstd.  The group scales of the block's
-// rows are staged in LDS and written as runs per group.  (One row per wave of four, with or without the next
-// row's loads issued ahead, left all blocks loading, then all computing, in step.)
+// rows are staged in LDS and written as runs per group.  (Four rows per wave, with or without the next row's loads
+// issued ahead, measured slower than one: all blocks loaded, then all computed, in step.)
 constexpr int RN_WAVES = 8;
 
 template <int NCH, int WPR>
