@@ -242,7 +242,9 @@ __global__ __launch_bounds__(SG_WAVES * 64) void swiglu_quant_kernel(const uint1
     uint4 gv[SG_PASSES], uv[SG_PASSES];
 #pragma unroll
     for (int p = 0; p < SG_PASSES; ++p) {
-        // the row offset goes into the lane offset, which the range check covers
+        // the row offset goes into the lane offset, which the range check covers; the largest lane offset,
+        // ro + 2 (F + col) <= 128 F + 1024, stays below 2^31 because the launcher bounds 128 F by 2^31 and F is a
+        // multiple of 128 (so 128 F <= 2^31 - 2^14)
         const int ro = (p * SG_WAVES + wave) * 4 * Fi;
         const u32x4_sg a = __builtin_amdgcn_raw_buffer_load_b128(rin, ro + 2 * col, 0, 0);
         const u32x4_sg b = __builtin_amdgcn_raw_buffer_load_b128(rin, ro + 2 * (Fi + col), 0, 0);
